@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for sparse MLA forward. Test infrastructure only: imported by
+the tests, the package smoke check and the benchmark's CPU-baseline leg, never by
+the library."""
+
+from .sparse_mla_oracle import (  # noqa: F401
+    D_V,
+    attend_row,
+    bf16_bits_to_f64,
+    decode_rows,
+    e4m3fn_table,
+    lse_combine,
+    softmax_weights,
+    sparse_mla_fwd,
+    sparse_mla_fwd_torch,
+)

@@ -1,0 +1,239 @@
+"""Seeded synthetic inputs for sparse MLA forward.
+
+This module only draws data. It holds none of the attention arithmetic, so both
+the HIP path's tests and the fp64 oracle can consume the same tensors without
+sharing any of the method's code.
+
+Every tensor is drawn on the CPU from one ``torch.Generator`` seeded per
+workload, in a fixed order: q, pool, indices, invalid slots. The same seed
+always gives the same bytes (``tensor_digest`` hashes them).
+
+Shapes follow the workloads of "[Triton/Gluon] GFX950 sparse mla optimizations"
+(aiter PR 6159, Technical Details tables): 5+1 speculative decode at C requests,
+8K/16K-row prefill, 16 or 64 heads, DeepSeek-style top-k 512 and GLM-style
+top-k 2048, 576-wide rows (512 latent + 64 rope) or 512-wide rope-free rows.
+"""
+
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+FP8_MAX = 448.0  # largest finite float8_e4m3fn value
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic sparse-MLA call.
+
+    ``index_mode`` says where each row's indices come from:
+      * ``"uniform"``  - distinct, uniform over the whole pool;
+      * ``"request"``  - row r belongs to request r // rows_per_request, which
+        owns pool rows [ctx * b, ctx * b + ctx); distinct within that range;
+      * ``"causal"``   - row i sits at position ``first_pos + i``; distinct
+        from [0, pos].
+    """
+
+    name: str
+    rows: int
+    heads: int
+    d_qk: int
+    pool_rows: int
+    topk: int
+    kv_dtype: str  # "bf16" or "fp8"
+    seed: int
+    index_mode: str = "uniform"
+    invalid_per_row: int = 0
+    rows_per_request: int = 1
+    ctx_per_request: int = 0
+    first_pos: int = 0
+    sm_scale: float | None = None
+    pool_pitch: int | None = None  # elements between pool rows (>= d_qk)
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return self.sm_scale if self.sm_scale is not None else self.d_qk ** -0.5
+
+    @property
+    def pitch(self) -> int:
+        return self.pool_pitch if self.pool_pitch is not None else self.d_qk
+
+
+# The five workloads. Where a workload leaves a detail open the plainest
+# reading is taken: sm_scale = d_qk^-0.5, a decode request owns an equal slice
+# of the pool, prefill rows are the last positions of one context.
+WORKLOADS: dict[str, Workload] = {
+    "tiny": Workload(
+        name="tiny", rows=4, heads=16, d_qk=576, pool_rows=4096, topk=128,
+        kv_dtype="bf16", seed=0, index_mode="uniform", invalid_per_row=2,
+        description="4 rows x 16 heads, bf16 pool 4096x576, top-k 128, 2 invalid per row"),
+    "decode_bf16": Workload(
+        name="decode_bf16", rows=192, heads=64, d_qk=576, pool_rows=131072, topk=512,
+        kv_dtype="bf16", seed=1, index_mode="request", invalid_per_row=26,
+        rows_per_request=6, ctx_per_request=4096,
+        description="DSv4-style decode: 32 requests x (5+1) rows, 64 heads, bf16 pool "
+                    "131072x576, top-k 512 from the request's context, 5% invalid"),
+    "decode_fp8": Workload(
+        name="decode_fp8", rows=768, heads=16, d_qk=576, pool_rows=262144, topk=2048,
+        kv_dtype="fp8", seed=2, index_mode="uniform",
+        description="fp8 decode: 128 requests x (5+1) rows, 16 heads, fp8 pool "
+                    "262144x576 + per-tensor scale, top-k 2048 uniform, no invalid"),
+    "prefill_fp8": Workload(
+        name="prefill_fp8", rows=8192, heads=64, d_qk=576, pool_rows=131072, topk=2048,
+        kv_dtype="fp8", seed=3, index_mode="causal", first_pos=122880,
+        description="fp8 prefill: 8192 rows at positions 122880..131071, 64 heads, "
+                    "fp8 pool 131072x576, top-k 2048 causal"),
+    "prefill_glm": Workload(
+        name="prefill_glm", rows=16384, heads=64, d_qk=512, pool_rows=262144, topk=2048,
+        kv_dtype="fp8", seed=4, index_mode="causal", first_pos=245760,
+        sm_scale=512 ** -0.5,
+        description="rope-free GLM-style prefill: 16384 rows, 64 heads, 512-wide fp8 "
+                    "pool 262144x512, top-k 2048 causal"),
+}
+
+
+@dataclass
+class Inputs:
+    q: torch.Tensor          # bf16 [R, H, D]
+    pool: torch.Tensor       # bf16 or float8_e4m3fn [N, pitch] (first d_qk used)
+    kv_scale: torch.Tensor | None  # fp32 [1] or None for bf16 pools
+    indices: torch.Tensor    # int32 [R, K]
+    sm_scale: float
+    workload: Workload
+    extra: dict = field(default_factory=dict)
+
+
+def _index_ranges(w: Workload) -> tuple[torch.Tensor, torch.Tensor]:
+    r = torch.arange(w.rows, dtype=torch.int64)
+    if w.index_mode == "uniform":
+        lo = torch.zeros(w.rows, dtype=torch.int64)
+        hi = torch.full((w.rows,), w.pool_rows, dtype=torch.int64)
+    elif w.index_mode == "request":
+        b = r // w.rows_per_request
+        lo = b * w.ctx_per_request
+        hi = lo + w.ctx_per_request
+    elif w.index_mode == "causal":
+        lo = torch.zeros(w.rows, dtype=torch.int64)
+        hi = w.first_pos + r + 1
+    else:
+        raise ValueError(f"unknown index_mode {w.index_mode!r}")
+    if int(hi.max()) > w.pool_rows or int((hi - lo).min()) < w.topk:
+        raise ValueError(f"{w.name}: index ranges do not fit pool/top-k")
+    return lo, hi
+
+
+def distinct_indices(lo: torch.Tensor, hi: torch.Tensor, k: int,
+                     gen: torch.Generator) -> torch.Tensor:
+    """k distinct ints per row, uniform over [lo_r, hi_r), kept in draw order.
+
+    Sampler: draw candidates lo + floor(u * (hi - lo)) with u ~ U[0,1) in fp64,
+    keep the first occurrence of each value in draw order, and take the first k
+    kept candidates. While any row has fewer than k distinct candidates another
+    block of candidates is drawn for every row. The result is exactly a uniform
+    draw without replacement (rejection of repeats).
+    """
+    rows = lo.shape[0]
+    span = (hi - lo).to(torch.float64)
+    if rows == 0:
+        return torch.empty((0, k), dtype=torch.int32)
+    # expected repeats among m draws from n values: about m^2 / (2n)
+    n_min = float(span.min())
+    extra = int(min(4 * k, 2 * k * k / n_min + 8 * math.sqrt(k * k / n_min + 1) + 32))
+    cand = torch.empty((rows, 0), dtype=torch.int64)
+    block = k + extra
+    while True:
+        u = torch.rand((rows, block), generator=gen, dtype=torch.float64)
+        new = lo[:, None] + torch.floor(u * span[:, None]).to(torch.int64)
+        cand = torch.cat([cand, new], dim=1)
+        # first occurrence of each value within its row, in draw order
+        sv, order = torch.sort(cand, dim=1, stable=True)
+        dup_sorted = torch.zeros_like(sv, dtype=torch.bool)
+        dup_sorted[:, 1:] = sv[:, 1:] == sv[:, :-1]
+        keep = torch.empty_like(dup_sorted)
+        keep.scatter_(1, order, ~dup_sorted)
+        if int(keep.sum(dim=1).min()) >= k:
+            break
+        block = max(64, k // 4)
+    rank = torch.cumsum(keep.to(torch.int64), dim=1) - 1
+    sel = keep & (rank < k)
+    out = cand[sel].view(rows, k)
+    return out.to(torch.int32)
+
+
+def set_invalid(indices: torch.Tensor, n_invalid: int, gen: torch.Generator) -> torch.Tensor:
+    """Set n_invalid slots per row, at uniformly random distinct slots, to -1."""
+    if n_invalid <= 0 or indices.numel() == 0:
+        return indices
+    rows, k = indices.shape
+    slots = torch.argsort(torch.rand((rows, k), generator=gen), dim=1)[:, :n_invalid]
+    out = indices.clone()
+    out.scatter_(1, slots, -1)
+    return out
+
+
+def quantize_fp8(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Per-tensor e4m3fn codes: s = max|x| / 448, codes = clamp(x / s) in e4m3fn.
+
+    The clamp keeps x / s inside the finite range (torch turns out-of-range
+    values into NaN). This quantiser only makes test data; the method itself
+    starts from the codes and the scale.
+    """
+    s = float(x.abs().max()) / FP8_MAX
+    if s == 0.0:
+        s = 1.0
+    s32 = torch.tensor([s], dtype=torch.float32)
+    codes = torch.clamp(x / s32, -FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return codes, s32
+
+
+def make_inputs(w: Workload | str, rows: int | None = None) -> Inputs:
+    """Draw the workload's tensors on the CPU.
+
+    ``rows`` (optional) keeps only the first ``rows`` query rows of q and of the
+    indices *after* drawing the full workload, so a prefix of a big workload is
+    byte-identical to the same rows of the full draw.
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    gen = torch.Generator(device="cpu").manual_seed(w.seed)
+    q = torch.randn((w.rows, w.heads, w.d_qk), generator=gen, dtype=torch.float32)
+    q = q.to(torch.bfloat16)
+    x = torch.randn((w.pool_rows, w.d_qk), generator=gen, dtype=torch.float32)
+    if w.kv_dtype == "bf16":
+        vals, kv_scale = x.to(torch.bfloat16), None
+    elif w.kv_dtype == "fp8":
+        vals, kv_scale = quantize_fp8(x)
+    else:
+        raise ValueError(f"unknown kv dtype {w.kv_dtype!r}")
+    del x
+    if w.pitch != w.d_qk:
+        pool = torch.zeros((w.pool_rows, w.pitch), dtype=vals.dtype)
+        pool[:, : w.d_qk] = vals
+    else:
+        pool = vals
+    lo, hi = _index_ranges(w)
+    idx = distinct_indices(lo, hi, w.topk, gen)
+    idx = set_invalid(idx, w.invalid_per_row, gen)
+    if rows is not None:
+        q = q[:rows].contiguous()
+        idx = idx[:rows].contiguous()
+    return Inputs(q=q, pool=pool, kv_scale=kv_scale, indices=idx, sm_scale=w.scale, workload=w)
+
+
+def custom_workload(name: str = "custom", **kw) -> Workload:
+    """A Workload with the given fields (for tests of edge shapes)."""
+    base = dict(name=name, rows=4, heads=16, d_qk=576, pool_rows=4096, topk=128,
+                kv_dtype="bf16", seed=123)
+    base.update(kw)
+    return Workload(**base)
+
+
+def tensor_digest(t: torch.Tensor) -> str:
+    """SHA-256 of a CPU tensor's bytes (dtype-agnostic)."""
+    t = t.contiguous()
+    b = t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+    return hashlib.sha256(b.numpy().tobytes()).hexdigest()
