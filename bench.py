@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MLA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_fp8]
+
+A step is one sparse_mla_fwd call (the whole hot path: gather, widening, QK,
+softmax, PV, epilogue, and the combine kernel when the plan splits) over the
+workload's seeded synthetic inputs, already resident in HBM. Before each timed
+step a 1 GiB buffer is written (untimed) so the call starts with cold caches
+(the MI355X MALL is 256 MB and would otherwise hold most of the pool). Device
+time per call comes from HIP events recorded on the stream the library
+launches on. Rank 0 prints one JSON line.
+
+Headline workload: fp8 decode, 128 requests x (5+1) rows = 768 rows, 16 heads,
+576-wide rows, pool 262144 x 576 e4m3fn + per-tensor scale, top-k 2048 (the
+decode shape the HBM-roofline target is set on). The two 64-head prefill
+workloads are timed too and reported under "prefill" with their MFMA fraction.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+KERNEL_SRC = os.path.join(ROOT, "sparse_mla_attention_05_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_fp8")
+    ap.add_argument("--prefill", default="prefill_fp8,prefill_glm",
+                    help="comma list of extra workloads to time ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle sample")
+    ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
+    return ap.parse_args()
+
+
+def algorithmic(inp):
+    """Algorithmic bytes and flops of one call.
+
+    bytes = gathered KV (one pool row per valid slot) + q + indices + out + lse;
+    flops = 2 * H * (valid slots) * (D_qk + 512)."""
+    R, H, D = inp.q.shape
+    K = inp.indices.shape[1]
+    valid = int((inp.indices >= 0).sum())
+    eb = 1 if inp.workload.kv_dtype == "fp8" else 2
+    kv = valid * D * eb
+    other = R * H * D * 2 + R * K * 4 + R * H * 512 * 2 + R * H * 4
+    flops = 2 * H * valid * (D + 512)
+    return dict(kv_bytes=kv, bytes=kv + other, flops=flops, valid_slots=valid)
+
+
+def source_digest():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fwd_kernel_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("kernel_source_sha256_16") != source_digest():
+            return None
+        return d.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def time_workload(name, steps, warmup, cold):
+    import torch
+    from sparse_mla_attention_05_amd import _lib
+    from sparse_mla_attention_05_amd.inputs import make_inputs
+
+    inp = make_inputs(name)
+    dev = torch.device("cuda:0")
+    q, pool, idx = inp.q.to(dev), inp.pool.to(dev), inp.indices.to(dev)
+    scale = inp.kv_scale.to(dev) if inp.kv_scale is not None else None
+    R, H = q.shape[0], q.shape[1]
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    plan = _lib.sparse_mla_plan(q, pool, idx)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if cold else None  # 1 GiB
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        _lib.sparse_mla_fwd(q, pool, scale, idx, inp.sm_scale, out, lse, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if flush is not None:
+            flush.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)  # us
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # warm: back-to-back calls, one event pair around all of them
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) * 1e3 / steps
+    alg = algorithmic(inp)
+    return dict(inp=inp, plan=plan, times=times, wall=wall, warm_us=warm_us, alg=alg)
+
+
+def cpu_baseline(inp, target_s):
+    """Time the fp64 oracle as it stands on a bounded sample of rows."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    R = inp.q.shape[0]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(R)
+    done, t0 = 0, time.perf_counter()
+    chunk = 8
+    while done < R and time.perf_counter() - t0 < target_s:
+        rows = np.sort(order[done:done + chunk])
+        oracle.sparse_mla_fwd_torch(inp.q, inp.pool, inp.kv_scale, inp.indices, inp.sm_scale,
+                                    rows=rows)
+        done += len(rows)
+        chunk = min(2 * chunk, 256)
+    el = time.perf_counter() - t0
+    us_per_call = el / done * R * 1e6
+    return {"value": round(us_per_call, 1), "unit": "us/call", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {R} rows (random, seed 0) in {el:.1f} s, scaled by {R}/{done} "
+                      f"to one call; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the forward has no cross-GPU "
+              "path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    from sparse_mla_attention_05_amd import _lib
+    _lib.load()  # fails loudly if the HIP library is not built
+
+    cold = not args.warm
+    head = time_workload(args.workload, args.steps, args.warmup, cold)
+    times = head["times"]
+    us = statistics.median(times)
+    alg = head["alg"]
+    # dominant kernel: the attention kernel (the whole call when splits == 1)
+    kernel_us = us
+    achieved = alg["bytes"] / (kernel_us * 1e-6) / 1e9
+    w = head["inp"].workload
+    line = {
+        "metric": "sparse MLA us/call; HBM TB/s (decode) and MFMA TFLOP/s (prefill), 1 GPU",
+        "value": round(us, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 MFMA, fp32 accumulate/softmax, fp8 e4m3fn KV" if w.kv_dtype == "fp8"
+                 else "bf16 MFMA, fp32 accumulate/softmax, bf16 KV",
+        "data": "synthetic (seeded, CPU-generated; no dataset or weights)",
+        "config": {
+            "workload": w.name, "description": w.description, "rows": w.rows, "heads": w.heads,
+            "d_qk": w.d_qk, "topk": w.topk, "pool_rows": w.pool_rows, "kv_dtype": w.kv_dtype,
+            "timing": "cold (1 GiB write before each call), median of device event times",
+            "plan": head["plan"],
+        },
+        "gathered_kv_tbs": round(alg["kv_bytes"] / (us * 1e-6) / 1e12, 3),
+        "alg_tbs": round(alg["bytes"] / (us * 1e-6) / 1e12, 3),
+        "tflops": round(alg["flops"] / (us * 1e-6) / 1e12, 2),
+        "us_min": round(min(times), 2),
+        "us_mean": round(statistics.mean(times), 2),
+        "warm_us_per_call": round(head["warm_us"], 2),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(w.name),
+            "bytes_per_launch": alg["bytes"],
+            "kernel": "smla::fwd_kernel (attention)",
+            "kernel_avg_us": round(kernel_us, 2),
+        },
+    }
+    prefill = []
+    for name in [s for s in args.prefill.split(",") if s]:
+        r = time_workload(name, max(3, args.steps // 2), 2, cold)
+        pus = statistics.median(r["times"])
+        tf = r["alg"]["flops"] / (pus * 1e-6) / 1e12
+        prefill.append({"workload": name, "us_per_call": round(pus, 1), "tflops": round(tf, 1),
+                        "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "warm_us_per_call": round(r["warm_us"], 1), "plan": r["plan"],
+                        "gathered_kv_tbs": round(r["alg"]["kv_bytes"] / (pus * 1e-6) / 1e12, 2)})
+        del r
+    if prefill:
+        line["prefill"] = prefill
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(head["inp"], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

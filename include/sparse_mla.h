@@ -1,0 +1,160 @@
+/*
+ * sparse_mla.h - C ABI of the gfx950 sparse multi-head latent attention (MLA)
+ * forward library (libsparse_mla.so).
+ *
+ * The operation. For query row r, head h and the row's K int32 slot indices
+ * idx[r, 0..K) into a pool of shared latent KV rows (one row serves every
+ * head, which is what makes it MLA):
+ *
+ *   s_j      = sm_scale * q[r,h,:D_qk] . K[idx[r,j], :D_qk]        valid j only
+ *   out[r,h] = sum_j softmax(s)_j * V[idx[r,j]]       V = the row's first 512
+ *   lse[r,h] = ln sum_j exp(s_j)
+ *
+ * A slot with a negative index is invalid and masked. A row with no valid
+ * slot gives out = 0 and lse = -inf. Pool rows are 576 wide (512 latent + 64
+ * rope) or 512 wide (rope-free), stored as bf16 or as float8_e4m3fn codes
+ * with one fp32 per-tensor scale (value = code * scale, for K and V alike).
+ * Sources: "[Triton/Gluon] GFX950 sparse mla optimizations" (aiter PR 6159),
+ * Technical Details (row widths, cache formats, index counts) and the commit
+ * notes on the 64-head program (rope dotted after the latent part), the
+ * per-tensor fp8 route (per-tensor scale, V scale taken off in the epilogue),
+ * the split-K reduce, and the sentinel slots of the walk.
+ *
+ * Conventions (after the status-code and dtype-code precedents of "aiter
+ * PR 6563" (dense MLA decode planner notes: int status enum, ctypes packers
+ * cast it) and "aiter PR 7183" (explicit fp8 dtype checks, is_supported)):
+ *   - every entry point returns an int status (smla_status); nothing throws;
+ *   - all tensors are caller-owned device memory described by smla_tensor;
+ *     the library never frees caller memory;
+ *   - arguments are validated on the host before any HIP call;
+ *   - work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream); no host synchronisation and no device->host copy on the
+ *     call path, except a one-time workspace growth (see sparse_mla_fwd_ex).
+ */
+#ifndef SPARSE_MLA_H
+#define SPARSE_MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_API __attribute__((visibility("default")))
+
+/* Element type codes. One-byte storage alone does not say which fp8 flavour
+ * it is, so the caller names it: only OCP float8_e4m3fn is accepted. */
+typedef enum smla_dtype {
+  SMLA_BF16 = 0,
+  SMLA_FP8_E4M3FN = 1,
+  SMLA_FP32 = 2,
+  SMLA_INT32 = 3
+} smla_dtype;
+
+typedef enum smla_status {
+  SMLA_OK = 0,
+  SMLA_ERR_INVALID_ARG = 1, /* null pointer, bad rank/dtype/stride/shape mismatch */
+  SMLA_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels cover */
+  SMLA_ERR_HIP = 3          /* a HIP call or kernel launch failed */
+} smla_status;
+
+/* A strided tensor view of caller memory. Strides are in elements. Only the
+ * first `ndim` entries of shape/stride are read. */
+typedef struct smla_tensor {
+  void* data;
+  int32_t dtype; /* smla_dtype */
+  int32_t ndim;
+  int64_t shape[3];
+  int64_t stride[3];
+} smla_tensor;
+
+/* Overrides for tests and benchmarks; zero-initialise for the defaults. */
+typedef struct smla_options {
+  int32_t head_block;      /* 0 = planner's choice, else 16, 32 or 64 heads per workgroup */
+  int32_t splits;          /* 0 = planner's choice, else 1..64 splits of each row's slots */
+  int32_t remap;           /* 0 = planner's choice, 1 = XCD-aware order, 2 = grid order */
+  int32_t reserved;
+  void* workspace;         /* optional caller device buffer for split partials */
+  int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
+} smla_options;
+
+/* What the planner picked for a call (sparse_mla_plan). */
+typedef struct smla_plan {
+  int32_t head_block;      /* heads per workgroup: 16, 32 or 64 */
+  int32_t head_blocks;     /* ceil(H / head_block) */
+  int32_t splits;          /* splits of each row's K slots (1 = no combine kernel) */
+  int32_t remap;           /* 1 = XCD-aware work order, 0 = grid order */
+  int32_t waves;           /* wavefronts per workgroup */
+  int32_t lds_bytes;       /* LDS per workgroup */
+  int32_t tiles_per_split; /* 64-slot tiles walked by one workgroup */
+  int32_t reserved;
+  int64_t grid;            /* workgroups of the attention kernel */
+  int64_t workspace_bytes; /* split partials (0 when splits == 1) */
+} smla_plan;
+
+/*
+ * sparse_mla_fwd - the forward pass.
+ *
+ *  q        bf16 [R, H, D_qk]; last dim contiguous; row and head strides free.
+ *  kv_pool  bf16 or fp8 e4m3fn [N, W], W >= D_qk (only the first D_qk columns
+ *           are read, so a padded row pitch needs no copy); last dim
+ *           contiguous; the row stride in bytes must be a multiple of 16 and
+ *           the base 16-byte aligned.
+ *  kv_scale fp32 [1] device pointer, given iff kv_pool is fp8 (NULL for bf16).
+ *  indices  int32 [R, K]; last dim contiguous; any negative value is an
+ *           invalid slot. Values >= N are a caller error: not checked on the
+ *           device, the result is then undefined.
+ *  sm_scale softmax scale applied to q.k.
+ *  out      bf16 [R, H, 512]; last dim contiguous; fully written.
+ *  lse      fp32 [R, H]; fully written (natural log; -inf for empty rows).
+ *
+ * D_qk must be 576 or 512; H in [1, 1024]; K in [1, 2^20]; R >= 0 (R == 0 is
+ * a no-op returning SMLA_OK); q rows, out rows and pool rows 16-byte aligned.
+ * out and lse must not alias any input. The same inputs and the same plan give
+ * bitwise-identical outputs.
+ */
+SMLA_API int sparse_mla_fwd(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
+                   const smla_tensor* indices, float sm_scale, smla_tensor* out, smla_tensor* lse,
+                   void* stream);
+
+/*
+ * sparse_mla_fwd_ex - sparse_mla_fwd with planner overrides and an optional
+ * caller workspace (opt may be NULL). With splits > 1 the partial outputs go
+ * to opt->workspace when given, else to a library-owned per-device buffer that
+ * grows on demand (growth synchronises the device once; the buffer is kept
+ * until process exit and is shared by calls on that device, so concurrent
+ * split calls on different streams of one device must pass their own
+ * workspace).
+ */
+SMLA_API int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
+                      const smla_tensor* indices, float sm_scale, smla_tensor* out, smla_tensor* lse,
+                      void* stream, const smla_options* opt);
+
+/* 1 if the shapes/dtypes/strides are covered by the kernels, else 0 (the
+ * reason is left in sparse_mla_last_error). Host-only; makes no HIP call. */
+SMLA_API int sparse_mla_is_supported(const smla_tensor* q, const smla_tensor* kv_pool,
+                            const smla_tensor* indices);
+
+/* The launch the forward would make for these shapes (opt may be NULL).
+ * Host-only; makes no HIP call. Returns a status. `num_cus` is the compute
+ * unit count to plan for (0 = 256, an MI355X). */
+SMLA_API int sparse_mla_plan(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* indices,
+                    const smla_options* opt, int32_t num_cus, smla_plan* plan_out);
+
+/* Work-order map used by the attention kernel: the work item that workgroup
+ * `pid` of a `grid`-workgroup launch processes, with the XCD-aware order
+ * (remap = 1) or grid order (remap = 0). Host-side copy of the device map,
+ * exported so the order can be checked without a GPU. Returns -1 on bad input. */
+SMLA_API int64_t sparse_mla_work_of(int64_t pid, int64_t grid, int32_t remap);
+
+/* Thread-local text for the last non-OK status of the calling thread. */
+SMLA_API const char* sparse_mla_last_error(void);
+
+/* Library version, "major.minor.patch". */
+SMLA_API const char* sparse_mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MLA_H */

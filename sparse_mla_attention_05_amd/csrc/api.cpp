@@ -1,0 +1,341 @@
+// C ABI of libsparse_mla.so: argument validation (host only, before any HIP
+// call), planning, workspace management and launch. See include/sparse_mla.h
+// for the contract.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "launch.h"
+#include "work_order.h"
+
+namespace smla {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+const char* dtype_name(int32_t d) {
+  switch (d) {
+    case SMLA_BF16: return "bf16";
+    case SMLA_FP8_E4M3FN: return "fp8_e4m3fn";
+    case SMLA_FP32: return "fp32";
+    case SMLA_INT32: return "int32";
+    default: return "unknown";
+  }
+}
+
+int elem_size(int32_t d) {
+  switch (d) {
+    case SMLA_BF16: return 2;
+    case SMLA_FP8_E4M3FN: return 1;
+    case SMLA_FP32: return 4;
+    case SMLA_INT32: return 4;
+    default: return 0;
+  }
+}
+
+// Structural checks shared by every tensor argument.
+int check_tensor(const smla_tensor* t, const char* name, int ndim, int32_t dtype) {
+  if (!t) return fail(SMLA_ERR_INVALID_ARG, std::string(name) + ": null descriptor");
+  if (t->ndim != ndim)
+    return fail(SMLA_ERR_INVALID_ARG, std::string(name) + ": expected " + std::to_string(ndim) +
+                                          " dims, got " + std::to_string(t->ndim));
+  if (t->dtype != dtype)
+    return fail(SMLA_ERR_UNSUPPORTED, std::string(name) + ": dtype " + dtype_name(t->dtype) +
+                                          " (code " + std::to_string(t->dtype) +
+                                          ") not supported, expected " + dtype_name(dtype));
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0)
+      return fail(SMLA_ERR_INVALID_ARG, std::string(name) + ": negative extent");
+    if (t->stride[i] < 0)
+      return fail(SMLA_ERR_INVALID_ARG, std::string(name) + ": negative stride");
+  }
+  if (t->shape[ndim - 1] > 1 && t->stride[ndim - 1] != 1)
+    return fail(SMLA_ERR_UNSUPPORTED, std::string(name) + ": last dimension must be contiguous");
+  return SMLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [lo, hi) touched by a strided tensor (empty if any extent is 0).
+void extent(const smla_tensor* t, uintptr_t* lo, uintptr_t* hi) {
+  int64_t last = 0;
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] == 0) {
+      *lo = *hi = 0;
+      return;
+    }
+    last += (t->shape[i] - 1) * t->stride[i];
+  }
+  *lo = reinterpret_cast<uintptr_t>(t->data);
+  *hi = *lo + uintptr_t((last + 1) * elem_size(t->dtype));
+}
+
+bool overlap(const smla_tensor* a, const smla_tensor* b) {
+  uintptr_t alo, ahi, blo, bhi;
+  extent(a, &alo, &ahi);
+  extent(b, &blo, &bhi);
+  if (alo == ahi || blo == bhi) return false;
+  return alo < bhi && blo < ahi;
+}
+
+struct Checked {
+  Problem pb;
+  bool fp8;
+};
+
+// q / kv_pool / indices: shapes, dtypes, strides, alignment.
+int validate_inputs(const smla_tensor* q, const smla_tensor* kv, const smla_tensor* idx,
+                    Checked* c) {
+  int s;
+  if ((s = check_tensor(q, "q", 3, SMLA_BF16))) return s;
+  if (!kv) return fail(SMLA_ERR_INVALID_ARG, "kv_pool: null descriptor");
+  if (kv->dtype != SMLA_BF16 && kv->dtype != SMLA_FP8_E4M3FN)
+    return fail(SMLA_ERR_UNSUPPORTED, std::string("kv_pool: dtype ") + dtype_name(kv->dtype) +
+                                          " (code " + std::to_string(kv->dtype) +
+                                          ") not supported, expected bf16 or fp8_e4m3fn");
+  if ((s = check_tensor(kv, "kv_pool", 2, kv->dtype))) return s;
+  if ((s = check_tensor(idx, "indices", 2, SMLA_INT32))) return s;
+
+  const int64_t R = q->shape[0], H = q->shape[1], D = q->shape[2];
+  if (D != 576 && D != 512)
+    return fail(SMLA_ERR_UNSUPPORTED, "q: D_qk must be 576 or 512, got " + std::to_string(D));
+  if (H < 1 || H > kMaxHeads)
+    return fail(SMLA_ERR_UNSUPPORTED, "q: heads must be in [1, 1024], got " + std::to_string(H));
+  if (idx->shape[0] != R)
+    return fail(SMLA_ERR_INVALID_ARG, "indices: rows " + std::to_string(idx->shape[0]) +
+                                          " != q rows " + std::to_string(R));
+  const int64_t K = idx->shape[1];
+  if (K < 1 || K > kMaxTopk)
+    return fail(SMLA_ERR_UNSUPPORTED, "indices: top-k must be in [1, 2^20], got " +
+                                          std::to_string(K));
+  if (kv->shape[1] < D)
+    return fail(SMLA_ERR_INVALID_ARG, "kv_pool: row width " + std::to_string(kv->shape[1]) +
+                                          " < D_qk " + std::to_string(D));
+  if (R > 0 && kv->shape[0] < 1) return fail(SMLA_ERR_INVALID_ARG, "kv_pool: no rows");
+  if (R > 0) {
+    if (!q->data) return fail(SMLA_ERR_INVALID_ARG, "q: null data");
+    if (!kv->data) return fail(SMLA_ERR_INVALID_ARG, "kv_pool: null data");
+    if (!idx->data) return fail(SMLA_ERR_INVALID_ARG, "indices: null data");
+  }
+  const int eb = elem_size(kv->dtype);
+  if (kv->shape[0] > 1 && kv->stride[0] < kv->shape[1])
+    return fail(SMLA_ERR_INVALID_ARG, "kv_pool: row stride smaller than row width");
+  if (!aligned16(kv->data) || (kv->stride[0] * eb) % 16 != 0)
+    return fail(SMLA_ERR_UNSUPPORTED, "kv_pool: base and row stride must be 16-byte aligned");
+  if (!aligned16(q->data) || (q->stride[0] * 2) % 16 != 0 || (q->stride[1] * 2) % 16 != 0)
+    return fail(SMLA_ERR_UNSUPPORTED, "q: base, row and head strides must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(idx->data) & 3u) != 0)
+    return fail(SMLA_ERR_INVALID_ARG, "indices: base must be 4-byte aligned");
+  if (kv->shape[0] > (int64_t(1) << 31))
+    return fail(SMLA_ERR_UNSUPPORTED, "kv_pool: more than 2^31 rows");
+  c->pb.rows = R;
+  c->pb.heads = int32_t(H);
+  c->pb.dqk = int32_t(D);
+  c->pb.topk = int32_t(K);
+  c->pb.kv_fp8 = kv->dtype == SMLA_FP8_E4M3FN;
+  c->fp8 = c->pb.kv_fp8 != 0;
+  return SMLA_OK;
+}
+
+int validate_all(const smla_tensor* q, const smla_tensor* kv, const smla_tensor* scale,
+                 const smla_tensor* idx, float sm_scale, const smla_tensor* out,
+                 const smla_tensor* lse, Checked* c) {
+  int s;
+  if ((s = validate_inputs(q, kv, idx, c))) return s;
+  const int64_t R = c->pb.rows, H = c->pb.heads;
+  if (c->fp8) {
+    if (!scale || !scale->data)
+      return fail(SMLA_ERR_INVALID_ARG, "kv_scale: required for an fp8 pool");
+    if ((s = check_tensor(scale, "kv_scale", 1, SMLA_FP32))) return s;
+    if (scale->shape[0] < 1) return fail(SMLA_ERR_INVALID_ARG, "kv_scale: empty");
+  } else if (scale && scale->data) {
+    return fail(SMLA_ERR_INVALID_ARG, "kv_scale: must be NULL for a bf16 pool");
+  }
+  if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_INVALID_ARG, "sm_scale: not finite");
+  if ((s = check_tensor(out, "out", 3, SMLA_BF16))) return s;
+  if ((s = check_tensor(lse, "lse", 2, SMLA_FP32))) return s;
+  if (out->shape[0] != R || out->shape[1] != H || out->shape[2] != kDv)
+    return fail(SMLA_ERR_INVALID_ARG, "out: shape must be [R, H, 512]");
+  if (lse->shape[0] != R || lse->shape[1] != H)
+    return fail(SMLA_ERR_INVALID_ARG, "lse: shape must be [R, H]");
+  if (R > 0) {
+    if (!out->data) return fail(SMLA_ERR_INVALID_ARG, "out: null data");
+    if (!lse->data) return fail(SMLA_ERR_INVALID_ARG, "lse: null data");
+    if ((reinterpret_cast<uintptr_t>(out->data) & 7u) != 0 || (out->stride[0] * 2) % 8 != 0 ||
+        (out->stride[1] * 2) % 8 != 0)
+      return fail(SMLA_ERR_UNSUPPORTED, "out: base, row and head strides must be 8-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse->data) & 3u) != 0)
+      return fail(SMLA_ERR_INVALID_ARG, "lse: base must be 4-byte aligned");
+    const smla_tensor* ins[4] = {q, kv, idx, c->fp8 ? scale : nullptr};
+    for (const smla_tensor* in : ins) {
+      if (!in) continue;
+      if (overlap(out, in) || overlap(lse, in))
+        return fail(SMLA_ERR_INVALID_ARG, "out/lse must not alias an input");
+    }
+    if (overlap(out, lse)) return fail(SMLA_ERR_INVALID_ARG, "out and lse overlap");
+  }
+  return SMLA_OK;
+}
+
+// Library-owned split workspace, one per device, grown on demand. Growth
+// synchronises the device before releasing the old buffer, so no in-flight
+// kernel still reads it.
+struct Workspace {
+  void* ptr = nullptr;
+  int64_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+Workspace g_ws[64];
+
+int device_workspace(int dev, int64_t need, void** out) {
+  if (dev < 0 || dev >= 64) return fail(SMLA_ERR_UNSUPPORTED, "device id beyond 63");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[dev];
+  if (w.bytes < need) {
+    hipError_t e;
+    if (w.ptr) {
+      if ((e = hipDeviceSynchronize()) != hipSuccess)
+        return fail(SMLA_ERR_HIP, std::string("hipDeviceSynchronize: ") + hipGetErrorString(e));
+      if ((e = hipFree(w.ptr)) != hipSuccess)
+        return fail(SMLA_ERR_HIP, std::string("hipFree: ") + hipGetErrorString(e));
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const int64_t grow = std::max<int64_t>(need, 2 * w.bytes);
+    if ((e = hipMalloc(&w.ptr, size_t(grow))) != hipSuccess) {
+      w.ptr = nullptr;
+      return fail(SMLA_ERR_HIP, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
+    }
+    w.bytes = grow;
+  }
+  *out = w.ptr;
+  return SMLA_OK;
+}
+
+int g_cu_count[64] = {0};
+
+int device_cus(int dev) {
+  if (dev < 0 || dev >= 64) return 256;
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
+}
+
+}  // namespace
+}  // namespace smla
+
+using namespace smla;
+
+extern "C" {
+
+int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
+                      const smla_tensor* kv_scale, const smla_tensor* indices, float sm_scale,
+                      smla_tensor* out, smla_tensor* lse, void* stream,
+                      const smla_options* opt) {
+  Checked c;
+  int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c);
+  if (s) return s;
+  if (c.pb.rows == 0) return SMLA_OK;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  smla_plan plan;
+  const char* perr = nullptr;
+  if ((s = make_plan(c.pb, opt, device_cus(dev), &plan, &perr))) return fail(s, perr);
+
+  FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.q_rs = q->stride[0];
+  p.q_hs = q->stride[1];
+  p.pool = static_cast<const uint8_t*>(kv_pool->data);
+  p.pool_rs_bytes = kv_pool->stride[0] * elem_size(kv_pool->dtype);
+  p.kv_scale = c.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr;
+  p.idx = static_cast<const int32_t*>(indices->data);
+  p.idx_rs = indices->stride[0];
+  p.out = static_cast<uint16_t*>(out->data);
+  p.out_rs = out->stride[0];
+  p.out_hs = out->stride[1];
+  p.lse = static_cast<float*>(lse->data);
+  p.lse_rs = lse->stride[0];
+  p.lse_hs = lse->stride[1];
+  p.rows = c.pb.rows;
+  p.heads = c.pb.heads;
+  p.topk = c.pb.topk;
+  p.splits = plan.splits;
+  p.tiles_per_split = plan.tiles_per_split;
+  p.head_blocks = plan.head_blocks;
+  p.remap = plan.remap;
+  p.grid = plan.grid;
+  p.sm_log2 = sm_scale * 1.4426950408889634f;
+
+  if (plan.splits > 1) {
+    void* ws = nullptr;
+    if (opt && opt->workspace) {
+      if (opt->workspace_bytes < plan.workspace_bytes)
+        return fail(SMLA_ERR_INVALID_ARG, "workspace smaller than the plan needs (" +
+                                              std::to_string(plan.workspace_bytes) + " bytes)");
+      if (!aligned16(opt->workspace))
+        return fail(SMLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+      ws = opt->workspace;
+    } else if ((s = device_workspace(dev, plan.workspace_bytes, &ws))) {
+      return s;
+    }
+    const int64_t o_bytes = int64_t(plan.splits) * c.pb.rows * c.pb.heads * kDv * 4;
+    p.part_o = static_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + (o_bytes + 255) / 256 * 256);
+  }
+  const int le = launch_forward(p, plan, c.pb.dqk, c.fp8, stream);
+  if (le != 0)
+    return fail(SMLA_ERR_HIP, std::string("kernel launch: ") +
+                                  hipGetErrorString(static_cast<hipError_t>(le)));
+  return SMLA_OK;
+}
+
+int sparse_mla_fwd(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
+                   const smla_tensor* indices, float sm_scale, smla_tensor* out, smla_tensor* lse,
+                   void* stream) {
+  return sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream, nullptr);
+}
+
+int sparse_mla_is_supported(const smla_tensor* q, const smla_tensor* kv_pool,
+                            const smla_tensor* indices) {
+  Checked c;
+  return validate_inputs(q, kv_pool, indices, &c) == SMLA_OK ? 1 : 0;
+}
+
+int sparse_mla_plan(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* indices,
+                    const smla_options* opt, int32_t num_cus, smla_plan* plan_out) {
+  if (!plan_out) return fail(SMLA_ERR_INVALID_ARG, "plan_out: null");
+  Checked c;
+  int s = validate_inputs(q, kv_pool, indices, &c);
+  if (s) return s;
+  const char* perr = nullptr;
+  s = make_plan(c.pb, opt, num_cus, plan_out, &perr);
+  return s ? fail(s, perr) : SMLA_OK;
+}
+
+int64_t sparse_mla_work_of(int64_t pid, int64_t grid, int32_t remap) {
+  if (grid <= 0 || pid < 0 || pid >= grid) return -1;
+  return remap ? smla_xcd_work(pid, grid) : pid;
+}
+
+const char* sparse_mla_last_error(void) { return g_last_error.c_str(); }
+
+const char* sparse_mla_version(void) { return "0.1.0"; }
+
+}  // extern "C"

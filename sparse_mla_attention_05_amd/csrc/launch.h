@@ -1,0 +1,64 @@
+// Internal interface between the host API (api.cpp), the planner (plan.cpp)
+// and the kernels (kernels.hip). Not part of the public C ABI.
+#pragma once
+#include <stdint.h>
+
+#include "../../include/sparse_mla.h"
+
+namespace smla {
+
+constexpr int kTileKeys = 64;   // KV slots per tile walked by a workgroup
+constexpr int kDv = 512;        // value width: the first 512 columns of a row
+constexpr int kMaxSplits = 64;
+constexpr int kMaxHeads = 1024;
+constexpr int64_t kMaxTopk = int64_t(1) << 20;
+
+// Everything the attention kernel reads, with strides in elements except
+// where named "_bytes".
+struct FwdParams {
+  const uint16_t* q;        // bf16 [R, H, Dqk]
+  int64_t q_rs, q_hs;
+  const uint8_t* pool;      // bf16 or e4m3fn rows
+  int64_t pool_rs_bytes;
+  const float* kv_scale;    // fp32 [1] (fp8 pools) or nullptr
+  const int32_t* idx;       // int32 [R, K]
+  int64_t idx_rs;
+  uint16_t* out;            // bf16 [R, H, 512]
+  int64_t out_rs, out_hs;
+  float* lse;               // fp32 [R, H]
+  int64_t lse_rs, lse_hs;
+  float* part_o;            // fp32 [S, R, H, 512] when splits > 1
+  float* part_lse;          // fp32 [S, R, H]
+  int64_t rows;
+  int32_t heads;
+  int32_t topk;
+  int32_t splits;
+  int32_t tiles_per_split;
+  int32_t head_blocks;
+  int32_t remap;
+  int64_t grid;
+  float sm_log2;            // sm_scale * log2(e)
+};
+
+struct Problem {
+  int64_t rows;
+  int32_t heads;
+  int32_t dqk;
+  int32_t topk;
+  int32_t kv_fp8;
+};
+
+// Per-workgroup LDS and wave count of the kernel instance for (head_block, dqk).
+int kernel_waves(int head_block);
+int kernel_lds_bytes(int head_block, int dqk);
+
+// Pure host planner: no HIP calls. Returns SMLA_OK or an error status and
+// fills `err` with the reason.
+int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan* plan,
+              const char** err);
+
+// Launches the attention kernel (and the combine kernel when splits > 1) on
+// `stream`. Returns 0 or a hipError_t value.
+int launch_forward(const FwdParams& p, const smla_plan& plan, int dqk, bool fp8, void* stream);
+
+}  // namespace smla

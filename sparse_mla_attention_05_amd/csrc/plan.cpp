@@ -1,0 +1,108 @@
+// Host-only launch planner for the sparse MLA forward. No HIP calls, so it is
+// unit-testable on a machine without a GPU.
+//
+// Choices, after the launcher rules described in "[Triton/Gluon] GFX950
+// sparse mla optimizations" (aiter PR 6159) commit notes (program size by
+// head count and rounds of programs; split count sized so small launches fill
+// the CUs; XCD remap only for rows of two or more head blocks), re-derived for
+// this kernel:
+//  * head block: 16 heads for H <= 16, 32 for H <= 32, else 64, so one
+//    workgroup gathers and stages each KV tile once for as many heads as fit.
+//  * splits: when rows x head blocks leaves the CUs' workgroup slots
+//    underfilled, each row's slots are split (each split keeping >= 2 tiles)
+//    until about two rounds of workgroups fill the slots; the combine kernel
+//    then merges the partials.
+//  * remap: XCD-aware order when a row has >= 2 head blocks or >= 2 splits,
+//    so the workgroups that read the same KV rows share an L2.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "launch.h"
+
+namespace smla {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan* plan,
+              const char** err) {
+  static const char* kBadHb = "head_block override must be 0, 16, 32 or 64";
+  static const char* kBadSplit = "splits override must be in [0, 64]";
+  static const char* kBadRemap = "remap override must be 0, 1 or 2";
+  static const char* kBadGrid = "launch grid exceeds 2^31 - 1 workgroups";
+  if (num_cus <= 0) num_cus = 256;
+  *plan = smla_plan{};
+
+  int hb = 0;
+  if (opt && opt->head_block) {
+    if (opt->head_block != 16 && opt->head_block != 32 && opt->head_block != 64) {
+      *err = kBadHb;
+      return SMLA_ERR_INVALID_ARG;
+    }
+    hb = opt->head_block;
+  } else {
+    hb = pb.heads <= 16 ? 16 : (pb.heads <= 32 ? 32 : 64);
+  }
+  const int waves = kernel_waves(hb);
+  const int lds = kernel_lds_bytes(hb, pb.dqk);
+  const int64_t head_blocks = ceil_div(pb.heads, hb);
+  const int64_t tiles = ceil_div(pb.topk, kTileKeys);
+
+  // Workgroups a CU holds at once: 160 KB of LDS and 8 waves (the kernels
+  // need up to 256 VGPRs, i.e. 2 waves per SIMD).
+  const int64_t by_lds = std::max<int64_t>(1, (160 * 1024) / lds);
+  const int64_t by_waves = std::max<int64_t>(1, 8 / waves);
+  const int64_t wg_per_cu = std::min(by_lds, by_waves);
+  const int64_t slots = int64_t(num_cus) * wg_per_cu;
+  const int64_t base = pb.rows * head_blocks;
+
+  int64_t splits = 1;
+  if (opt && opt->splits) {
+    if (opt->splits < 0 || opt->splits > kMaxSplits) {
+      *err = kBadSplit;
+      return SMLA_ERR_INVALID_ARG;
+    }
+    splits = std::min<int64_t>(opt->splits, tiles);
+  } else if (base > 0 && base < slots) {
+    const int64_t want = ceil_div(2 * slots, base);
+    const int64_t cap = std::max<int64_t>(1, tiles / 2);
+    splits = std::max<int64_t>(1, std::min<int64_t>({want, cap, int64_t(kMaxSplits)}));
+  }
+  // No empty splits: every split walks at least one tile.
+  const int64_t tps = ceil_div(tiles, splits);
+  splits = ceil_div(tiles, tps);
+
+  int remap;
+  if (opt && opt->remap) {
+    if (opt->remap != 1 && opt->remap != 2) {
+      *err = kBadRemap;
+      return SMLA_ERR_INVALID_ARG;
+    }
+    remap = opt->remap == 1 ? 1 : 0;
+  } else {
+    remap = (head_blocks >= 2 || splits >= 2) ? 1 : 0;
+  }
+
+  const int64_t grid = base * splits;
+  if (grid > int64_t(0x7fffffff) || pb.rows * pb.heads > int64_t(0x7fffffff)) {
+    *err = kBadGrid;
+    return SMLA_ERR_UNSUPPORTED;
+  }
+
+  plan->head_block = hb;
+  plan->head_blocks = int32_t(head_blocks);
+  plan->splits = int32_t(splits);
+  plan->remap = remap;
+  plan->waves = waves;
+  plan->lds_bytes = lds;
+  plan->tiles_per_split = int32_t(tps);
+  plan->grid = grid;
+  if (splits > 1) {
+    const int64_t o_bytes = splits * pb.rows * pb.heads * kDv * 4;
+    const int64_t l_bytes = splits * pb.rows * pb.heads * 4;
+    plan->workspace_bytes = ceil_div(o_bytes, 256) * 256 + ceil_div(l_bytes, 256) * 256;
+  }
+  return SMLA_OK;
+}
+
+}  // namespace smla

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar (per element over the whole output): max |out - ref| <= 2e-2 and
+||out - ref||_F / ||ref||_F <= 5e-3 for the bf16 output; |lse - ref| <= 1e-3 on
+every (row, head) with a valid slot; rows without a valid slot exactly out = 0
+and lse = -inf. Every call writes into NaN-poisoned out/lse buffers, so an
+element the kernel forgets to write fails the check.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_05_amd import _lib
+from sparse_mla_attention_05_amd.inputs import custom_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+OUT_MAX_ABS = 2e-2
+OUT_REL_FRO = 5e-3
+LSE_ABS = 1e-3
+
+
+def _dev(inp):
+    q = inp.q.cuda()
+    pool = inp.pool.cuda()
+    scale = inp.kv_scale.cuda() if inp.kv_scale is not None else None
+    idx = inp.indices.cuda()
+    return q, pool, scale, idx
+
+
+def run_gpu(inp, dev=None, out_like=None, **opts):
+    q, pool, scale, idx = dev or _dev(inp)
+    R, H = q.shape[0], q.shape[1]
+    out = torch.full((R, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((R, H), float("nan"), dtype=torch.float32, device="cuda")
+    if out_like is not None:
+        out = out_like
+        out.fill_(float("nan"))
+    if opts:
+        _lib.sparse_mla_fwd_ex(q, pool, scale, idx, inp.sm_scale, out, lse, **opts)
+    else:
+        _lib.sparse_mla_fwd(q, pool, scale, idx, inp.sm_scale, out, lse)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def run_oracle(inp, rows=None):
+    return oracle.sparse_mla_fwd_torch(inp.q, inp.pool, inp.kv_scale, inp.indices, inp.sm_scale,
+                                       rows=rows)
+
+
+def assert_parity(out, lse, ref_out, ref_lse, indices, rows=None):
+    """out/lse: GPU results for `rows` (all rows if None); ref_*: oracle."""
+    if rows is not None:
+        out, lse, indices = out[rows], lse[rows], indices[rows]
+    o = out.to(torch.float64).numpy()
+    l_ = lse.to(torch.float64).numpy()
+    assert not np.isnan(o).any(), "NaN in output (unwritten or poisoned element)"
+    assert not np.isnan(l_).any(), "NaN in lse"
+    has_valid = (indices >= 0).any(dim=1).numpy()
+    empty = ~has_valid
+    if empty.any():
+        assert np.all(o[empty] == 0.0), "row without valid slot must give out = 0"
+        assert np.all(l_[empty] == -np.inf), "row without valid slot must give lse = -inf"
+    if has_valid.any():
+        d = o[has_valid] - ref_out[has_valid]
+        max_abs = float(np.max(np.abs(d)))
+        rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref_out[has_valid]), 1e-30))
+        lse_err = float(np.max(np.abs(l_[has_valid] - ref_lse[has_valid])))
+        assert max_abs <= OUT_MAX_ABS, f"max abs {max_abs}"
+        assert rel <= OUT_REL_FRO, f"relative Frobenius {rel}"
+        assert lse_err <= LSE_ABS, f"lse error {lse_err}"
+        return dict(max_abs=max_abs, rel_fro=rel, lse_err=lse_err)
+    return {}
+
+
+def _check(inp, **opts):
+    out, lse = run_gpu(inp, **opts)
+    ref_out, ref_lse = run_oracle(inp)
+    return assert_parity(out, lse, ref_out, ref_lse, inp.indices)
+
+
+# ---------------------------------------------------------- the workloads
+
+@pytest.mark.parametrize("name", ["tiny", "decode_bf16", "decode_fp8"])
+def test_workload_full_parity(name):
+    print(f"\n[parity] workload={name}", flush=True)
+    inp = make_inputs(name)
+    stats = _check(inp)
+    print(f"[parity] {name}: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["prefill_fp8", "prefill_glm"])
+def test_prefill_parity_on_sampled_rows(name):
+    """The whole workload runs in the launch the benchmark times; the oracle
+    checks every 64th row plus the last one."""
+    print(f"\n[parity] workload={name} (sampled rows)", flush=True)
+    inp = make_inputs(name)
+    out, lse = run_gpu(inp)
+    R = inp.q.shape[0]
+    rows = np.unique(np.r_[np.arange(0, R, 64), R - 1])
+    ref_out, ref_lse = run_oracle(inp, rows=rows)
+    stats = assert_parity(out, lse, ref_out, ref_lse, inp.indices, rows=torch.from_numpy(rows))
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    print(f"[parity] {name}: {stats}", flush=True)
+
+
+# ------------------------------------------------------------- edge cases
+
+def _case(**kw):
+    base = dict(rows=6, heads=16, d_qk=576, pool_rows=3000, topk=256, kv_dtype="bf16", seed=31)
+    base.update(kw)
+    return make_inputs(custom_workload(**base))
+
+
+@pytest.mark.parametrize("valid", [1, 2, 63, 64, 65, 127, 128, 129, 191, 192])
+def test_valid_count_on_tile_edges(valid):
+    inp = _case(topk=192, seed=valid)
+    idx = inp.indices.clone()
+    idx[:, valid:] = -1
+    inp.indices = idx
+    _check(inp)
+
+
+@pytest.mark.parametrize("topk", [1, 31, 63, 64, 65, 129, 300])
+def test_topk_on_tile_edges(topk):
+    _check(_case(topk=topk, pool_rows=4096, seed=topk, invalid_per_row=min(3, topk - 1)))
+
+
+def test_invalid_every_other_slot_and_leading_tiles():
+    inp = _case(topk=384, kv_dtype="fp8")
+    idx = inp.indices.clone()
+    idx[0:3, ::2] = -1             # every other slot
+    idx[3:5, :192] = -1            # three whole leading tiles
+    idx[5, :] = -5                 # a row with no valid slot
+    inp.indices = idx
+    _check(inp)
+    _check(inp, splits=3)
+
+
+def test_all_invalid_split_and_rows():
+    inp = _case(topk=512)
+    idx = inp.indices.clone()
+    idx[1, 128:256] = -1           # split 1 of 4 empty
+    idx[2, :384] = -1              # splits 0-2 empty
+    idx[4, :] = -1                 # whole row empty
+    inp.indices = idx
+    for s in (1, 4, 8):
+        _check(inp, splits=s)
+
+
+@pytest.mark.parametrize("heads", [1, 8, 16, 24, 32, 48, 64, 80])
+@pytest.mark.parametrize("d_qk,kv", [(576, "bf16"), (576, "fp8"), (512, "fp8"), (512, "bf16")])
+def test_heads_widths_dtypes(heads, d_qk, kv):
+    _check(_case(heads=heads, d_qk=d_qk, kv_dtype=kv, rows=5, topk=200, invalid_per_row=7,
+                 seed=heads + d_qk))
+
+
+@pytest.mark.parametrize("head_block", [16, 32, 64])
+@pytest.mark.parametrize("splits", [1, 2, 8])
+@pytest.mark.parametrize("remap", [1, 2])
+def test_forced_plans(head_block, splits, remap):
+    inp = _case(heads=40, rows=5, topk=640, kv_dtype="fp8", invalid_per_row=11, seed=head_block)
+    _check(inp, head_block=head_block, splits=splits, remap=remap)
+
+
+def test_caller_workspace():
+    inp = _case(rows=7, topk=512)
+    ws = torch.empty(8 * 7 * 16 * 513 + 1024, dtype=torch.float32, device="cuda")
+    _check(inp, splits=8, workspace=ws)
+
+
+def test_guard_row_before_pool_is_never_read():
+    """The pool view starts one row into a buffer whose first row is NaN; a read
+    of index -1 would pull the NaN row into the output."""
+    inp = _case(topk=256, invalid_per_row=40, kv_dtype="bf16")
+    q, pool, scale, idx = _dev(inp)
+    big = torch.empty((pool.shape[0] + 1, pool.shape[1]), dtype=pool.dtype, device="cuda")
+    big[0] = float("nan")
+    big[1:] = pool
+    out, lse = run_gpu(inp, dev=(q, big[1:], scale, idx))
+    ref_out, ref_lse = run_oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, inp.indices)
+
+
+def test_fp8_guard_row_and_padded_pitch():
+    w = custom_workload(rows=4, heads=16, d_qk=576, pool_rows=2000, topk=320, kv_dtype="fp8",
+                        seed=77, pool_pitch=640, invalid_per_row=33)
+    inp = make_inputs(w)
+    q, pool, scale, idx = _dev(inp)
+    big = torch.empty((pool.shape[0] + 1, pool.shape[1]), dtype=torch.uint8, device="cuda")
+    big[0] = 0x7F  # e4m3fn NaN code
+    big[1:] = pool.view(torch.uint8)
+    out, lse = run_gpu(inp, dev=(q, big[1:].view(torch.float8_e4m3fn), scale, idx))
+    ref_out, ref_lse = run_oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, inp.indices)
+
+
+def test_strided_q_and_out():
+    inp = _case(rows=5, heads=16, topk=130)
+    q, pool, scale, idx = _dev(inp)
+    qbig = torch.zeros((5, 20, 584), dtype=torch.bfloat16, device="cuda")
+    qbig[:, 2:18, :576] = q
+    qv = qbig[:, 2:18, :576]
+    outbig = torch.full((5, 17, 520), float("nan"), dtype=torch.bfloat16, device="cuda")
+    outv = outbig[:, :16, :512]
+    lse = torch.full((5, 16), float("nan"), dtype=torch.float32, device="cuda")
+    _lib.sparse_mla_fwd(qv, pool, scale, idx, inp.sm_scale, outv, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = run_oracle(inp)
+    assert_parity(outv.cpu(), lse.cpu(), ref_out, ref_lse, inp.indices)
+    assert torch.isnan(outbig[:, 16].float()).all() and torch.isnan(outbig[:, :16, 512:].float()).all()
+
+
+def test_fp8_widening_is_exact_for_every_code():
+    """One valid slot per row: out is that pool row exactly (scale 1), so each
+    finite e4m3fn code must widen to its exact value."""
+    codes = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+    pool = torch.zeros((2, 576), dtype=torch.uint8)
+    pool[0, :254] = codes
+    pool[1, :254] = codes.flip(0)
+    pool[1, 254:508] = codes
+    inp = make_inputs(custom_workload(rows=2, heads=16, d_qk=576, pool_rows=2, topk=2,
+                                      kv_dtype="fp8", seed=1))
+    inp.pool = pool.view(torch.float8_e4m3fn)
+    inp.kv_scale = torch.ones(1, dtype=torch.float32)
+    inp.indices = torch.tensor([[0, -1], [-1, 1]], dtype=torch.int32)
+    out, lse = run_gpu(inp)
+    ref = pool.view(torch.float8_e4m3fn)[:, :512].to(torch.float32)
+    assert torch.equal(out[0].float(), ref[0].expand(16, -1))
+    assert torch.equal(out[1].float(), ref[1].expand(16, -1))
+    ref_out, ref_lse = run_oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, inp.indices)
+
+
+def test_deterministic_repeat_and_permutation():
+    inp = _case(rows=8, topk=512, kv_dtype="fp8", invalid_per_row=20)
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+    g = torch.Generator().manual_seed(2)
+    perm = torch.argsort(torch.rand(inp.indices.shape, generator=g), dim=1)
+    inp2 = _case(rows=8, topk=512, kv_dtype="fp8", invalid_per_row=20)
+    inp2.indices = torch.gather(inp.indices, 1, perm).contiguous()
+    c = run_gpu(inp2)
+    ref_out, ref_lse = run_oracle(inp)
+    assert_parity(c[0], c[1], ref_out, ref_lse, inp2.indices)
+
+
+def test_large_scores_stay_finite():
+    inp = _case(rows=4, topk=256)
+    inp.q = (inp.q.float() * 30).to(torch.bfloat16)
+    _check(inp)
+
+
+def test_zero_rows_noop():
+    inp = _case(rows=1)
+    q, pool, scale, idx = _dev(inp)
+    out = torch.empty((0, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((0, 16), dtype=torch.float32, device="cuda")
+    _lib.sparse_mla_fwd(q[:0], pool, scale, idx[:0], inp.sm_scale, out, lse)
+    torch.cuda.synchronize()
