@@ -47,7 +47,23 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (to calibrate HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written, 3 times.
+    Its FETCH_SIZE / WRITE_SIZE under rocprofv3 --pmc give the factor that
+    turns those counters into HBM bytes."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": a.numel() * 4,
+                      "copy_calibration_bytes_written": b.numel() * 4}), flush=True)
 
 
 def algorithmic(inp):
@@ -166,13 +182,16 @@ def cpu_baseline(inp, target_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the forward has no cross-GPU "
+        print("bench.py: the sparse MLA forward runs on one GPU (it has no cross-GPU "
               "path); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     from sparse_mla_attention_05_amd import _lib
     _lib.load()  # fails loudly if the HIP library is not built
 

@@ -26,9 +26,10 @@ Sources on the pages:
     per-tensor fp8 two-loop route (a per-tensor scale on the cache; the V scale
     comes off in the epilogue, i.e. value = code * kv_scale for K and V alike),
     and on the walk's sentinel slots (masked slots).
-  * The benchmark spec for this method fixes: -1 slots are invalid and masked,
-    V is the first 512 columns of the gathered rows, LSE is returned per
-    (r, h), an all-invalid row gives O = 0 and LSE = -inf.
+  * The method as stated for this library fixes what the pages leave open:
+    -1 slots are invalid and masked, V is the first 512 columns of the
+    gathered rows, LSE is returned per (r, h), an all-invalid row gives O = 0
+    and LSE = -inf.
 
 Readings where the pages are silent (each listed again in the design doc):
   * LSE is the natural log of the sum of exp of the sm_scale-scaled scores.
