@@ -73,7 +73,9 @@ typedef struct smla_options {
   int32_t head_block;      /* 0 = planner's choice, else 16, 32 or 64 heads per workgroup */
   int32_t splits;          /* 0 = planner's choice, else 1..64 splits of each row's slots */
   int32_t remap;           /* 0 = planner's choice, 1 = XCD-aware order, 2 = grid order */
-  int32_t reserved;
+  int32_t variant;         /* kernel instance; 0 = default. 16-head fp8 only: 1 = 4-wave
+                              64-slot staged-tile kernel, 2 = 8-wave 128-slot staged-tile
+                              kernel with two tiles of gathers in flight */
   void* workspace;         /* optional caller device buffer for split partials */
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
 } smla_options;
@@ -86,10 +88,12 @@ typedef struct smla_plan {
   int32_t remap;           /* 1 = XCD-aware work order, 0 = grid order */
   int32_t waves;           /* wavefronts per workgroup */
   int32_t lds_bytes;       /* LDS per workgroup */
-  int32_t tiles_per_split; /* 64-slot tiles walked by one workgroup */
-  int32_t reserved;
+  int32_t tiles_per_split; /* tiles walked by one workgroup */
+  int32_t tile_slots;      /* slots per tile (16, 64 or 128) */
   int64_t grid;            /* workgroups of the attention kernel */
   int64_t workspace_bytes; /* split partials (0 when splits == 1) */
+  int32_t variant;         /* kernel instance variant */
+  int32_t reserved;
 } smla_plan;
 
 /*
@@ -105,11 +109,12 @@ typedef struct smla_plan {
  *           invalid slot. Values >= N are a caller error: not checked on the
  *           device, the result is then undefined.
  *  sm_scale softmax scale applied to q.k.
- *  out      bf16 [R, H, 512]; last dim contiguous; fully written.
+ *  out      bf16 [R, H, 512]; last dim contiguous; base, row and head strides
+ *           16-byte aligned; fully written.
  *  lse      fp32 [R, H]; fully written (natural log; -inf for empty rows).
  *
  * D_qk must be 576 or 512; H in [1, 1024]; K in [1, 2^20]; R >= 0 (R == 0 is
- * a no-op returning SMLA_OK); q rows, out rows and pool rows 16-byte aligned.
+ * a no-op returning SMLA_OK); q, out and pool rows 16-byte aligned.
  * out and lse must not alias any input. The same inputs and the same plan give
  * bitwise-identical outputs.
  */

@@ -31,7 +31,7 @@ Sources on the pages:
     gathered rows, LSE is returned per (r, h), an all-invalid row gives O = 0
     and LSE = -inf.
 
-Readings where the pages are silent (each listed again in the design doc):
+Readings where the pages are silent:
   * LSE is the natural log of the sum of exp of the sm_scale-scaled scores.
   * Any negative index is invalid; an index >= pool rows is a caller error and
     the oracle raises.

@@ -33,7 +33,7 @@ class SmlaTensor(ctypes.Structure):
 
 class SmlaOptions(ctypes.Structure):
     _fields_ = [("head_block", ctypes.c_int32), ("splits", ctypes.c_int32),
-                ("remap", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("remap", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
 
 
@@ -41,8 +41,9 @@ class SmlaPlan(ctypes.Structure):
     _fields_ = [("head_block", ctypes.c_int32), ("head_blocks", ctypes.c_int32),
                 ("splits", ctypes.c_int32), ("remap", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("tiles_per_split", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("grid", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_int64)]
+                ("tile_slots", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64), ("variant", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class SparseMLAError(RuntimeError):
@@ -133,9 +134,9 @@ def _check(status: int):
         raise SparseMLAError(status, last_error())
 
 
-def _options(head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None):
+def _options(head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None, variant=0):
     o = SmlaOptions()
-    o.head_block, o.splits, o.remap = head_block, splits, remap
+    o.head_block, o.splits, o.remap, o.variant = head_block, splits, remap, variant
     if workspace is not None:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size() \
@@ -153,12 +154,14 @@ def sparse_mla_fwd(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=Non
 
 
 def sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None,
-                      head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None) -> None:
+                      head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None,
+                      variant=0) -> None:
     """sparse_mla_fwd with planner overrides (head_block 16/32/64, splits,
-    remap 1 = XCD-aware / 2 = grid order) and an optional caller workspace."""
+    remap 1 = XCD-aware / 2 = grid order, kernel variant) and an optional
+    caller workspace."""
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, out, lse)]
-    opt = _options(head_block, splits, remap, workspace, workspace_bytes)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant)
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd_ex(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), _ptr(ds[3]),
                                  float(sm_scale), _ptr(ds[4]), _ptr(ds[5]), st, ctypes.byref(opt)))
@@ -178,10 +181,11 @@ def sparse_mla_is_supported(q, kv_pool, indices) -> bool:
     return bool(lib.sparse_mla_is_supported(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2])))
 
 
-def sparse_mla_plan(q, kv_pool, indices, head_block=0, splits=0, remap=0, num_cus=0) -> dict:
+def sparse_mla_plan(q, kv_pool, indices, head_block=0, splits=0, remap=0, num_cus=0,
+                    variant=0) -> dict:
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, indices)]
-    opt = _options(head_block, splits, remap)
+    opt = _options(head_block, splits, remap, variant=variant)
     plan = SmlaPlan()
     _check(lib.sparse_mla_plan(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), ctypes.byref(opt),
                                int(num_cus), ctypes.byref(plan)))

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <mutex>
@@ -143,6 +144,7 @@ int validate_inputs(const smla_tensor* q, const smla_tensor* kv, const smla_tens
   c->pb.topk = int32_t(K);
   c->pb.kv_fp8 = kv->dtype == SMLA_FP8_E4M3FN;
   c->fp8 = c->pb.kv_fp8 != 0;
+  c->pb.pool_bytes = kv->shape[0] > 0 ? (kv->shape[0] - 1) * kv->stride[0] * eb + D * eb : 0;
   return SMLA_OK;
 }
 
@@ -170,9 +172,8 @@ int validate_all(const smla_tensor* q, const smla_tensor* kv, const smla_tensor*
   if (R > 0) {
     if (!out->data) return fail(SMLA_ERR_INVALID_ARG, "out: null data");
     if (!lse->data) return fail(SMLA_ERR_INVALID_ARG, "lse: null data");
-    if ((reinterpret_cast<uintptr_t>(out->data) & 7u) != 0 || (out->stride[0] * 2) % 8 != 0 ||
-        (out->stride[1] * 2) % 8 != 0)
-      return fail(SMLA_ERR_UNSUPPORTED, "out: base, row and head strides must be 8-byte aligned");
+    if (!aligned16(out->data) || (out->stride[0] * 2) % 16 != 0 || (out->stride[1] * 2) % 16 != 0)
+      return fail(SMLA_ERR_UNSUPPORTED, "out: base, row and head strides must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(lse->data) & 3u) != 0)
       return fail(SMLA_ERR_INVALID_ARG, "lse: base must be 4-byte aligned");
     const smla_tensor* ins[4] = {q, kv, idx, c->fp8 ? scale : nullptr};
@@ -264,6 +265,7 @@ int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
   p.q_hs = q->stride[1];
   p.pool = static_cast<const uint8_t*>(kv_pool->data);
   p.pool_rs_bytes = kv_pool->stride[0] * elem_size(kv_pool->dtype);
+  p.pool_bytes = uint32_t(std::min<int64_t>(c.pb.pool_bytes, kMaxBufferBytes));
   p.kv_scale = c.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr;
   p.idx = static_cast<const int32_t*>(indices->data);
   p.idx_rs = indices->stride[0];

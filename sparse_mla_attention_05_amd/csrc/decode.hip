@@ -1,0 +1,340 @@
+// gfx950 decode kernel of the sparse MLA forward: up to 16 heads per
+// workgroup, fp8 e4m3fn pool, 576- or 512-wide rows.
+//
+// The method (per row r, head h, over the row's valid slots j):
+//   s_j = sm_scale * q[r,h] . K[idx_j] (D_qk columns), out = softmax(s) V
+//   (V = first 512 columns), lse = ln sum_j exp(s_j)
+// after "[Triton/Gluon] GFX950 sparse mla optimizations" (aiter PR 6159),
+// Technical Details and the commit notes on the per-tensor fp8 route and the
+// split-K reduce. With 16 heads the work per gathered byte is small, so the
+// kernel is built to keep gathers in flight and spend few cycles per slot:
+//
+//  * One workgroup = (row, 16-head block, split), 4 wavefronts, one per SIMD.
+//    Each wave walks its own quarter of the split's slots in 16-slot steps
+//    (steps w, w+4, ...) with its own running max, row sum and O, like an
+//    independent split; the four are merged once at the end. No barrier
+//    inside the walk.
+//  * Gathers go straight into VGPRs, three steps in flight per wave. Lane
+//    (l16, g) loads 16-byte chunks 4i+g (i = 0..8) of the step's slot l16, so
+//    every load instruction reads 64 contiguous bytes of 16 rows. Those
+//    chunks are exactly the A operand of S^T = K Q^T on
+//    v_mfma_f32_16x16x32_bf16 once widened to bf16 in registers, provided
+//    Q^T uses the same column order (k-step 2i+h takes columns
+//    64i + 16g + 8h .. +8), which it does: K never goes through LDS.
+//  * S^T leaves each lane with slots 4g..4g+3 of head l16, which is the A
+//    operand of P on v_mfma_f32_16x16x16_bf16 (k-slots 4g..4g+3): P stays in
+//    registers.
+//  * V (the first 512 columns, still fp8) is written to a wave-private LDS
+//    area and read back with the transposed byte read: pointing rows 0..3 of
+//    the 8 x 16 byte block at slots 4g..4g+3 of one 16-column block and rows
+//    4..7 at the same slots of the next one hands each lane the B operands of
+//    two column blocks in one read. The 32-byte row pitch offset puts the
+//    rows one half-wave reads on distinct banks.
+//  * Online softmax in the exp2 domain with a lazy reference: the reference
+//    max moves only when a tile max exceeds it by more than 8 (so P <= 2^8),
+//    which skips most O rescales and is exact in real arithmetic (the final
+//    normalisation uses the same reference).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "launch.h"
+#include "work_order.h"
+
+namespace smla {
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecStep = 16;        // slots per wave step
+constexpr int kDecBufs = 2;         // steps of gathers in flight per wave
+constexpr int kVPitch = 544;        // V staging row pitch (bytes): 512 + 32
+constexpr int kVWave = 16 * kVPitch;  // V staging bytes per wave
+constexpr int kIdxChunk = 4096;     // slot indices staged in LDS at a time
+constexpr int kIdxOffset = kDecWaves * kVWave;  // their LDS offset (bytes)
+constexpr int kOPitch = 528;        // partial-O row pitch (floats): 2112 B = 64 mod 256
+constexpr int kOWave = 16 * kOPitch * 4;        // partial-O bytes per wave
+constexpr int kDecSmem = (kDecWaves * kOWave > kIdxOffset + 4 * kIdxChunk)
+                             ? kDecWaves * kOWave
+                             : kIdxOffset + 4 * kIdxChunk;
+constexpr float kLazyMax = 8.0f;    // log2-domain slack before the reference max moves
+constexpr uint32_t kOutOfRange = 0xFFFFF000u;  // buffer offset of an invalid slot's row
+constexpr int kBufferWord3 = 0x00020000;       // raw buffer descriptor word 3 (gfx9 family)
+
+template <int DQK>
+__global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdParams p) {
+  constexpr int NCH = DQK / 16;  // 16-byte fp8 chunks per row
+  constexpr int NI = NCH / 4;    // chunks per lane per step
+  constexpr int KS = DQK / 32;   // k-steps of the QK dot
+  constexpr int VI = kDv / 64;   // chunk rounds holding V columns (8)
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  static_assert(NCH % 4 == 0 && 2 * NI == KS, "row width");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kDecSmem];
+  __shared__ float red_m[kDecWaves * 16];
+  __shared__ float red_l[kDecWaves * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  int64_t work = p.remap ? smla_xcd_work(blockIdx.x, p.grid) : int64_t(blockIdx.x);
+  const int hb = int(work % p.head_blocks);
+  work /= p.head_blocks;
+  const int split = int(work % p.splits);
+  const int64_t r = work / p.splits;
+  const int h0 = hb * 16;
+
+  // Q^T fragments in the gather's column order.
+  bf16x8 qf[KS];
+  {
+    const int h = h0 + l16;
+    if (h < p.heads) {
+      const uint16_t* qp = p.q + r * p.q_rs + int64_t(h) * p.q_hs + 16 * g;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        qf[s] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(qp + 64 * (s >> 1) + 8 * (s & 1)));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+  }
+  const float kv_scale = *p.kv_scale;
+  const float c = p.sm_log2 * kv_scale;  // raw dot -> log2-domain score
+
+  // This split's slots, walked in chunks whose indices are staged in LDS.
+  const int kbeg = split * p.tiles_per_split * kDecStep;
+  const int kend = min(p.topk, kbeg + p.tiles_per_split * kDecStep);
+  const int32_t* idx_row = p.idx + r * p.idx_rs;
+  int32_t* idx_s = reinterpret_cast<int32_t*>(smem + kIdxOffset);
+
+  // Every global load in the walk is unconditional and its result is only
+  // read where it is consumed: loads in divergent branches, or loaded values
+  // copied between iterations, make the compiler wait for all outstanding
+  // loads. An invalid slot's row is read at an offset past the end of the
+  // pool's buffer range, which returns zeros without touching memory.
+  const __amdgpu_buffer_rsrc_t pool_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.pool), 0, p.pool_bytes, kBufferWord3);
+  auto gather = [&](u32x4 (&kr)[NI], int id) {
+    const uint32_t off = id >= 0 ? uint32_t(id) * uint32_t(p.pool_rs_bytes) + 16u * g : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pool_rsrc, off + 64u * i, 0, 0));
+  };
+
+  uint8_t* vst = smem + wave * kVWave;
+  // Transposed-read address of this lane: byte row t = l16/2 of the read is
+  // slot 4g + (t & 3) in column block nb + (t >> 2); column half l16 & 1.
+  const int t8 = l16 >> 1;
+  const uint8_t* vrd = vst + (4 * g + (t8 & 3)) * kVPitch + 16 * (t8 >> 2) + 8 * (l16 & 1);
+
+  floatx4 o[32];
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb) o[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf;  // log2-domain reference max of head l16
+  float l_part = 0.f;     // this lane's share of the row sum of head l16
+
+  auto step = [&](const u32x4 (&kr)[NI], int id) {
+    // V columns into the wave's staging area (fp8 as is).
+#pragma unroll
+    for (int i = 0; i < VI; ++i)
+      *reinterpret_cast<u32x4*>(vst + l16 * kVPitch + 16 * (4 * i + g)) = kr[i];
+
+    // S^T = K Q^T, two accumulators.
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_fp8x8(kr[i].x, kr[i].y), qf[2 * i], s0,
+                                                    0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_fp8x8(kr[i].z, kr[i].w), qf[2 * i + 1],
+                                                    s1, 0, 0, 0);
+      // Keep each k-step's widening next to its MFMAs: hoisting all of them
+      // would hold 18 widened operands (72 VGPRs) at once.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Scores of head l16 for slots 4g + i; invalid slots -> -inf.
+    const uint32_t bits = uint32_t(__ballot(id >= 0) >> (4 * g));
+    float sv[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = ((bits >> i) & 1u) ? (s0[i] + s1[i]) * c : kNegInf;
+      mx = fmaxf(mx, sv[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    const bool upd = mx > m_ref + kLazyMax;
+    if (__ballot(upd) != 0) {
+      const float m_new = upd ? mx : m_ref;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+      l_part *= alpha;
+      floatx4 a4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) o[nb] *= a4;
+      m_ref = m_new;
+    }
+    const float mu = m_ref == kNegInf ? 0.f : m_ref;
+    float e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+      l_part += e[i];
+    }
+    const s16x4 pa = __builtin_bit_cast(s16x4, u32x2{pack2_bf16(e[0], e[1]), pack2_bf16(e[2], e[3])});
+
+    // O += P V, two column blocks per transposed read.
+#pragma unroll
+    for (int nb = 0; nb < 32; nb += 2) {
+      const u32x2 v = lds_read_tr8(vrd + 16 * nb);
+      const u32x2 w0 = widen_fp8x4(v.x), w1 = widen_fp8x4(v.y);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, w0), o[nb], 0, 0, 0);
+      o[nb + 1] =
+          __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, w1), o[nb + 1], 0, 0, 0);
+      if ((nb & 6) == 6) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int c0 = kbeg; c0 < kend; c0 += kIdxChunk) {
+    const int c1 = min(kend, c0 + kIdxChunk);
+    __syncthreads();  // every wave is done with the previous chunk's indices
+    for (int t = tid; t < c1 - c0; t += kDecWaves * 64) idx_s[t] = idx_row[c0 + t];
+    __syncthreads();
+    const int nst = (c1 - c0 + kDecStep - 1) / kDecStep;
+    const int nj = nst > wave ? (nst - wave + kDecWaves - 1) / kDecWaves : 0;
+    // Index of this lane's slot in the wave's step j, -1 when out of range.
+    auto slot_idx = [&](int j) -> int {
+      const int t = kDecStep * (wave + kDecWaves * j) + l16;
+      return (j < nj && t < c1 - c0) ? idx_s[t] : -1;
+    };
+    if (nj > 0) {
+      // kDecBufs steps of gathers in flight; the walk is unrolled by kDecBufs
+      // so each buffer keeps its registers, and runs a multiple of kDecBufs
+      // steps with no condition inside (steps past nj have no valid slot:
+      // their loads return zeros and their scores are -inf).
+      u32x4 kr[kDecBufs][NI];
+      int idb[kDecBufs];
+#pragma unroll
+      for (int u = 0; u < kDecBufs; ++u) {
+        idb[u] = slot_idx(u);
+        gather(kr[u], idb[u]);
+      }
+      const int nj_pad = (nj + kDecBufs - 1) / kDecBufs * kDecBufs;
+      for (int j = 0; j < nj_pad; j += kDecBufs) {
+#pragma unroll
+        for (int u = 0; u < kDecBufs; ++u) {
+          step(kr[u], idb[u]);
+          idb[u] = slot_idx(j + u + kDecBufs);
+          gather(kr[u], idb[u]);
+        }
+      }
+    }
+  }
+
+  // ---- merge the four waves: M = max_w m_w, L = sum_w 2^(m_w - M) l_w,
+  // out = sum_w 2^(m_w - M) O_w * kv_scale / L, summed in wave order.
+  float l_head = l_part;
+  l_head += __shfl_xor(l_head, 16);
+  l_head += __shfl_xor(l_head, 32);
+  if (g == 0) {
+    red_m[wave * 16 + l16] = m_ref;
+    red_l[wave * 16 + l16] = l_head;
+  }
+  __syncthreads();  // also: every wave is done with its V staging area
+
+  float* part = reinterpret_cast<float*>(smem) + wave * (kOWave / 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int head = 4 * g + i;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_m[w * 16 + head]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = red_m[w * 16 + head];
+      L += mw == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mw - M) * red_l[w * 16 + head];
+    }
+    const float mine = red_m[wave * 16 + head];
+    const float f = (L > 0.f && mine != kNegInf) ? __builtin_amdgcn_exp2f(mine - M) * kv_scale / L : 0.f;
+    float* prow = part + head * kOPitch + l16;
+#pragma unroll
+    for (int nb = 0; nb < 32; ++nb) prow[16 * nb] = o[nb][i] * f;
+  }
+  __syncthreads();
+
+  // 16 heads x 64 chunks of 8 columns; thread t takes chunk t % 64 of heads
+  // t / 64 + 4k, so consecutive threads store consecutive 16-byte pieces.
+  const bool split_mode = p.splits > 1;
+  const float* parts = reinterpret_cast<const float*>(smem);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int head = (tid >> 6) + 4 * k;
+    const int col = 8 * (tid & 63);
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float* src = parts + w * (kOWave / 4) + head * kOPitch + col;
+      s0 += *reinterpret_cast<const floatx4*>(src);
+      s1 += *reinterpret_cast<const floatx4*>(src + 4);
+    }
+    const int h = h0 + head;
+    if (h < p.heads) {
+      if (!split_mode) {
+        *reinterpret_cast<u32x4*>(p.out + r * p.out_rs + int64_t(h) * p.out_hs + col) =
+            u32x4{pack2_bf16(s0.x, s0.y), pack2_bf16(s0.z, s0.w), pack2_bf16(s1.x, s1.y),
+                  pack2_bf16(s1.z, s1.w)};
+      } else {
+        float* dst = p.part_o + ((int64_t(split) * p.rows + r) * p.heads + h) * kDv + col;
+        *reinterpret_cast<floatx4*>(dst) = s0;
+        *reinterpret_cast<floatx4*>(dst + 4) = s1;
+      }
+    }
+  }
+  if (tid < 16) {
+    const int h = h0 + tid;
+    if (h < p.heads) {
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_m[w * 16 + tid]);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float mw = red_m[w * 16 + tid];
+        L += mw == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mw - M) * red_l[w * 16 + tid];
+      }
+      const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+      if (!split_mode)
+        p.lse[r * p.lse_rs + int64_t(h) * p.lse_hs] = lse;
+      else
+        p.part_lse[(int64_t(split) * p.rows + r) * p.heads + h] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+KernelShape decode_shape(int dqk) {
+  KernelShape k;
+  if (dqk != 576 && dqk != 512) return k;
+  k.waves = kDecWaves;
+  k.tile = kDecStep;
+  k.lds_bytes = kDecSmem + 2 * kDecWaves * 16 * 4;
+  return k;
+}
+
+int launch_decode(const FwdParams& p, int dqk, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dqk == 576)
+    hipLaunchKernelGGL(decode_kernel<576>, dim3(uint32_t(p.grid)), dim3(kDecWaves * 64), 0, st, p);
+  else if (dqk == 512)
+    hipLaunchKernelGGL(decode_kernel<512>, dim3(uint32_t(p.grid)), dim3(kDecWaves * 64), 0, st, p);
+  else
+    return int(hipErrorInvalidValue);
+  return int(hipGetLastError());
+}
+
+}  // namespace smla

@@ -41,43 +41,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "launch.h"
 #include "work_order.h"
 
 namespace smla {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
-}
-
-// Four e4m3fn codes (one dword, code 0 in the low byte) to four bf16 values
-// (two dwords, value 0 in the low half). Exact: every finite e4m3fn value is
-// a bf16 value, and the scale operand is 1.
-__device__ __forceinline__ u32x2 widen_fp8x4(uint32_t w) {
-  return u32x2{
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
-}
-
-template <int NHG, int NW, int DQK, bool FP8>
+template <int NHG, int NW, int TK_, int DQK, bool FP8>
 struct Cfg {
   static constexpr int HB = 16 * NHG;          // heads per workgroup
   static constexpr int NT = NW * 64;           // threads per workgroup
-  static constexpr int TK = kTileKeys;         // slots per tile
+  static constexpr int TK = TK_;               // slots per tile
   static constexpr int KSTEPS = DQK / 32;      // k-steps of the QK dot
   static constexpr int PITCH = DQK + 8;        // LDS tile row pitch (elements)
   static constexpr int PP = TK + 8;            // LDS P row pitch (elements)
@@ -91,16 +66,20 @@ struct Cfg {
   static constexpr int LPT = (CH + TPK - 1) / TPK;  // chunks per gather thread
   static constexpr int LDS_BYTES =
       TK * PITCH * 2 + HB * PP * 2 + NKG * HB * 4 + 2 * HB * 4 + TK;
-  static_assert(NKG * NHG == NW && NKG >= 1 && NKG <= 4, "wave split");
-  static_assert(DW % 16 == 0 && DQK % 32 == 0, "shape");
+  static_assert(NKG * NHG == NW && BPW >= 1 && BPW * NKG * 16 == TK, "wave split");
+  static_assert(NT % TK == 0 && DW % 16 == 0 && DQK % 32 == 0 && TK % 32 == 0, "shape");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-template <int NHG, int NW, int DQK, bool FP8>
+// One workgroup: (row, block of HB = 16*NHG heads, split). NW waves, TK-slot
+// tiles. DBUF keeps two tiles of gathers in flight (two register buffers,
+// the tile loop unrolled by two); otherwise one.
+template <int NHG, int NW, int TK_, bool DBUF, int DQK, bool FP8>
 __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
-  using C = Cfg<NHG, NW, DQK, FP8>;
+  using C = Cfg<NHG, NW, TK_, DQK, FP8>;
   constexpr int HB = C::HB, TK = C::TK, PITCH = C::PITCH, PP = C::PP;
   constexpr int NKG = C::NKG, BPW = C::BPW, NB = C::NB, TPK = C::TPK, LPT = C::LPT;
-  constexpr int CH = C::CH;
+  constexpr int CH = C::CH, KSTEPS = C::KSTEPS;
 
   __shared__ __attribute__((aligned(16))) uint16_t kt[TK * PITCH];  // bf16 tile
   __shared__ __attribute__((aligned(16))) uint16_t pt[HB * PP];     // bf16 P
@@ -127,17 +106,17 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   // QK role: head group hg, slot group kg.
   const int hg = wave / NKG, kg = wave % NKG;
 
-  bf16x8 qf[C::KSTEPS];
+  bf16x8 qf[KSTEPS];
   {
     const int h = h0 + hg * 16 + l16;
     if (h < p.heads) {
       const uint16_t* qp = p.q + r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s)
+      for (int s = 0; s < KSTEPS; ++s)
         qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
     } else {
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
 
@@ -157,8 +136,7 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
     return (t < t_end && j < p.topk) ? idx_row[j] : -1;
   };
 
-  u32x4 pre[LPT];
-  auto gather = [&](int id) {
+  auto gather = [&](u32x4 (&pre)[LPT], int id) {
     if (id >= 0) {
       const uint8_t* rp = p.pool + int64_t(id) * p.pool_rs_bytes;
 #pragma unroll
@@ -171,7 +149,7 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
       for (int i = 0; i < LPT; ++i) pre[i] = u32x4{0, 0, 0, 0};
     }
   };
-  auto stage = [&](int id) {
+  auto stage = [&](const u32x4 (&pre)[LPT], int id) {
     uint16_t* rowp = kt + gk * PITCH;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
@@ -199,29 +177,21 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
     for (int b = 0; b < NB; ++b) o[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  int id_cur = load_idx(t_begin);
-  int id_next = load_idx(t_begin + 1);
-  gather(id_cur);
-
-  for (int t = t_begin; t < t_end; ++t) {
-    __syncthreads();  // every wave is done with the previous tile, P and alpha
-    stage(id_cur);
-    id_cur = id_next;
-    if (t + 1 < t_end) gather(id_cur);
-    id_next = load_idx(t + 2);
-    __syncthreads();  // tile visible
-
-    // ---- S^T = K Q^T for this wave's 16-slot blocks and 16-head group
-    floatx4 sacc[BPW];
+  // Everything after the tile is staged and visible: QK, softmax, PV.
+  auto compute = [&]() {
+    // ---- S^T = K Q^T for this wave's 16-slot blocks and 16-head group; two
+    // accumulators per block halve the dependent MFMA chain.
+    floatx4 sacc[BPW][2];
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < BPW; ++j)
+      sacc[j][0] = sacc[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
+    for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
         const int key = (kg * BPW + j) * 16 + l16;
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + key * PITCH + 32 * s + 8 * g);
-        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[j], 0, 0, 0);
+        sacc[j][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[j][s & 1], 0, 0, 0);
       }
     }
 
@@ -231,9 +201,10 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
       const uint32_t vf = *reinterpret_cast<const uint32_t*>(kvalid + (kg * BPW + j) * 16 + 4 * g);
+      const floatx4 sj = sacc[j][0] + sacc[j][1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v = ((vf >> (8 * i)) & 0xffu) ? sacc[j][i] * score_scale : kNegInf;
+        const float v = ((vf >> (8 * i)) & 0xffu) ? sj[i] * score_scale : kNegInf;
         sv[j][i] = v;
         mx = fmaxf(mx, v);
       }
@@ -257,7 +228,11 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
         e[i] = __builtin_amdgcn_exp2f(sv[j][i] - m_ref);
         psum += e[i];
       }
-      *reinterpret_cast<u32x2*>(pt + (hg * 16 + l16) * PP + (kg * BPW + j) * 16 + 4 * g) =
+      // P is stored in the PV MFMA's k-slot order: within each 32-slot step,
+      // k-slots 8g..8g+3 hold slots 4g..4g+3 and k-slots 8g+4..8g+7 hold slots
+      // 16+4g..16+4g+3, which is the order S^T leaves in the lanes.
+      const int kb = kg * BPW + j;
+      *reinterpret_cast<u32x2*>(pt + (hg * 16 + l16) * PP + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1)) =
           u32x2{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3])};
     }
     psum += __shfl_xor(psum, 16);
@@ -280,19 +255,58 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int a = 0; a < NHG; ++a)
         pa[a] = *reinterpret_cast<const bf16x8*>(pt + (a * 16 + l16) * PP + 32 * ks + 8 * g);
+      // V operand: k-slots 8g..8g+3 = slots 32ks+4g+(0..3), k-slots 8g+4..8g+7
+      // = slots 32ks+16+4g+(0..3), two transposed reads of 4 rows each. The 16
+      // rows one read touches are consecutive, so with the tile pitch an odd
+      // multiple of 16 bytes modulo 256 they fall on distinct banks.
+      const uint16_t* vrow = kt + (32 * ks + 4 * g + (l16 >> 2)) * PITCH + wave * C::DW + 4 * (l16 & 3);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const uint16_t* vp = kt + (32 * ks + 8 * g) * PITCH + wave * C::DW + b * 16 + l16;
-        u32x4 vv;
-        vv.x = uint32_t(vp[0]) | (uint32_t(vp[PITCH]) << 16);
-        vv.y = uint32_t(vp[2 * PITCH]) | (uint32_t(vp[3 * PITCH]) << 16);
-        vv.z = uint32_t(vp[4 * PITCH]) | (uint32_t(vp[5 * PITCH]) << 16);
-        vv.w = uint32_t(vp[6 * PITCH]) | (uint32_t(vp[7 * PITCH]) << 16);
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
+        const u32x2 v0 = lds_read_tr16(vrow + b * 16);
+        const u32x2 v1 = lds_read_tr16(vrow + 16 * PITCH + b * 16);
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
 #pragma unroll
         for (int a = 0; a < NHG; ++a)
           o[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[a], vb, o[a][b], 0, 0, 0);
       }
+    }
+  };
+
+  u32x4 pre0[LPT];
+  int id0 = load_idx(t_begin);
+  gather(pre0, id0);
+  if constexpr (!DBUF) {
+    int id_next = load_idx(t_begin + 1);
+    for (int t = t_begin; t < t_end; ++t) {
+      __syncthreads();  // every wave is done with the previous tile, P and alpha
+      stage(pre0, id0);
+      id0 = id_next;
+      if (t + 1 < t_end) gather(pre0, id0);
+      id_next = load_idx(t + 2);
+      __syncthreads();  // tile visible
+      compute();
+    }
+  } else {
+    u32x4 pre1[LPT];
+    int id1 = load_idx(t_begin + 1);
+    if (t_begin + 1 < t_end) gather(pre1, id1);
+    int id_next = load_idx(t_begin + 2);
+    for (int t = t_begin; t < t_end; t += 2) {
+      __syncthreads();
+      stage(pre0, id0);
+      id0 = id_next;
+      if (t + 2 < t_end) gather(pre0, id0);
+      id_next = load_idx(t + 3);
+      __syncthreads();
+      compute();
+      if (t + 1 >= t_end) break;
+      __syncthreads();
+      stage(pre1, id1);
+      id1 = id_next;
+      if (t + 3 < t_end) gather(pre1, id1);
+      id_next = load_idx(t + 4);
+      __syncthreads();
+      compute();
     }
   }
 
@@ -375,54 +389,79 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
   if (tid == 0) p.lse[r * p.lse_rs + int64_t(h) * p.lse_hs] = m + __logf(tot);
 }
 
-template <int NHG, int NW, int DQK, bool FP8>
-hipError_t launch_fwd(const FwdParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<NHG, NW, DQK, FP8>), dim3(uint32_t(p.grid)), dim3(NW * 64), 0,
-                     st, p);
+// Kernel instances per (head block, pool dtype, variant): waves, tile size,
+// whether two tiles of gathers are kept in flight. For 16 heads over an fp8
+// pool, variant 0 is the decode kernel (decode.hip); variant 1 is the
+// 4-wave, 64-slot instance below and variant 2 runs 8 waves over 128-slot
+// tiles, one workgroup per CU (its bf16 tile takes 146 KB of LDS), with two
+// tiles of gathers in flight. Elsewhere every variant is variant 0.
+template <int NHG, int NW, int TK, bool DBUF>
+struct Inst {
+  static constexpr int kNHG = NHG, kNW = NW, kTK = TK;
+  static constexpr bool kDBUF = DBUF;
+};
+template <int HB, bool FP8, int V> struct InstFor;
+template <int V> struct InstFor<16, true, V> : Inst<1, 4, 64, false> {};
+template <> struct InstFor<16, true, 2> : Inst<1, 8, 128, true> {};
+template <int V> struct InstFor<16, false, V> : Inst<1, 4, 64, false> {};
+template <bool FP8, int V> struct InstFor<32, FP8, V> : Inst<2, 8, 64, false> {};
+template <bool FP8, int V> struct InstFor<64, FP8, V> : Inst<4, 8, 64, false> {};
+
+template <int HB, int V, int DQK, bool FP8>
+hipError_t launch_inst(const FwdParams& p, hipStream_t st) {
+  using I = InstFor<HB, FP8, V>;
+  hipLaunchKernelGGL((fwd_kernel<I::kNHG, I::kNW, I::kTK, I::kDBUF, DQK, FP8>),
+                     dim3(uint32_t(p.grid)), dim3(I::kNW * 64), 0, st, p);
   return hipGetLastError();
 }
 
+template <int HB, bool FP8, int V>
+KernelShape shape_of(int dqk) {
+  using I = InstFor<HB, FP8, V>;
+  KernelShape k;
+  k.waves = I::kNW;
+  k.tile = I::kTK;
+  k.lds_bytes = dqk == 576 ? Cfg<I::kNHG, I::kNW, I::kTK, 576, FP8>::LDS_BYTES
+                           : Cfg<I::kNHG, I::kNW, I::kTK, 512, FP8>::LDS_BYTES;
+  return k;
+}
+
 template <int DQK, bool FP8>
-hipError_t launch_by_head_block(int head_block, const FwdParams& p, hipStream_t st) {
+hipError_t launch_by_head_block(int head_block, int variant, const FwdParams& p, hipStream_t st) {
   switch (head_block) {
-    case 16: return launch_fwd<1, 4, DQK, FP8>(p, st);
-    case 32: return launch_fwd<2, 8, DQK, FP8>(p, st);
-    case 64: return launch_fwd<4, 8, DQK, FP8>(p, st);
+    case 16:
+      if (FP8 && variant == 0) return static_cast<hipError_t>(launch_decode(p, DQK, st));
+      return variant == 2 ? launch_inst<16, 2, DQK, FP8>(p, st) : launch_inst<16, 0, DQK, FP8>(p, st);
+    case 32: return launch_inst<32, 0, DQK, FP8>(p, st);
+    case 64: return launch_inst<64, 0, DQK, FP8>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int kernel_waves(int head_block) { return head_block == 16 ? 4 : 8; }
-
-int kernel_lds_bytes(int head_block, int dqk) {
-  // Cfg<...>::LDS_BYTES does not depend on the pool dtype.
-  if (dqk == 576) {
-    switch (head_block) {
-      case 16: return Cfg<1, 4, 576, false>::LDS_BYTES;
-      case 32: return Cfg<2, 8, 576, false>::LDS_BYTES;
-      case 64: return Cfg<4, 8, 576, false>::LDS_BYTES;
-    }
-  } else if (dqk == 512) {
-    switch (head_block) {
-      case 16: return Cfg<1, 4, 512, false>::LDS_BYTES;
-      case 32: return Cfg<2, 8, 512, false>::LDS_BYTES;
-      case 64: return Cfg<4, 8, 512, false>::LDS_BYTES;
-    }
+KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant) {
+  if (dqk != 576 && dqk != 512) return KernelShape{};
+  switch (head_block) {
+    case 16:
+      if (fp8 && variant == 0) return decode_shape(dqk);
+      if (variant == 2) return fp8 ? shape_of<16, true, 2>(dqk) : shape_of<16, false, 2>(dqk);
+      return fp8 ? shape_of<16, true, 0>(dqk) : shape_of<16, false, 0>(dqk);
+    case 32: return fp8 ? shape_of<32, true, 0>(dqk) : shape_of<32, false, 0>(dqk);
+    case 64: return fp8 ? shape_of<64, true, 0>(dqk) : shape_of<64, false, 0>(dqk);
+    default: return KernelShape{};
   }
-  return -1;
 }
 
 int launch_forward(const FwdParams& p, const smla_plan& plan, int dqk, bool fp8, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dqk == 576)
-    e = fp8 ? launch_by_head_block<576, true>(plan.head_block, p, st)
-            : launch_by_head_block<576, false>(plan.head_block, p, st);
+    e = fp8 ? launch_by_head_block<576, true>(plan.head_block, plan.variant, p, st)
+            : launch_by_head_block<576, false>(plan.head_block, plan.variant, p, st);
   else
-    e = fp8 ? launch_by_head_block<512, true>(plan.head_block, p, st)
-            : launch_by_head_block<512, false>(plan.head_block, p, st);
+    e = fp8 ? launch_by_head_block<512, true>(plan.head_block, plan.variant, p, st)
+            : launch_by_head_block<512, false>(plan.head_block, plan.variant, p, st);
   if (e != hipSuccess) return int(e);
   if (plan.splits > 1) {
     hipLaunchKernelGGL(combine_kernel, dim3(uint32_t(p.rows * p.heads)), dim3(128), 0, st, p);

@@ -7,7 +7,6 @@
 
 namespace smla {
 
-constexpr int kTileKeys = 64;   // KV slots per tile walked by a workgroup
 constexpr int kDv = 512;        // value width: the first 512 columns of a row
 constexpr int kMaxSplits = 64;
 constexpr int kMaxHeads = 1024;
@@ -20,6 +19,8 @@ struct FwdParams {
   int64_t q_rs, q_hs;
   const uint8_t* pool;      // bf16 or e4m3fn rows
   int64_t pool_rs_bytes;
+  uint32_t pool_bytes;      // bytes from pool to the end of its last row read, capped
+                            // at kMaxBufferBytes (buffer-load range)
   const float* kv_scale;    // fp32 [1] (fp8 pools) or nullptr
   const int32_t* idx;       // int32 [R, K]
   int64_t idx_rs;
@@ -46,11 +47,26 @@ struct Problem {
   int32_t dqk;
   int32_t topk;
   int32_t kv_fp8;
+  int64_t pool_bytes;       // bytes from pool to the end of its last row read
 };
 
-// Per-workgroup LDS and wave count of the kernel instance for (head_block, dqk).
-int kernel_waves(int head_block);
-int kernel_lds_bytes(int head_block, int dqk);
+// Largest pool (bytes) the decode kernel addresses through a buffer
+// descriptor with 32-bit offsets; larger pools use the staged-tile kernel.
+constexpr int64_t kMaxBufferBytes = 0xFFFFF000ll - 4096;
+
+// Shape of the attention-kernel instance used for (head_block, dqk, pool
+// dtype, variant): wavefronts per workgroup, slots per tile, LDS per
+// workgroup.
+struct KernelShape {
+  int waves = 0;
+  int tile = 0;
+  int lds_bytes = 0;
+};
+KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant);
+
+// The 16-head fp8 decode kernel (decode.hip): its shape and its launch.
+KernelShape decode_shape(int dqk);
+int launch_decode(const FwdParams& p, int dqk, void* stream);
 
 // Pure host planner: no HIP calls. Returns SMLA_OK or an error status and
 // fills `err` with the reason.

@@ -8,10 +8,10 @@
 // this kernel:
 //  * head block: 16 heads for H <= 16, 32 for H <= 32, else 64, so one
 //    workgroup gathers and stages each KV tile once for as many heads as fit.
-//  * splits: when rows x head blocks leaves the CUs' workgroup slots
-//    underfilled, each row's slots are split (each split keeping >= 2 tiles)
-//    until about two rounds of workgroups fill the slots; the combine kernel
-//    then merges the partials.
+//  * splits: when rows x head blocks leave the CUs' workgroup slots
+//    underfilled, each row's slots are split if a makespan model (rounds of
+//    workgroups x (tiles per split + a fixed per-workgroup cost) + the
+//    combine pass) says it pays; the combine kernel merges the partials.
 //  * remap: XCD-aware order when a row has >= 2 head blocks or >= 2 splits,
 //    so the workgroups that read the same KV rows share an L2.
 #include <stdint.h>
@@ -24,12 +24,19 @@ namespace smla {
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Cost-model constants, in slots walked (measured on MI355X: a 192-row,
+// 64-head, 512-slot launch ran 1.5x slower with 2 splits and 1.7x with 4 than
+// unsplit, which a per-workgroup cost of about 256 slots reproduces).
+constexpr int64_t kWgFixedSlots = 256;
+constexpr int64_t kCombineSlots = 128;
+
 int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan* plan,
               const char** err) {
   static const char* kBadHb = "head_block override must be 0, 16, 32 or 64";
   static const char* kBadSplit = "splits override must be in [0, 64]";
   static const char* kBadRemap = "remap override must be 0, 1 or 2";
   static const char* kBadGrid = "launch grid exceeds 2^31 - 1 workgroups";
+  static const char* kBadVariant = "variant override must be 0, 1 or 2";
   if (num_cus <= 0) num_cus = 256;
   *plan = smla_plan{};
 
@@ -43,10 +50,22 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   } else {
     hb = pb.heads <= 16 ? 16 : (pb.heads <= 32 ? 32 : 64);
   }
-  const int waves = kernel_waves(hb);
-  const int lds = kernel_lds_bytes(hb, pb.dqk);
+  int variant = 0;
+  if (opt && opt->variant) {
+    if (opt->variant != 1 && opt->variant != 2) {
+      *err = kBadVariant;
+      return SMLA_ERR_INVALID_ARG;
+    }
+    variant = opt->variant;
+  }
+  // The decode kernel (16 heads, fp8) reads the pool through a 32-bit
+  // buffer range; a larger pool takes the staged-tile kernel.
+  if (variant == 0 && hb == 16 && pb.kv_fp8 && pb.pool_bytes > kMaxBufferBytes) variant = 1;
+  const KernelShape ks = kernel_shape(hb, pb.dqk, pb.kv_fp8 != 0, variant);
+  const int waves = ks.waves;
+  const int lds = ks.lds_bytes;
   const int64_t head_blocks = ceil_div(pb.heads, hb);
-  const int64_t tiles = ceil_div(pb.topk, kTileKeys);
+  const int64_t tiles = ceil_div(pb.topk, ks.tile);
 
   // Workgroups a CU holds at once: 160 KB of LDS and 8 waves (the kernels
   // need up to 256 VGPRs, i.e. 2 waves per SIMD).
@@ -63,10 +82,24 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
       return SMLA_ERR_INVALID_ARG;
     }
     splits = std::min<int64_t>(opt->splits, tiles);
-  } else if (base > 0 && base < slots) {
-    const int64_t want = ceil_div(2 * slots, base);
-    const int64_t cap = std::max<int64_t>(1, tiles / 2);
-    splits = std::max<int64_t>(1, std::min<int64_t>({want, cap, int64_t(kMaxSplits)}));
+  } else if (base > 0 && base < 2 * slots) {
+    // Makespan in tile-walk units: rounds of workgroups times the tiles each
+    // walks plus a fixed per-workgroup cost (Q load, first gather, epilogue),
+    // plus the combine pass when splitting. Smallest cost wins; ties keep
+    // fewer splits.
+    auto cost = [&](int64_t s) {
+      const int64_t tps_s = ceil_div(tiles, s);
+      const int64_t rounds = ceil_div(base * s, slots);
+      return rounds * (tps_s * ks.tile + kWgFixedSlots) + (s > 1 ? kCombineSlots : 0);
+    };
+    int64_t best = cost(1);
+    for (int64_t s = 2; s <= std::min<int64_t>(tiles, kMaxSplits); ++s) {
+      const int64_t c = cost(s);
+      if (c < best) {
+        best = c;
+        splits = s;
+      }
+    }
   }
   // No empty splits: every split walks at least one tile.
   const int64_t tps = ceil_div(tiles, splits);
@@ -96,6 +129,8 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   plan->waves = waves;
   plan->lds_bytes = lds;
   plan->tiles_per_split = int32_t(tps);
+  plan->tile_slots = ks.tile;
+  plan->variant = variant;
   plan->grid = grid;
   if (splits > 1) {
     const int64_t o_bytes = splits * pb.rows * pb.heads * kDv * 4;

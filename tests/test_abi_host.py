@@ -122,7 +122,8 @@ def _plan(R, H, D=576, K=2048, dtype=torch.float8_e4m3fn, **kw):
 ])
 def test_plan_is_legal(R, H, D, K):
     p = _plan(R, H, D, K)
-    tiles = -(-K // 64)
+    assert p["tile_slots"] in (16, 64, 128)
+    tiles = -(-K // p["tile_slots"])
     assert p["head_block"] in (16, 32, 64)
     assert p["head_blocks"] == -(-H // p["head_block"])
     assert 1 <= p["splits"] <= 64
@@ -144,7 +145,8 @@ def test_plan_head_block_choice_and_overrides():
     assert _plan(4, 16, K=2048)["splits"] > 1      # a tiny launch gets split
     p = _plan(4, 16, K=2048, head_block=64, splits=8, remap=2)
     assert (p["head_block"], p["splits"], p["remap"]) == (64, 8, 0)
-    assert _plan(4, 16, K=128, splits=8)["splits"] == 2  # capped at the tile count
+    p = _plan(4, 16, K=128, splits=8, dtype=torch.bfloat16)
+    assert p["splits"] == 128 // p["tile_slots"]  # capped at the tile count
     with pytest.raises(_lib.SparseMLAError):
         _plan(4, 16, head_block=24)
     with pytest.raises(_lib.SparseMLAError):

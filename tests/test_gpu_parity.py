@@ -135,7 +135,7 @@ def test_invalid_every_other_slot_and_leading_tiles():
     inp = _case(topk=384, kv_dtype="fp8")
     idx = inp.indices.clone()
     idx[0:3, ::2] = -1             # every other slot
-    idx[3:5, :192] = -1            # three whole leading tiles
+    idx[3:5, :192] = -1            # 192 leading slots (whole leading tiles)
     idx[5, :] = -5                 # a row with no valid slot
     inp.indices = idx
     _check(inp)
@@ -265,3 +265,18 @@ def test_zero_rows_noop():
     lse = torch.empty((0, 16), dtype=torch.float32, device="cuda")
     _lib.sparse_mla_fwd(q[:0], pool, scale, idx[:0], inp.sm_scale, out, lse)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (129, 1), (17, 1), (1000, 3), (2048, 5)])
+def test_decode_fp8_variants(variant, topk, splits):
+    """The three 16-head fp8 kernels (the decode kernel; the staged-tile kernel
+    with 4 waves over 64-slot tiles; with 8 waves over 128-slot tiles and two
+    tiles in flight) on ragged top-k, with and without splits."""
+    inp = _case(rows=7, heads=16, topk=topk, pool_rows=8192, kv_dtype="fp8", invalid_per_row=37,
+                seed=topk + splits)
+    idx = inp.indices.clone()
+    idx[2, : min(topk, 300)] = -1   # leading tiles of a row invalid
+    idx[5, :] = -1                  # a row with no valid slot
+    inp.indices = idx
+    _check(inp, variant=variant, splits=splits)
