@@ -73,9 +73,10 @@ typedef struct smla_options {
   int32_t head_block;      /* 0 = planner's choice, else 16, 32 or 64 heads per workgroup */
   int32_t splits;          /* 0 = planner's choice, else 1..64 splits of each row's slots */
   int32_t remap;           /* 0 = planner's choice, 1 = XCD-aware order, 2 = grid order */
-  int32_t variant;         /* kernel instance; 0 = default. 16-head fp8 only: 1 = 4-wave
+  int32_t variant;         /* kernel instance; 0 = default. 16-head fp8: 1 = 4-wave
                               64-slot staged-tile kernel, 2 = 8-wave 128-slot staged-tile
-                              kernel with two tiles of gathers in flight */
+                              kernel with two tiles of gathers in flight. 64-head: 1 =
+                              single-buffered staged-tile kernel */
   void* workspace;         /* optional caller device buffer for split partials */
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
 } smla_options;

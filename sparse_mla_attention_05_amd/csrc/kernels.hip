@@ -394,7 +394,9 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
 // pool, variant 0 is the decode kernel (decode.hip); variant 1 is the
 // 4-wave, 64-slot instance below and variant 2 runs 8 waves over 128-slot
 // tiles, one workgroup per CU (its bf16 tile takes 146 KB of LDS), with two
-// tiles of gathers in flight. Elsewhere every variant is variant 0.
+// tiles of gathers in flight. For 64 heads, variant 0 is the prefill kernel
+// (prefill.hip) and variant 1 the 8-wave staged-tile instance below.
+// Elsewhere every variant is variant 0.
 template <int NHG, int NW, int TK, bool DBUF>
 struct Inst {
   static constexpr int kNHG = NHG, kNW = NW, kTK = TK;
@@ -433,7 +435,9 @@ hipError_t launch_by_head_block(int head_block, int variant, const FwdParams& p,
       if (FP8 && variant == 0) return static_cast<hipError_t>(launch_decode(p, DQK, st));
       return variant == 2 ? launch_inst<16, 2, DQK, FP8>(p, st) : launch_inst<16, 0, DQK, FP8>(p, st);
     case 32: return launch_inst<32, 0, DQK, FP8>(p, st);
-    case 64: return launch_inst<64, 0, DQK, FP8>(p, st);
+    case 64:
+      if (variant == 0) return static_cast<hipError_t>(launch_prefill(p, DQK, FP8, st));
+      return launch_inst<64, 0, DQK, FP8>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -448,7 +452,9 @@ KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant) {
       if (variant == 2) return fp8 ? shape_of<16, true, 2>(dqk) : shape_of<16, false, 2>(dqk);
       return fp8 ? shape_of<16, true, 0>(dqk) : shape_of<16, false, 0>(dqk);
     case 32: return fp8 ? shape_of<32, true, 0>(dqk) : shape_of<32, false, 0>(dqk);
-    case 64: return fp8 ? shape_of<64, true, 0>(dqk) : shape_of<64, false, 0>(dqk);
+    case 64:
+      if (variant == 0) return prefill_shape(dqk, fp8);
+      return fp8 ? shape_of<64, true, 0>(dqk) : shape_of<64, false, 0>(dqk);
     default: return KernelShape{};
   }
 }

@@ -68,6 +68,10 @@ KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant);
 KernelShape decode_shape(int dqk);
 int launch_decode(const FwdParams& p, int dqk, void* stream);
 
+// The 64-head prefill kernel (prefill.hip): its shape and its launch.
+KernelShape prefill_shape(int dqk, bool fp8);
+int launch_prefill(const FwdParams& p, int dqk, bool fp8, void* stream);
+
 // Pure host planner: no HIP calls. Returns SMLA_OK or an error status and
 // fills `err` with the reason.
 int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan* plan,
