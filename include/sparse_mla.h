@@ -76,7 +76,9 @@ typedef struct smla_options {
   int32_t variant;         /* kernel instance; 0 = default. 16-head fp8: 1 = 4-wave
                               64-slot staged-tile kernel, 2 = 8-wave 128-slot staged-tile
                               kernel with two tiles of gathers in flight. 64-head: 1 =
-                              single-buffered staged-tile kernel */
+                              single-buffered staged-tile kernel, 2 = 8-wave
+                              double-buffered kernel (the default over bf16 pools; the
+                              fp8 default is the 4-wave kernel) */
   void* workspace;         /* optional caller device buffer for split partials */
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
 } smla_options;

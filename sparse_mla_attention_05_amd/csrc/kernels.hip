@@ -394,9 +394,11 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
 // pool, variant 0 is the decode kernel (decode.hip); variant 1 is the
 // 4-wave, 64-slot instance below and variant 2 runs 8 waves over 128-slot
 // tiles, one workgroup per CU (its bf16 tile takes 146 KB of LDS), with two
-// tiles of gathers in flight. For 64 heads, variant 0 is the prefill kernel
-// (prefill.hip) and variant 1 the 8-wave staged-tile instance below.
-// Elsewhere every variant is variant 0.
+// tiles of gathers in flight. For 64 heads, variant 0 is the 4-wave kernel
+// of prefill_fp8.hip over fp8 pools and the 8-wave kernel of prefill.hip
+// over bf16 pools, variant 1 the 8-wave staged-tile instance below and
+// variant 2 the 8-wave kernel of prefill.hip. Elsewhere every variant is
+// variant 0.
 template <int NHG, int NW, int TK, bool DBUF>
 struct Inst {
   static constexpr int kNHG = NHG, kNW = NW, kTK = TK;
@@ -436,8 +438,9 @@ hipError_t launch_by_head_block(int head_block, int variant, const FwdParams& p,
       return variant == 2 ? launch_inst<16, 2, DQK, FP8>(p, st) : launch_inst<16, 0, DQK, FP8>(p, st);
     case 32: return launch_inst<32, 0, DQK, FP8>(p, st);
     case 64:
-      if (variant == 0) return static_cast<hipError_t>(launch_prefill(p, DQK, FP8, st));
-      return launch_inst<64, 0, DQK, FP8>(p, st);
+      if (variant == 1) return launch_inst<64, 0, DQK, FP8>(p, st);
+      if (FP8 && variant == 0) return static_cast<hipError_t>(launch_prefill_fp8(p, DQK, st));
+      return static_cast<hipError_t>(launch_prefill(p, DQK, FP8, st));
     default: return hipErrorInvalidValue;
   }
 }
@@ -453,8 +456,9 @@ KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant) {
       return fp8 ? shape_of<16, true, 0>(dqk) : shape_of<16, false, 0>(dqk);
     case 32: return fp8 ? shape_of<32, true, 0>(dqk) : shape_of<32, false, 0>(dqk);
     case 64:
-      if (variant == 0) return prefill_shape(dqk, fp8);
-      return fp8 ? shape_of<64, true, 0>(dqk) : shape_of<64, false, 0>(dqk);
+      if (variant == 1) return fp8 ? shape_of<64, true, 0>(dqk) : shape_of<64, false, 0>(dqk);
+      if (fp8 && variant == 0) return prefill_fp8_shape(dqk);
+      return prefill_shape(dqk, fp8);
     default: return KernelShape{};
   }
 }

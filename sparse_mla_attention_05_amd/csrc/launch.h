@@ -68,9 +68,20 @@ KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant);
 KernelShape decode_shape(int dqk);
 int launch_decode(const FwdParams& p, int dqk, void* stream);
 
-// The 64-head prefill kernel (prefill.hip): its shape and its launch.
+// The 8-wave 64-head kernel (prefill.hip): its shape and its launch.
 KernelShape prefill_shape(int dqk, bool fp8);
 int launch_prefill(const FwdParams& p, int dqk, bool fp8, void* stream);
+
+// The 4-wave 64-head kernel for fp8 pools (prefill_fp8.hip).
+KernelShape prefill_fp8_shape(int dqk);
+int launch_prefill_fp8(const FwdParams& p, int dqk, void* stream);
+
+// True when the (head block, pool dtype, variant) instance addresses the pool
+// through a buffer descriptor with 32-bit offsets (pools up to
+// kMaxBufferBytes); the other instances use 64-bit addresses.
+inline bool uses_buffer_range(int head_block, bool fp8, int variant) {
+  return (head_block == 16 && fp8 && variant == 0) || (head_block == 64 && variant != 1);
+}
 
 // Pure host planner: no HIP calls. Returns SMLA_OK or an error status and
 // fills `err` with the reason.

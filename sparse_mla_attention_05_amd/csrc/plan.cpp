@@ -58,9 +58,9 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
     }
     variant = opt->variant;
   }
-  // The decode (16 heads, fp8) and prefill (64 heads) kernels read the pool
-  // through a 32-bit buffer range; a larger pool takes the staged-tile kernel.
-  if (variant == 0 && ((hb == 16 && pb.kv_fp8) || hb == 64) && pb.pool_bytes > kMaxBufferBytes)
+  // The decode (16 heads, fp8) and 64-head kernels read the pool through a
+  // 32-bit buffer range; a larger pool takes the staged-tile kernel.
+  if (uses_buffer_range(hb, pb.kv_fp8 != 0, variant) && pb.pool_bytes > kMaxBufferBytes)
     variant = 1;
   const KernelShape ks = kernel_shape(hb, pb.dqk, pb.kv_fp8 != 0, variant);
   const int waves = ks.waves;

@@ -280,3 +280,51 @@ def test_decode_fp8_variants(variant, topk, splits):
     idx[5, :] = -1                  # a row with no valid slot
     inp.indices = idx
     _check(inp, variant=variant, splits=splits)
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("d_qk,kv,heads", [(576, "fp8", 64), (512, "fp8", 80), (576, "bf16", 64)])
+@pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (17, 1), (1000, 3)])
+def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
+    """The 64-head kernels (variant 0: the 4-wave kernel over fp8 pools, the
+    8-wave kernel over bf16 pools; 1: the single-buffered staged-tile kernel;
+    2: the 8-wave kernel) on ragged top-k, odd tile counts, a partial head
+    block, leading invalid tiles and an empty row, with and without splits."""
+    inp = _case(rows=5, heads=heads, d_qk=d_qk, topk=topk, pool_rows=8192, kv_dtype=kv,
+                invalid_per_row=29, seed=topk + splits + d_qk)
+    idx = inp.indices.clone()
+    idx[1, : min(topk, 200)] = -1   # leading tiles of a row invalid
+    idx[3, :] = -1                  # a row with no valid slot
+    inp.indices = idx
+    print(f"\n[parity] 64-head variant={variant} d={d_qk} kv={kv} H={heads} K={topk} S={splits}",
+          flush=True)
+    _check(inp, variant=variant, splits=splits, head_block=64)
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("splits", [1, 2])
+def test_score_jump_after_first_tile(kv, splits):
+    """Every head's first 64 slots point at near-zero keys and later slots at
+    keys whose scores are ~138 higher in the log2 domain, so a reference max
+    taken from the first tile would overflow P: the kernels must move their
+    reference (rescale, or a second walk from the row max)."""
+    R, H, D, K, N = 3, 64, 576, 320, 600
+    inp = _case(rows=R, heads=H, d_qk=D, topk=K, pool_rows=N, kv_dtype=kv, seed=5)
+    g = torch.Generator().manual_seed(11)
+    pool = torch.randn((N, D), generator=g) * 0.01
+    pool[300:] = 1.0 + 0.05 * torch.randn((N - 300, D), generator=g)
+    q = torch.full((R, H, D), 4.0) + 0.1 * torch.randn((R, H, D), generator=g)
+    inp.q = q.to(torch.bfloat16)
+    if kv == "fp8":
+        from sparse_mla_attention_05_amd.inputs import quantize_fp8
+        inp.pool, inp.kv_scale = quantize_fp8(pool)
+    else:
+        inp.pool = pool.to(torch.bfloat16)
+    idx = torch.empty((R, K), dtype=torch.int32)
+    for r in range(R):
+        idx[r, :64] = torch.randperm(300, generator=g)[:64].to(torch.int32)
+        idx[r, 64:] = (300 + torch.randperm(N - 300, generator=g)[: K - 64]).to(torch.int32)
+    idx[1, 100:110] = -1
+    inp.indices = idx
+    print(f"\n[parity] score jump kv={kv} splits={splits}", flush=True)
+    _check(inp, splits=splits)
