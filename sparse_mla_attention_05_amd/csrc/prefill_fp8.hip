@@ -11,28 +11,34 @@
 //
 // Layout of the work, chosen for gfx950 rather than taken from the pages:
 //  * One workgroup = (row, 64 heads, split), 4 wavefronts, one workgroup per
-//    CU, one wavefront per SIMD. Wave w owns heads 16w..16w+15 over every
-//    slot: Q^T in VGPRs, S^T and O^T accumulators in AGPRs. S^T = K Q^T
-//    leaves each lane 4 consecutive slots of one head, which is the B operand
-//    layout of O^T += V^T P^T, so P never leaves the registers and the
-//    softmax needs no exchange between waves.
-//  * K/V tiles of 64 slots are staged once per workgroup as bf16 rows in
-//    LDS, double buffered. Rows are unpadded; the 16-byte chunk index of
-//    row r is XOR-permuted by a function of r chosen so that the K operand
-//    reads (ds_read_b128), the transposed V reads (ds_read_b64_tr_b16) and
-//    the staging writes (ds_write_b128) are all free of bank conflicts on
-//    gfx950.
-//  * The gather for tile t+2 (unconditional raw buffer loads: invalid slots
-//    read past the buffer range and get zeros) is in flight while tile t is
-//    computed; tile t+1 is widened and written into the other buffer between
-//    the QK dots of tile t. One barrier per tile.
-//  * Fixed reference: a head's reference max is the max of its first tile
-//    with a valid slot (O is still zero then), so O is never rescaled and
-//    stays in the MFMA accumulators. P = exp2(s - ref) is exact in real
-//    arithmetic whatever the reference; the bf16 P and fp32 sums stay in
-//    range while every later score is below ref + 64 (log2 domain). If any
-//    head exceeds that, the workgroup walks its slots a second time with the
-//    exact row max, tracked during the first walk, as the reference.
+//    CU, one wavefront per SIMD. The kernel is bound by LDS traffic, so each
+//    operand fragment read from LDS feeds two dots: wave (hp, kh) holds Q^T
+//    of heads 32hp..32hp+31 and computes S^T = K Q^T for slot half kh of
+//    each 64-slot tile (one K fragment, two head blocks); for O^T += V^T P^T
+//    it owns output columns 256kh..256kh+255 of the same 32 heads over all
+//    64 slots (one V fragment, two head blocks). S^T leaves each lane 4
+//    consecutive slots of one head, the B operand layout of the PV dot, so a
+//    wave's own P never leaves its registers; the two waves of a pair swap
+//    the other half's P through LDS (2 KB each way per tile).
+//  * K/V tiles are staged once per workgroup as bf16 rows in LDS, double
+//    buffered. Rows are unpadded; the 16-byte chunk index of row r is
+//    XOR-permuted by a function of r chosen so that the K operand reads
+//    (ds_read_b128), the transposed V reads (ds_read_b64_tr_b16) and the
+//    staging writes (ds_write_b128) are all free of bank conflicts on gfx950.
+//  * Tile t+1 is widened and written into the other buffer between the QK
+//    dots of tile t; as each of a thread's chunks is written, its registers
+//    are refilled with the gather for tile t+2 (unconditional raw buffer
+//    loads: invalid slots read past the buffer range and get zeros), so each
+//    gather has about a whole tile to land. Two barriers per tile: P swap,
+//    buffer reuse.
+//  * Fixed reference: a head's reference max is the max of the first tile
+//    that has a valid slot (O is still zero then; the pair agrees on it
+//    through LDS), so O is never rescaled and stays in the MFMA
+//    accumulators. P = exp2(s - ref) is exact in real arithmetic whatever the
+//    reference; the bf16 P and fp32 sums stay in range while every later
+//    score is below ref + 64 (log2 domain). If any head exceeds that, the
+//    workgroup walks its slots a second time with the exact row max,
+//    tracked during the first walk, as the reference.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,15 +66,15 @@ struct XCfg {
   static constexpr int TPR = NT / TK;              // staging threads per slot
   static constexpr int LPT = SRC_CH / TPR;         // fp8 chunks per staging thread
   static constexpr int TILE = TK * ROW;            // bytes per bf16 tile
-  static constexpr int NDB = kDv / 16;             // 16-column output blocks
+  static constexpr int NDW = kDv / 16 / 2;         // 16-column output blocks per wave
   static constexpr int SWB = DQK == 576 ? 8 : 16;  // chunk span the row permutation touches
   static constexpr int NQB = SWB / 4;              // K-operand address bases
   static constexpr int NVB = SWB / 2;              // V-operand address bases
   static constexpr int NSB = SWB / 8;              // staging address bases per half
-  static constexpr int NSLOTB = TK / 16;           // 16-slot blocks per tile
-  static constexpr int LDS_BYTES = 2 * TILE + 2 * TK * 4 + 16;
+  static constexpr int LDS_BYTES = 2 * TILE + 2 * TK * 4 + kXWaves * 2 * 64 * 16 + 64;
   static_assert(SRC_CH % TPR == 0, "staging split");
   static_assert(LPT % NSB == 0, "staging bases");
+  static_assert(LPT <= KSTEPS / 2, "staging spread over the k-steps");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -86,43 +92,57 @@ __global__ void __launch_bounds__(kXWaves * 64, 1) __attribute__((amdgpu_waves_p
 prefill_fp8_kernel(const FwdParams p) {
   using C = XCfg<DQK>;
   constexpr int TK = C::TK, ROW = C::ROW, TILE = C::TILE, KSTEPS = C::KSTEPS;
-  constexpr int LPT = C::LPT, NDB = C::NDB, SWB = C::SWB;
+  constexpr int LPT = C::LPT, NDW = C::NDW, SWB = C::SWB;
   constexpr int NQB = C::NQB, NVB = C::NVB, NSB = C::NSB;
 
   // Two bf16 tile buffers as separate arrays, so the compiler can tell the
   // staging writes into one from the operand reads of the other.
   __shared__ __attribute__((aligned(16))) uint8_t tile0[TILE];
   __shared__ __attribute__((aligned(16))) uint8_t tile1[TILE];
-  __shared__ __attribute__((aligned(16))) float kbias[2 * TK];  // 0 (valid slot) or -inf
+  __shared__ __attribute__((aligned(16))) float kbias[2 * TK];   // 0 (valid slot) or -inf
+  // P swap (and, outside the tile loop, the pair's max / sum exchange):
+  // [wave][head block][lane] 16 bytes.
+  __shared__ __attribute__((aligned(16))) u32x4 xch[kXWaves * 2 * 64];
   __shared__ uint32_t redo[1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const int hp = wave >> 1, kh = wave & 1;
+  const int partner = wave ^ 1;
 
   int64_t work = p.remap ? smla_xcd_work(blockIdx.x, p.grid) : int64_t(blockIdx.x);
   const int hblk = int(work % p.head_blocks);
   work /= p.head_blocks;
   const int split = int(work % p.splits);
   const int64_t r = work / p.splits;
-  const int head = hblk * C::HB + 16 * wave + l16;  // this lane's head (S^T / O^T column)
-  const bool head_ok = head < p.heads;
+  const int h0 = hblk * C::HB + 32 * hp;  // heads h0 + 16hb + l16 of this lane
 
   const int ntiles = (p.topk + TK - 1) / TK;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(ntiles, t_begin + p.tiles_per_split);
 
-  // Q^T operands: columns 8g + 32s .. +7 of this lane's head.
-  bf16x8 qf[KSTEPS];
-  if (head_ok) {
-    const uint16_t* qp = p.q + r * p.q_rs + int64_t(head) * p.q_hs + 8 * g;
+  // Q^T operands: head h0 + 16hb + l16, columns 8g + 32s .. +7.
+  bf16x8 qf[2][KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
-  } else {
+  for (int hb = 0; hb < 2; ++hb) {
+    const int h = h0 + 16 * hb + l16;
+    if (h < p.heads) {
+      const uint16_t* qp = p.q + r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      for (int s = 0; s < KSTEPS; ++s)
+        qf[hb][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
   }
+  // Keep Q^T in VGPRs: left to itself the allocator parks it in AGPRs (the
+  // dots can read it there) and then has no AGPRs left for O^T and S^T.
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(qf[hb][s]));
   const float kv_scale = *p.kv_scale;
   const float score_scale = p.sm_log2 * kv_scale;
 
@@ -138,12 +158,17 @@ prefill_fp8_kernel(const FwdParams p) {
   const __amdgpu_buffer_rsrc_t pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.pool), 0, p.pool_bytes, kXBufferWord3);
   u32x4 pre[LPT];
+  auto row_off = [&](int id) -> uint32_t {
+    return id >= 0 ? uint32_t(id) * uint32_t(p.pool_rs_bytes) : kXOutOfRange;
+  };
+  auto gather_one = [&](int i, uint32_t off) {
+    pre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           pool_rsrc, off + 16u * uint32_t(gq + 4 * i), 0, 0));
+  };
   auto gather = [&](int id) {
-    const uint32_t off = id >= 0 ? uint32_t(id) * uint32_t(p.pool_rs_bytes) : kXOutOfRange;
+    const uint32_t off = row_off(id);
 #pragma unroll
-    for (int i = 0; i < LPT; ++i)
-      pre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             pool_rsrc, off + 16u * uint32_t(gq + 4 * i), 0, 0));
+    for (int i = 0; i < LPT; ++i) gather_one(i, off);
   };
   // Destination of widened chunk i (low or high 8 columns) in a tile:
   // logical chunk 8i + 2gq + half of row gk.
@@ -162,41 +187,42 @@ prefill_fp8_kernel(const FwdParams p) {
     *reinterpret_cast<u32x4*>(tile + sbase[1][i % NSB] + hi_off) = u32x4{w2.x, w2.y, w3.x, w3.y};
   };
 
-  // ---- K operand addresses: row 16j + l16, logical chunk g + 4s.
+  // ---- K operand addresses: row 32kh + 16j + l16, logical chunk g + 4s.
   const int qperm = tile_perm<DQK>(l16);
   int kbase[NQB];
 #pragma unroll
-  for (int b = 0; b < NQB; ++b) kbase[b] = l16 * ROW + 16 * ((4 * b + g) ^ qperm);
-  // ---- V^T operand addresses: rows 32ks + 4g + l16/4 (+16), columns
-  // 16d + 4(l16 % 4) .. +3, i.e. logical chunk 2d + (l16/2)%2, byte 8(l16%2).
+  for (int b = 0; b < NQB; ++b) kbase[b] = (32 * kh + l16) * ROW + 16 * ((4 * b + g) ^ qperm);
+  // ---- V^T operand addresses: rows 32x + 4g + l16/4 (+16) of slot half x,
+  // columns 256kh + 16d + 4(l16 % 4) .. +3, i.e. logical chunk
+  // 32kh + 2d + (l16/2)%2, byte 8(l16%2).
   const int vrow = 4 * g + (l16 >> 2);
   const int vperm = tile_perm<DQK>(vrow);
   int vbase[NVB];
 #pragma unroll
   for (int b = 0; b < NVB; ++b)
-    vbase[b] = vrow * ROW + 16 * ((2 * b + ((l16 >> 1) & 1)) ^ vperm) + 8 * (l16 & 1);
+    vbase[b] = vrow * ROW + 16 * 32 * kh + 16 * ((2 * b + ((l16 >> 1) & 1)) ^ vperm) + 8 * (l16 & 1);
 
-  floatx4 o[NDB];
-  float m_ref;       // reference max (log2 domain) of this lane's head
-  float m_run;       // running max of this lane's scores
-  float l_part;      // this lane's share of the head's row sum
+  floatx4 o[NDW][2];
+  float m_ref[2];    // reference max (log2 domain) of head 16hb + l16, shared by the pair
+  float m_run[2];    // running max of this lane's scores of that head
+  float l_part[2];   // this lane's share of the head's row sum over the wave's slots
+  bool ref_set;      // the references are set (uniform over the workgroup)
   bool over;         // some score of this lane exceeded m_ref + kXRefSlack
 
-  // QK of the tile in `cur`, with the staging of the next tile from `pre`
-  // into `nxt` spread between the k-steps.
-  floatx4 sacc[C::NSLOTB];
-  auto qk_and_stage = [&](const uint8_t* cur, uint8_t* nxt) {
+  // QK of this wave's 32 slots of the tile in `cur`, with the staging of the
+  // next tile from `pre` into `nxt` spread between the k-steps.
+  floatx4 sacc[2][2];
+  auto qk_and_stage = [&](const uint8_t* cur, uint8_t* nxt, uint32_t next_off) {
 #pragma unroll
-    for (int j = 0; j < C::NSLOTB; ++j) sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) sacc[j][0] = sacc[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
     // K fragments in a ring of KRING k-steps: the reads run KRING-1 k-steps
     // ahead of the dots that use them.
     constexpr int KRING = 3;
-    bf16x8 ka[KRING][C::NSLOTB];
-    auto load_k = [&](int s, bf16x8 (&dst)[C::NSLOTB]) {
+    bf16x8 ka[KRING][2];
+    auto load_k = [&](int s, bf16x8 (&dst)[2]) {
       const uint8_t* kp = cur + kbase[s % NQB] + 16 * SWB * (s / NQB);
-#pragma unroll
-      for (int j = 0; j < C::NSLOTB; ++j)
-        dst[j] = *reinterpret_cast<const bf16x8*>(kp + j * 16 * ROW);
+      dst[0] = *reinterpret_cast<const bf16x8*>(kp);
+      dst[1] = *reinterpret_cast<const bf16x8*>(kp + 16 * ROW);
     };
 #pragma unroll
     for (int s = 0; s < KRING - 1; ++s) load_k(s, ka[s]);
@@ -207,90 +233,115 @@ prefill_fp8_kernel(const FwdParams p) {
       if (s + KRING - 1 < KSTEPS) load_k(s + KRING - 1, ka[(s + KRING - 1) % KRING]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < C::NSLOTB; ++j)
-        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s % KRING][j], qf[s], sacc[j], 0, 0, 0);
-      if (s % 2 == 1 && s / 2 < LPT) stage_chunk(s / 2, nxt);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          sacc[j][hb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s % KRING][j], qf[hb][s], sacc[j][hb], 0, 0, 0);
+      if (s % 2 == 1 && s / 2 < LPT) {
+        // Stage chunk s/2 of the next tile, then refill its registers with
+        // the tile after: each gather gets almost a whole tile to land.
+        stage_chunk(s / 2, nxt);
+        gather_one(s / 2, next_off);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Softmax weights of the tile in buffer `buf`; returns the P^T operands of
-  // the two 32-slot k-steps (k-slot order: slots 4g..4g+3 of block 2ks, then
-  // of block 2ks+1).
-  auto softmax = [&](int buf, bf16x8 (&pf)[2]) {
-    const float* kb = kbias + buf * TK + 4 * g;
-    float v[C::NSLOTB][4];
-    float mx = kNegInf;
+  // Softmax weights of this wave's 32 slots of the tile in buffer `buf`;
+  // returns its P^T operands (k-slot order: slots 4g..4g+3 of the first 16,
+  // then of the second 16) for both head blocks.
+  auto softmax = [&](int buf, bf16x8 (&pown)[2]) {
+    const float* kb = kbias + buf * TK + 32 * kh + 4 * g;
+    const floatx4 b0 = *reinterpret_cast<const floatx4*>(kb);
+    const floatx4 b1 = *reinterpret_cast<const floatx4*>(kb + 16);
+    float v[2][8];
+    float mx[2];
 #pragma unroll
-    for (int j = 0; j < C::NSLOTB; ++j) {
-      const floatx4 b = *reinterpret_cast<const floatx4*>(kb + 16 * j);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[j][i] = __builtin_fmaf(sacc[j][i], score_scale, b[i]);
-        mx = fmaxf(mx, v[j][i]);
-      }
-    }
-    m_run = fmaxf(m_run, mx);
-    // Slot validity is shared by all heads, so the reference is unset either
-    // for every lane of the wave or for none.
-    if (m_ref == kNegInf) {
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      m_ref = fmaxf(mx, __shfl_xor(mx, 32));
-    }
-    over = over || mx > m_ref + kXRefSlack;
-    const float mu = m_ref == kNegInf ? 0.f : m_ref;
-    float e[C::NSLOTB][4];
-#pragma unroll
-    for (int j = 0; j < C::NSLOTB; ++j)
+    for (int hb = 0; hb < 2; ++hb) {
+      mx[hb] = kNegInf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        e[j][i] = __builtin_amdgcn_exp2f(v[j][i] - mu);
-        l_part += e[j][i];
+        v[hb][i] = __builtin_fmaf(sacc[0][hb][i], score_scale, b0[i]);
+        v[hb][4 + i] = __builtin_fmaf(sacc[1][hb][i], score_scale, b1[i]);
+        mx[hb] = fmaxf(mx[hb], fmaxf(v[hb][i], v[hb][4 + i]));
       }
+      m_run[hb] = fmaxf(m_run[hb], mx[hb]);
+    }
+    if (!ref_set) {
+      // Uniform over the workgroup: does this tile hold any valid slot?
+      if (__ballot(kbias[buf * TK + lane] == 0.f) != 0) {
+        // First tile with a valid slot: the pair agrees on the reference.
+        float* xf = reinterpret_cast<float*>(xch);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      pf[ks] = __builtin_bit_cast(
-          bf16x8, u32x4{pack2_bf16(e[2 * ks][0], e[2 * ks][1]), pack2_bf16(e[2 * ks][2], e[2 * ks][3]),
-                        pack2_bf16(e[2 * ks + 1][0], e[2 * ks + 1][1]),
-                        pack2_bf16(e[2 * ks + 1][2], e[2 * ks + 1][3])});
+        for (int hb = 0; hb < 2; ++hb) {
+          float t = fmaxf(mx[hb], __shfl_xor(mx[hb], 16));
+          t = fmaxf(t, __shfl_xor(t, 32));
+          xf[(wave * 2 + hb) * 64 + lane] = t;
+          mx[hb] = t;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) m_ref[hb] = fmaxf(mx[hb], xf[(partner * 2 + hb) * 64 + lane]);
+        __syncthreads();  // the exchange area is free again before the P swap
+        ref_set = true;
+      }
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      over = over || mx[hb] > m_ref[hb] + kXRefSlack;
+      const float mu = m_ref[hb] == kNegInf ? 0.f : m_ref[hb];
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(v[hb][i] - mu);
+        l_part[hb] += e[i];
+      }
+      pown[hb] = __builtin_bit_cast(bf16x8, u32x4{pack2_bf16(e[0], e[1]), pack2_bf16(e[2], e[3]),
+                                                  pack2_bf16(e[4], e[5]), pack2_bf16(e[6], e[7])});
+    }
   };
-  // O^T += V^T P^T over the tile in `cur`.
-  // V^T fragments in a ring of VRING output blocks; the first VRING-1 are
-  // read before the softmax (they do not depend on P).
+  // V^T fragments of slot half x (0: the wave's own, 1: the partner's) for
+  // the wave's output blocks d, in a ring of VRING; the first VRING-1 of a
+  // pass are read ahead of the work that precedes it.
   constexpr int VRING = 3;
-  bf16x8 vf[VRING][2];
-  auto load_v = [&](const uint8_t* cur, int d, bf16x8 (&dst)[2]) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint16_t* va = reinterpret_cast<const uint16_t*>(
-          cur + vbase[d % NVB] + 16 * SWB * (d / NVB) + 32 * ks * ROW);
-      const u32x2 v0 = lds_read_tr16(va);
-      const u32x2 v1 = lds_read_tr16(va + 8 * ROW);  // 16 rows further
-      dst[ks] = __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
-    }
+  bf16x8 vf[VRING];
+  const int vhalf[2] = {32 * kh * ROW, 32 * (kh ^ 1) * ROW};
+  auto load_v = [&](const uint8_t* cur, int x, int d) -> bf16x8 {
+    const uint16_t* va = reinterpret_cast<const uint16_t*>(
+        cur + vbase[d % NVB] + 16 * SWB * (d / NVB) + vhalf[x]);
+    const u32x2 v0 = lds_read_tr16(va);
+    const u32x2 v1 = lds_read_tr16(va + 8 * ROW);  // 16 rows further
+    return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
   };
-  auto pv_prefetch = [&](const uint8_t* cur) {
+  auto pv_prefetch = [&](const uint8_t* cur, int x) {
 #pragma unroll
-    for (int d = 0; d < VRING - 1; ++d) load_v(cur, d, vf[d]);
+    for (int d = 0; d < VRING - 1; ++d) vf[d] = load_v(cur, x, d);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto pv = [&](const uint8_t* cur, const bf16x8 (&pf)[2]) {
+  // O^T += V^T P^T over slot half x of the tile in `cur` for this wave's
+  // output columns; pk is that half's P^T operand.
+  auto pv_half = [&](const uint8_t* cur, int x, const bf16x8 (&pk)[2]) {
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      if (d + VRING - 1 < NDB) load_v(cur, d + VRING - 1, vf[(d + VRING - 1) % VRING]);
+    for (int d = 0; d < NDW; ++d) {
+      if (d + VRING - 1 < NDW) vf[(d + VRING - 1) % VRING] = load_v(cur, x, d + VRING - 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d % VRING][ks], pf[ks], o[d], 0, 0, 0);
+      for (int hb = 0; hb < 2; ++hb)
+        o[d][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d % VRING], pk[hb], o[d][hb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // One walk over this split's tiles with the given starting reference.
-  auto walk = [&](float m_init) {
+
+  // One walk over this split's tiles; `preset` says m_init holds the
+  // references already (second walk).
+  auto walk = [&](float m_init0, float m_init1, bool preset) {
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-    m_ref = m_init;
-    m_run = kNegInf;
-    l_part = 0.f;
+    for (int d = 0; d < NDW; ++d) o[d][0] = o[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    m_ref[0] = m_init0;
+    m_ref[1] = m_init1;
+    m_run[0] = m_run[1] = kNegInf;
+    l_part[0] = l_part[1] = 0.f;
+    ref_set = preset;
     over = false;
     if (t_begin >= t_end) return;
     int id_a = load_idx(t_begin);
@@ -304,18 +355,29 @@ prefill_fp8_kernel(const FwdParams p) {
     __syncthreads();
     // One tile: QK of tile t from `cur` with tile t+1 (zeros past the end:
     // harmless, never read) staged into `nxt`, the buffer tile t-1 used,
-    // which every wave finished before the last barrier; then softmax, PV.
+    // which every wave finished before the last barrier; softmax; P swap;
+    // PV.
     auto step = [&](int t, const uint8_t* cur, uint8_t* nxt, int buf) {
-      qk_and_stage(cur, nxt);
+      qk_and_stage(cur, nxt, row_off(id_n));
       if (gq == 0) kbias[(buf ^ 1) * TK + gk] = id_b >= 0 ? 0.f : kNegInf;
       id_b = id_n;
-      gather(id_b);
       id_n = load_idx(t + 3);
-      pv_prefetch(cur);
-      bf16x8 pf[2];
-      softmax(buf, pf);
-      pv(cur, pf);
-      __syncthreads();
+      pv_prefetch(cur, 0);
+      bf16x8 pown[2], ppart[2];
+      softmax(buf, pown);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        xch[(wave * 2 + hb) * 64 + lane] = __builtin_bit_cast(u32x4, pown[hb]);
+      // The wave's own half first: its P is in registers, and the work
+      // covers the partner's softmax before the swap.
+      pv_half(cur, 0, pown);
+      pv_prefetch(cur, 1);
+      __syncthreads();  // P of both halves visible; tile t+1 staged
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        ppart[hb] = __builtin_bit_cast(bf16x8, xch[(partner * 2 + hb) * 64 + lane]);
+      pv_half(cur, 1, ppart);
+      __syncthreads();  // every wave is done with `cur` and with the P swap
     };
     // Tiles go in pairs (static buffer roles); an odd count ends with one
     // tile past the end, all slots invalid, which adds exactly nothing.
@@ -324,49 +386,69 @@ prefill_fp8_kernel(const FwdParams p) {
       step(t + 1, tile1, tile0, 1);
     }
   };
+
+  float* const xf = reinterpret_cast<float*>(xch);
   // Walk once; if any lane of the workgroup went over the slack, walk again
-  // from the row max (the loop body is emitted once).
-  float m_init = kNegInf;
+  // from the pair's row max (the loop body is emitted once).
+  float mi0 = kNegInf, mi1 = kNegInf;
+  bool preset = false;
 #pragma clang loop unroll(disable)
   for (int pass = 0; pass < 2; ++pass) {
-    walk(m_init);
+    walk(mi0, mi1, preset);
     if (pass == 1) break;
     if (tid == 0) redo[0] = 0u;
     __syncthreads();
     if (__ballot(over) != 0 && lane == 0) redo[0] = 1u;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float t = fmaxf(m_run[hb], __shfl_xor(m_run[hb], 16));
+      xf[(wave * 2 + hb) * 64 + lane] = fmaxf(t, __shfl_xor(t, 32));
+    }
     __syncthreads();
     const bool again = redo[0] != 0u;
+    mi0 = fmaxf(xf[(wave * 2 + 0) * 64 + lane], xf[(partner * 2 + 0) * 64 + lane]);
+    mi1 = fmaxf(xf[(wave * 2 + 1) * 64 + lane], xf[(partner * 2 + 1) * 64 + lane]);
+    preset = true;
     __syncthreads();  // every wave has read the flag before a walk reuses LDS
     if (!again) break;
-    m_init = fmaxf(m_run, __shfl_xor(m_run, 16));
-    m_init = fmaxf(m_init, __shfl_xor(m_init, 32));
   }
 
-  // ---- epilogue: the four lanes of a head hold parts of its row sum.
-  float lt = l_part;
-  lt += __shfl_xor(lt, 16);
-  lt += __shfl_xor(lt, 32);
-  if (head_ok) {
-    const float inv = lt > 0.f ? kv_scale / lt : 0.f;
-    const bool split_mode = p.splits > 1;
+  // ---- epilogue: row sums over both slot halves; normalise; store.
+  float lt[2];
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const floatx4 res = o[d] * inv;
-      const int col = 16 * d + 4 * g;
+  for (int hb = 0; hb < 2; ++hb) {
+    float t = l_part[hb] + __shfl_xor(l_part[hb], 16);
+    t += __shfl_xor(t, 32);
+    xf[(wave * 2 + hb) * 64 + lane] = t;
+    lt[hb] = t;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) lt[hb] += xf[(partner * 2 + hb) * 64 + lane];
+  const bool split_mode = p.splits > 1;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int h = h0 + 16 * hb + l16;
+    if (h >= p.heads) continue;
+    const float inv = lt[hb] > 0.f ? kv_scale / lt[hb] : 0.f;
+#pragma unroll
+    for (int d = 0; d < NDW; ++d) {
+      const floatx4 res = o[d][hb] * inv;
+      const int col = 256 * kh + 16 * d + 4 * g;
       if (!split_mode) {
-        *reinterpret_cast<u32x2*>(p.out + r * p.out_rs + int64_t(head) * p.out_hs + col) =
+        *reinterpret_cast<u32x2*>(p.out + r * p.out_rs + int64_t(h) * p.out_hs + col) =
             u32x2{pack_bf16(res[0], res[1]), pack_bf16(res[2], res[3])};
       } else {
         *reinterpret_cast<floatx4*>(
-            p.part_o + ((int64_t(split) * p.rows + r) * p.heads + head) * kDv + col) = res;
+            p.part_o + ((int64_t(split) * p.rows + r) * p.heads + h) * kDv + col) = res;
       }
     }
-    if (g == 0) {
-      const float lse = lt > 0.f ? (m_ref + __log2f(lt)) * kLn2 : kNegInf;
+    if (kh == 0 && g == 0) {
+      const float lse = lt[hb] > 0.f ? (m_ref[hb] + __log2f(lt[hb])) * kLn2 : kNegInf;
       if (!split_mode)
-        p.lse[r * p.lse_rs + int64_t(head) * p.lse_hs] = lse;
+        p.lse[r * p.lse_rs + int64_t(h) * p.lse_hs] = lse;
       else
-        p.part_lse[(int64_t(split) * p.rows + r) * p.heads + head] = lse;
+        p.part_lse[(int64_t(split) * p.rows + r) * p.heads + h] = lse;
     }
   }
 }
