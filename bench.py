@@ -32,7 +32,20 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
-KERNEL_SRC = os.path.join(ROOT, "sparse_mla_attention_05_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "sparse_mla_attention_05_amd", "csrc")
+
+
+def attention_kernel(plan, d_qk, fp8):
+    """(kernel name as rocprofv3 shows it, source file) of the attention
+    kernel a plan launches; mirrors the dispatch in csrc/kernels.hip."""
+    hb, v = plan["head_block"], plan["variant"]
+    if hb == 16 and fp8 and v == 0:
+        return f"smla::decode_kernel<{d_qk}>", "decode.hip"
+    if hb == 64 and v != 1:
+        if fp8 and v == 0:
+            return f"smla::prefill_fp8_kernel<{d_qk}>", "prefill_fp8.hip"
+        return f"smla::prefill_kernel<{d_qk}, {str(fp8).lower()}>", "prefill.hip"
+    return "smla::fwd_kernel (staged tile)", "kernels.hip"
 
 
 def parse():
@@ -81,21 +94,22 @@ def algorithmic(inp):
     return dict(kv_bytes=kv, bytes=kv + other, flops=flops, valid_slots=valid)
 
 
-def source_digest():
-    with open(KERNEL_SRC, "rb") as f:
+def source_digest(src):
+    with open(os.path.join(CSRC, src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(workload):
+def traffic_from_profiles(kernel_src, workload):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"fwd_kernel_{workload}_pmc.json")
+    was taken on the current source of the kernel; else None."""
+    stem = kernel_src.rsplit(".", 1)[0]
+    path = os.path.join(ROOT, "profiles", f"{stem}_kernel_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             d = json.load(f)
-        if d.get("kernel_source_sha256_16") != source_digest():
+        if d.get("kernel_source_sha256_16") != source_digest(kernel_src):
             return None
         return d.get("hbm_bytes_per_launch")
     except Exception:
@@ -152,7 +166,9 @@ def time_workload(name, steps, warmup, cold):
 
 
 def cpu_baseline(inp, target_s):
-    """Time the fp64 oracle as it stands on a bounded sample of rows."""
+    """Time the fp64 oracle as it stands on a bounded sample of rows (random
+    order, cycling through the rows again if one pass takes less than
+    target_s)."""
     import numpy as np
     import oracle
     try:
@@ -165,8 +181,9 @@ def cpu_baseline(inp, target_s):
     order = rng.permutation(R)
     done, t0 = 0, time.perf_counter()
     chunk = 8
-    while done < R and time.perf_counter() - t0 < target_s:
-        rows = np.sort(order[done:done + chunk])
+    while time.perf_counter() - t0 < target_s:
+        start = done % R
+        rows = np.sort(order[start:start + chunk])
         oracle.sparse_mla_fwd_torch(inp.q, inp.pool, inp.kv_scale, inp.indices, inp.sm_scale,
                                     rows=rows)
         done += len(rows)
@@ -175,8 +192,8 @@ def cpu_baseline(inp, target_s):
     us_per_call = el / done * R * 1e6
     return {"value": round(us_per_call, 1), "unit": "us/call", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} of {R} rows (random, seed 0) in {el:.1f} s, scaled by {R}/{done} "
-                      f"to one call; host has {os.cpu_count()} logical CPUs"}
+            "sample": f"{done} rows of {R} (random order, seed 0, cycling) in {el:.1f} s, "
+                      f"scaled by {R}/{done} to one call; host has {os.cpu_count()} logical CPUs"}
 
 
 def main():
@@ -202,6 +219,8 @@ def main():
     alg = head["alg"]
     # dominant kernel: the attention kernel (the whole call when splits == 1)
     kernel_us = us
+    w0 = head["inp"].workload
+    kname, ksrc = attention_kernel(head["plan"], w0.d_qk, w0.kv_dtype == "fp8")
     achieved = alg["bytes"] / (kernel_us * 1e-6) / 1e9
     w = head["inp"].workload
     line = {
@@ -233,9 +252,9 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles(w.name),
+            "traffic": traffic_from_profiles(ksrc, w.name),
             "bytes_per_launch": alg["bytes"],
-            "kernel": "smla::fwd_kernel (attention)",
+            "kernel": kname,
             "kernel_avg_us": round(kernel_us, 2),
         },
     }
@@ -244,8 +263,10 @@ def main():
         r = time_workload(name, max(3, args.steps // 2), 2, cold)
         pus = statistics.median(r["times"])
         tf = r["alg"]["flops"] / (pus * 1e-6) / 1e12
+        wp = r["inp"].workload
         prefill.append({"workload": name, "us_per_call": round(pus, 1), "tflops": round(tf, 1),
                         "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "kernel": attention_kernel(r["plan"], wp.d_qk, wp.kv_dtype == "fp8")[0],
                         "warm_us_per_call": round(r["warm_us"], 1), "plan": r["plan"],
                         "gathered_kv_tbs": round(r["alg"]["kv_bytes"] / (pus * 1e-6) / 1e12, 2)})
         del r

@@ -14,7 +14,7 @@
 //    (steps w, w+4, ...) with its own running max, row sum and O, like an
 //    independent split; the four are merged once at the end. No barrier
 //    inside the walk.
-//  * Gathers go straight into VGPRs, three steps in flight per wave. Lane
+//  * Gathers go straight into VGPRs, two steps in flight per wave. Lane
 //    (l16, g) loads 16-byte chunks 4i+g (i = 0..8) of the step's slot l16, so
 //    every load instruction reads 64 contiguous bytes of 16 rows. Those
 //    chunks are exactly the A operand of S^T = K Q^T on
