@@ -150,11 +150,20 @@ prefill_fp8_kernel(const FwdParams p) {
   const int gk = tid / C::TPR, gq = tid % C::TPR;
   const int32_t* idx_row = p.idx + r * p.idx_rs;
   const int last_slot = min(p.topk, t_end * TK) - 1;
-  auto load_idx = [&](int t) -> int {
-    const int j = t * TK + gk;
-    const int v = idx_row[min(j, last_slot)];
-    return v | -int(!(t < t_end && j <= last_slot));
+  // The index load and its validity mask are split so that a load can be
+  // issued a tile before it is used: applying the mask right after the load
+  // would make the wave wait for every gather issued before it.
+  // The row's indices up to last_slot through a buffer resource: a load past
+  // it reads 0, which the mask then marks invalid.
+  const __amdgpu_buffer_rsrc_t idx_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(idx_row), 0, 4 * (last_slot + 1), kXBufferWord3);
+  // The per-lane part of the slot number stays gk (tile offsets are uniform),
+  // so no per-lane counter is carried through the tile loop.
+  auto idx_raw = [&](int t) -> int {
+    return __builtin_amdgcn_raw_buffer_load_b32(idx_rsrc, uint32_t(4 * gk), 4 * t * TK, 0);
   };
+  auto idx_mask = [&](int t) -> int { return -int(!(t < t_end && gk <= last_slot - t * TK)); };
+  auto load_idx = [&](int t) -> int { return idx_raw(t) | idx_mask(t); };
   const __amdgpu_buffer_rsrc_t pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.pool), 0, p.pool_bytes, kXBufferWord3);
   u32x4 pre[LPT];
@@ -350,18 +359,22 @@ prefill_fp8_kernel(const FwdParams p) {
     for (int i = 0; i < LPT; ++i) stage_chunk(i, tile0);
     if (gq == 0) kbias[gk] = id_a >= 0 ? 0.f : kNegInf;
     int id_b = load_idx(t_begin + 1);
+    int raw_n = idx_raw(t_begin + 2);  // masked where it is used
     gather(id_b);
-    int id_n = load_idx(t_begin + 2);
     __syncthreads();
     // One tile: QK of tile t from `cur` with tile t+1 (zeros past the end:
     // harmless, never read) staged into `nxt`, the buffer tile t-1 used,
     // which every wave finished before the last barrier; softmax; P swap;
-    // PV.
+    // PV. The index of tile t+3 is loaded before the gathers of tile t+2, so
+    // waiting for it never waits for them.
     auto step = [&](int t, const uint8_t* cur, uint8_t* nxt, int buf) {
+      const int raw_f = idx_raw(t + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      const int id_n = raw_n | idx_mask(t + 2);
       qk_and_stage(cur, nxt, row_off(id_n));
       if (gq == 0) kbias[(buf ^ 1) * TK + gk] = id_b >= 0 ? 0.f : kNegInf;
       id_b = id_n;
-      id_n = load_idx(t + 3);
+      raw_n = raw_f;
       pv_prefetch(cur, 0);
       bf16x8 pown[2], ppart[2];
       softmax(buf, pown);
