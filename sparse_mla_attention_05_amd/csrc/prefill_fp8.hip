@@ -51,7 +51,7 @@ namespace {
 
 constexpr int kXWaves = 4;
 constexpr int kXTile = 64;
-constexpr float kXRefSlack = 64.0f;  // P <= 2^64 against the reference
+constexpr float kXSumLimit = 0x1p64f;  // bound on the weights against the reference
 constexpr uint32_t kXOutOfRange = 0xFFFFF000u;
 constexpr int kXBufferWord3 = 0x00020000;
 
@@ -74,7 +74,7 @@ struct XCfg {
   static constexpr int LDS_BYTES = 2 * TILE + 2 * TK * 4 + kXWaves * 2 * 64 * 16 + 64;
   static_assert(SRC_CH % TPR == 0, "staging split");
   static_assert(LPT % NSB == 0, "staging bases");
-  static_assert(LPT <= KSTEPS / 2, "staging spread over the k-steps");
+  static_assert(4 * LPT <= 2 * KSTEPS, "staging spread over the k-steps");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -213,100 +213,94 @@ prefill_fp8_kernel(const FwdParams p) {
 
   floatx4 o[NDW][2];
   float m_ref[2];    // reference max (log2 domain) of head 16hb + l16, shared by the pair
-  float m_run[2];    // running max of this lane's scores of that head
+  float nmu[2];      // -m_ref, or 0 when the split has no valid slot
   float l_part[2];   // this lane's share of the head's row sum over the wave's slots
-  bool ref_set;      // the references are set (uniform over the workgroup)
-  bool over;         // some score of this lane exceeded m_ref + kXRefSlack
 
-  // QK of this wave's 32 slots of the tile in `cur`, with the staging of the
-  // next tile from `pre` into `nxt` spread between the k-steps.
+  // Scores of this wave's 32 slots of a tile: S^T blocks j = 0 (slots
+  // 32kh..32kh+15) and j = 1 (the next 16), head blocks hb.
   floatx4 sacc[2][2];
-  auto qk_and_stage = [&](const uint8_t* cur, uint8_t* nxt, uint32_t next_off) {
+  // Softmax weights of slots 4g..4g+3 of block j = i / 4 (i % 4 within them)
+  // for head block hb, and the bf16 pairs of block 0.
+  float ew[2][8];
+  u32x2 p0[2];
+  // Weight of slot i of head block hb: 2^(s * score_scale + bias - m_ref);
+  // bias = 0 for a valid slot, -inf for an invalid one. Summed into l_part.
+  auto weight = [&](int hb, int i, const float (&bias)[8]) {
+    const float v = __builtin_fmaf(sacc[i / 4][hb][i % 4], score_scale, bias[i] + nmu[hb]);
+    ew[hb][i] = __builtin_amdgcn_exp2f(v);
+    l_part[hb] += ew[hb][i];
+    // Pure arithmetic would otherwise be sunk to its uses after the dots.
+    asm volatile("" : "+v"(ew[hb][i]), "+v"(l_part[hb]));
+  };
+  auto pack_block0 = [&]() {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+      p0[hb] = u32x2{pack2_bf16(ew[hb][0], ew[hb][1]), pack2_bf16(ew[hb][2], ew[hb][3])};
+    asm volatile("" : "+v"(p0[0]), "+v"(p0[1]));
+  };
+  // QK of this wave's 32 slots of the tile in `cur`, block j = 0 over all
+  // k-steps first, then j = 1, each K fragment feeding both head blocks.
+  // With `stage`, the next tile's chunks are widened from `pre` into `nxt`
+  // between the dots, one chunk per 4 k-steps (each chunk's registers then
+  // refilled with the gather of the tile after, which so gets a whole tile to
+  // land); with `soft`, the block-0 weights are computed between the dots of
+  // block 1.
+  constexpr int NU = 2 * KSTEPS;
+  constexpr int KRING = 4;  // K fragments read KRING-1 steps ahead of their dots
+  auto load_k = [&](const uint8_t* cur, int u) -> bf16x8 {
+    const int j = u / KSTEPS, s = u % KSTEPS;
+    return *reinterpret_cast<const bf16x8*>(cur + kbase[s % NQB] + 16 * SWB * (s / NQB) + 16 * ROW * j);
+  };
+  auto qk = [&](const uint8_t* cur, uint8_t* nxt, uint32_t next_off, bool stage, bool soft,
+                const float (&bias)[8]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) sacc[j][0] = sacc[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // K fragments in a ring of KRING k-steps: the reads run KRING-1 k-steps
-    // ahead of the dots that use them.
-    constexpr int KRING = 3;
-    bf16x8 ka[KRING][2];
-    auto load_k = [&](int s, bf16x8 (&dst)[2]) {
-      const uint8_t* kp = cur + kbase[s % NQB] + 16 * SWB * (s / NQB);
-      dst[0] = *reinterpret_cast<const bf16x8*>(kp);
-      dst[1] = *reinterpret_cast<const bf16x8*>(kp + 16 * ROW);
-    };
+    bf16x8 ka[KRING];
+    u32x2 wz[4];  // widened quarters of the chunk being staged
 #pragma unroll
-    for (int s = 0; s < KRING - 1; ++s) load_k(s, ka[s]);
+    for (int u = 0; u < KRING - 1; ++u) ka[u] = load_k(cur, u);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
+    for (int u = 0; u < NU; ++u) {
       // The fences keep the scheduler from sinking the reads to their uses.
-      if (s + KRING - 1 < KSTEPS) load_k(s + KRING - 1, ka[(s + KRING - 1) % KRING]);
+      if (u + KRING - 1 < NU) ka[(u + KRING - 1) % KRING] = load_k(cur, u + KRING - 1);
       __builtin_amdgcn_sched_barrier(0);
+      const int j = u / KSTEPS, s = u % KSTEPS;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          sacc[j][hb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s % KRING][j], qf[hb][s], sacc[j][hb], 0, 0, 0);
-      if (s % 2 == 1 && s / 2 < LPT) {
-        // Stage chunk s/2 of the next tile, then refill its registers with
-        // the tile after: each gather gets almost a whole tile to land.
-        stage_chunk(s / 2, nxt);
-        gather_one(s / 2, next_off);
+      for (int hb = 0; hb < 2; ++hb)
+        sacc[j][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u % KRING], qf[hb][s], sacc[j][hb], 0, 0, 0);
+      if (stage && u / 4 < LPT) {
+        // Chunk u/4 of the next tile is widened a quarter per k-step and
+        // written a half every other step (a burst of widenings or writes
+        // between two dots stalls them); its registers are then refilled
+        // with the gather of the tile after.
+        const int c = u / 4, ph = u % 4;
+        wz[ph] = widen_fp8x4(pre[c][ph]);
+        const int hi_off = 16 * SWB * (c / NSB);
+        if (ph == 1)
+          *reinterpret_cast<u32x4*>(nxt + sbase[0][c % NSB] + hi_off) = u32x4{wz[0].x, wz[0].y, wz[1].x, wz[1].y};
+        if (ph == 3) {
+          *reinterpret_cast<u32x4*>(nxt + sbase[1][c % NSB] + hi_off) = u32x4{wz[2].x, wz[2].y, wz[3].x, wz[3].y};
+          gather_one(c, next_off);
+        }
       }
+      // Block 0's last dots went out at u = KSTEPS - 1; one step later their
+      // results are in.
+      const int k = u - (KSTEPS + 1);
+      if (soft && k >= 0 && k < 8) weight(k / 4, k % 4, bias);
+      if (soft && k == 8) pack_block0();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Softmax weights of this wave's 32 slots of the tile in buffer `buf`;
-  // returns its P^T operands (k-slot order: slots 4g..4g+3 of the first 16,
-  // then of the second 16) for both head blocks.
-  auto softmax = [&](int buf, bf16x8 (&pown)[2]) {
-    const float* kb = kbias + buf * TK + 32 * kh + 4 * g;
-    const floatx4 b0 = *reinterpret_cast<const floatx4*>(kb);
-    const floatx4 b1 = *reinterpret_cast<const floatx4*>(kb + 16);
-    float v[2][8];
-    float mx[2];
+  // This lane's bias terms of the tile whose flags are kbias[kb..]: slots
+  // 32kh + 4g + i (i < 4) and 32kh + 16 + 4g + i - 4.
+  auto load_bias = [&](int kb, float (&bias)[8]) {
+    const floatx4 b0 = *reinterpret_cast<const floatx4*>(kbias + kb + 32 * kh + 4 * g);
+    const floatx4 b1 = *reinterpret_cast<const floatx4*>(kbias + kb + 32 * kh + 16 + 4 * g);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      mx[hb] = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[hb][i] = __builtin_fmaf(sacc[0][hb][i], score_scale, b0[i]);
-        v[hb][4 + i] = __builtin_fmaf(sacc[1][hb][i], score_scale, b1[i]);
-        mx[hb] = fmaxf(mx[hb], fmaxf(v[hb][i], v[hb][4 + i]));
-      }
-      m_run[hb] = fmaxf(m_run[hb], mx[hb]);
-    }
-    if (!ref_set) {
-      // Uniform over the workgroup: does this tile hold any valid slot?
-      if (__ballot(kbias[buf * TK + lane] == 0.f) != 0) {
-        // First tile with a valid slot: the pair agrees on the reference.
-        float* xf = reinterpret_cast<float*>(xch);
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          float t = fmaxf(mx[hb], __shfl_xor(mx[hb], 16));
-          t = fmaxf(t, __shfl_xor(t, 32));
-          xf[(wave * 2 + hb) * 64 + lane] = t;
-          mx[hb] = t;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) m_ref[hb] = fmaxf(mx[hb], xf[(partner * 2 + hb) * 64 + lane]);
-        __syncthreads();  // the exchange area is free again before the P swap
-        ref_set = true;
-      }
-    }
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      over = over || mx[hb] > m_ref[hb] + kXRefSlack;
-      const float mu = m_ref[hb] == kNegInf ? 0.f : m_ref[hb];
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(v[hb][i] - mu);
-        l_part[hb] += e[i];
-      }
-      pown[hb] = __builtin_bit_cast(bf16x8, u32x4{pack2_bf16(e[0], e[1]), pack2_bf16(e[2], e[3]),
-                                                  pack2_bf16(e[4], e[5]), pack2_bf16(e[6], e[7])});
+    for (int i = 0; i < 4; ++i) {
+      bias[i] = b0[i];
+      bias[4 + i] = b1[i];
     }
   };
   // V^T fragments of slot half x (0: the wave's own, 1: the partner's) for
@@ -341,25 +335,59 @@ prefill_fp8_kernel(const FwdParams p) {
     }
   };
 
-  // One walk over this split's tiles; `preset` says m_init holds the
-  // references already (second walk).
-  auto walk = [&](float m_init0, float m_init1, bool preset) {
+  float* const xf = reinterpret_cast<float*>(xch);
+  // Reference: per head, the max score (log2 domain, valid slots only) over
+  // tiles [t_from, t_to), agreed by the pair; -inf if there is none. Each
+  // tile is staged and scored on its own (no overlap): this runs over one
+  // tile per walk, and over all of them only before a second walk.
+  auto max_pass = [&](int t_from, int t_to) {
+    float mx[2] = {kNegInf, kNegInf};
+#pragma clang loop unroll(disable)
+    for (int t = t_from; t < t_to; ++t) {
+      const int id = load_idx(t);
+      gather(id);
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) stage_chunk(i, tile0);
+      if (gq == 0) kbias[gk] = id >= 0 ? 0.f : kNegInf;
+      __syncthreads();
+      float bias[8];
+      load_bias(0, bias);
+      qk(tile0, tile1, 0u, false, false, bias);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          mx[hb] = fmaxf(mx[hb], __builtin_fmaf(sacc[i / 4][hb][i % 4], score_scale, bias[i]));
+      __syncthreads();  // tile0 and the flags are free for the next tile
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float t = fmaxf(mx[hb], __shfl_xor(mx[hb], 16));
+      t = fmaxf(t, __shfl_xor(t, 32));
+      xf[(wave * 2 + hb) * 64 + lane] = t;
+      mx[hb] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) m_ref[hb] = fmaxf(mx[hb], xf[(partner * 2 + hb) * 64 + lane]);
+    __syncthreads();  // the exchange area is free again
+  };
+
+  // One walk over tiles [t0, t_end) with the references in m_ref.
+  auto walk = [&](int t0) {
 #pragma unroll
     for (int d = 0; d < NDW; ++d) o[d][0] = o[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-    m_ref[0] = m_init0;
-    m_ref[1] = m_init1;
-    m_run[0] = m_run[1] = kNegInf;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) nmu[hb] = m_ref[hb] == kNegInf ? 0.f : -m_ref[hb];
     l_part[0] = l_part[1] = 0.f;
-    ref_set = preset;
-    over = false;
-    if (t_begin >= t_end) return;
-    int id_a = load_idx(t_begin);
+    if (t0 >= t_end) return;
+    int id_a = load_idx(t0);
     gather(id_a);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) stage_chunk(i, tile0);
     if (gq == 0) kbias[gk] = id_a >= 0 ? 0.f : kNegInf;
-    int id_b = load_idx(t_begin + 1);
-    int raw_n = idx_raw(t_begin + 2);  // masked where it is used
+    int id_b = load_idx(t0 + 1);
+    int raw_n = idx_raw(t0 + 2);  // masked where it is used
     gather(id_b);
     __syncthreads();
     // One tile: QK of tile t from `cur` with tile t+1 (zeros past the end:
@@ -371,16 +399,24 @@ prefill_fp8_kernel(const FwdParams p) {
       const int raw_f = idx_raw(t + 3);
       __builtin_amdgcn_sched_barrier(0);
       const int id_n = raw_n | idx_mask(t + 2);
-      qk_and_stage(cur, nxt, row_off(id_n));
+      float bias[8];
+      load_bias(buf * TK, bias);
+      qk(cur, nxt, row_off(id_n), true, true, bias);
       if (gq == 0) kbias[(buf ^ 1) * TK + gk] = id_b >= 0 ? 0.f : kNegInf;
       id_b = id_n;
       raw_n = raw_f;
       pv_prefetch(cur, 0);
-      bf16x8 pown[2], ppart[2];
-      softmax(buf, pown);
+      // Block 1's weights; P^T operands in k-slot order: slots 4g..4g+3 of
+      // block 0, then of block 1.
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int k = 0; k < 8; ++k) weight(k / 4, 4 + k % 4, bias);
+      bf16x8 pown[2], ppart[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        pown[hb] = __builtin_bit_cast(
+            bf16x8, u32x4{p0[hb].x, p0[hb].y, pack2_bf16(ew[hb][4], ew[hb][5]), pack2_bf16(ew[hb][6], ew[hb][7])});
         xch[(wave * 2 + hb) * 64 + lane] = __builtin_bit_cast(u32x4, pown[hb]);
+      }
       // The wave's own half first: its P is in registers, and the work
       // covers the partner's softmax before the swap.
       pv_half(cur, 0, pown);
@@ -394,35 +430,33 @@ prefill_fp8_kernel(const FwdParams p) {
     };
     // Tiles go in pairs (static buffer roles); an odd count ends with one
     // tile past the end, all slots invalid, which adds exactly nothing.
-    for (int t = t_begin; t < t_end; t += 2) {
+    for (int t = t0; t < t_end; t += 2) {
       step(t, tile0, tile1, 0);
       step(t + 1, tile1, tile0, 1);
     }
   };
 
-  float* const xf = reinterpret_cast<float*>(xch);
-  // Walk once; if any lane of the workgroup went over the slack, walk again
-  // from the pair's row max (the loop body is emitted once).
-  float mi0 = kNegInf, mi1 = kNegInf;
-  bool preset = false;
+  // The first tile with a valid slot (uniform over the workgroup); tiles
+  // before it add nothing.
+  int t0 = t_begin;
+  while (t0 < t_end && __syncthreads_or(load_idx(t0) >= 0) == 0) ++t0;
+  // Walk once with the first valid tile's max as the reference. Every
+  // weight of a lane is at most its partial row sum, so if no lane's sum
+  // passed kXSumLimit no weight did, and the bf16 weights and fp32 sums
+  // stayed in range. Otherwise walk again from the exact max of the split
+  // (the loop body is emitted once).
 #pragma clang loop unroll(disable)
   for (int pass = 0; pass < 2; ++pass) {
-    walk(mi0, mi1, preset);
+    max_pass(t0, pass == 0 ? min(t0 + 1, t_end) : t_end);
+    walk(t0);
     if (pass == 1) break;
     if (tid == 0) redo[0] = 0u;
     __syncthreads();
+    const bool over = l_part[0] > kXSumLimit || l_part[1] > kXSumLimit;
     if (__ballot(over) != 0 && lane == 0) redo[0] = 1u;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const float t = fmaxf(m_run[hb], __shfl_xor(m_run[hb], 16));
-      xf[(wave * 2 + hb) * 64 + lane] = fmaxf(t, __shfl_xor(t, 32));
-    }
     __syncthreads();
     const bool again = redo[0] != 0u;
-    mi0 = fmaxf(xf[(wave * 2 + 0) * 64 + lane], xf[(partner * 2 + 0) * 64 + lane]);
-    mi1 = fmaxf(xf[(wave * 2 + 1) * 64 + lane], xf[(partner * 2 + 1) * 64 + lane]);
-    preset = true;
-    __syncthreads();  // every wave has read the flag before a walk reuses LDS
+    __syncthreads();  // every wave has read the flag before it is reset
     if (!again) break;
   }
 
