@@ -25,20 +25,23 @@
 //    XOR-permuted by a function of r chosen so that the K operand reads
 //    (ds_read_b128), the transposed V reads (ds_read_b64_tr_b16) and the
 //    staging writes (ds_write_b128) are all free of bank conflicts on gfx950.
-//  * Tile t+1 is widened and written into the other buffer between the QK
-//    dots of tile t; as each of a thread's chunks is written, its registers
-//    are refilled with the gather for tile t+2 (unconditional raw buffer
-//    loads: invalid slots read past the buffer range and get zeros), so each
-//    gather has about a whole tile to land. Two barriers per tile: P swap,
-//    buffer reuse.
-//  * Fixed reference: a head's reference max is the max of the first tile
-//    that has a valid slot (O is still zero then; the pair agrees on it
-//    through LDS), so O is never rescaled and stays in the MFMA
+//  * QK runs slot block 0 (16 slots) over all k-steps, then block 1. Tile
+//    t+1 is widened and written into the other buffer between the QK dots
+//    of tile t, a quarter chunk per k-step; as each of a thread's chunks is
+//    written, its registers are refilled with the gather for tile t+2
+//    (unconditional raw buffer loads: invalid slots read past the buffer
+//    range and get zeros), so each gather has a whole tile to land. Block
+//    0's softmax weights are computed between block 1's dots. Two barriers
+//    per tile: P swap, buffer reuse.
+//  * Fixed reference: a head's reference max is the max over the first tile
+//    that has a valid slot, from a scoring pre-pass over that tile (the pair
+//    agrees on it through LDS), so O is never rescaled and stays in the MFMA
 //    accumulators. P = exp2(s - ref) is exact in real arithmetic whatever the
-//    reference; the bf16 P and fp32 sums stay in range while every later
-//    score is below ref + 64 (log2 domain). If any head exceeds that, the
-//    workgroup walks its slots a second time with the exact row max,
-//    tracked during the first walk, as the reference.
+//    reference; the bf16 P and fp32 sums stay in range while every weight is
+//    at most 2^64. Every weight a lane adds is at most the lane's partial
+//    row sum, so if no partial sum passes 2^64 none did; otherwise the
+//    workgroup scores all its tiles for the exact row max and walks its
+//    slots a second time with that as the reference.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
