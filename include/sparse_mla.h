@@ -138,6 +138,46 @@ SMLA_API int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
                       const smla_tensor* indices, float sm_scale, smla_tensor* out, smla_tensor* lse,
                       void* stream, const smla_options* opt);
 
+/*
+ * sparse_mla_fwd2 - two-segment forward, after "[Triton/Gluon] GFX950 sparse
+ * mla optimizations" (aiter PR 6159), the commit notes on the per-tensor fp8
+ * two-loop route: a row attends, under one softmax, to the valid slots of its
+ * main indices (into kv_pool, scale kv_scale) and of its extra indices (into
+ * extra_pool, scale extra_kv_scale), e.g. top-k slots of a compressed cache
+ * plus a sliding window of a second cache. For row r and head h, with
+ * K1 = kv_scale * codes (or bf16 values) and K2 likewise for the extra pool:
+ *   s over { K1[i] : indices[r,j] = i >= 0 } and { K2[i] : extra_indices[r,j]
+ *   = i >= 0 }, out = softmax(sm_scale * q . k) V, lse = ln sum exp(...).
+ *
+ *  extra_pool      same dtype as kv_pool, [N2, W2] with W2 >= D_qk, same
+ *                  alignment rules; its own rows and row stride.
+ *  extra_kv_scale  fp32 [1] device pointer for an fp8 pool; NULL means the
+ *                  extra segment uses kv_scale. Must be NULL for bf16 pools.
+ *  extra_indices   int32 [R, K2], K2 in [1, 2^20]; negative = invalid slot.
+ *                  NULL makes this sparse_mla_fwd_ex.
+ *  opt             as for sparse_mla_fwd_ex; head_block, splits, remap and
+ *                  variant apply to each segment's launch. The workspace
+ *                  holds both segments' partials (sparse_mla_plan2 gives its
+ *                  size); without one the library's per-device buffer is used.
+ *
+ * Each segment's kernel writes normalised partials with its own scale, and
+ * the split-combine kernel merges them (exact in real arithmetic). Every
+ * other rule is sparse_mla_fwd's; out and lse must not alias any input.
+ */
+SMLA_API int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool,
+                    const smla_tensor* kv_scale, const smla_tensor* indices,
+                    const smla_tensor* extra_pool, const smla_tensor* extra_kv_scale,
+                    const smla_tensor* extra_indices, float sm_scale, smla_tensor* out,
+                    smla_tensor* lse, void* stream, const smla_options* opt);
+
+/* The launches sparse_mla_fwd2 would make: each segment's plan and the bytes
+ * of workspace for both segments' partials. Host-only; makes no HIP call. */
+SMLA_API int sparse_mla_plan2(const smla_tensor* q, const smla_tensor* kv_pool,
+                     const smla_tensor* indices, const smla_tensor* extra_pool,
+                     const smla_tensor* extra_indices, const smla_options* opt,
+                     int32_t num_cus, smla_plan* plan_main, smla_plan* plan_extra,
+                     int64_t* workspace_bytes);
+
 /* 1 if the shapes/dtypes/strides are covered by the kernels, else 0 (the
  * reason is left in sparse_mla_last_error). Host-only; makes no HIP call. */
 SMLA_API int sparse_mla_is_supported(const smla_tensor* q, const smla_tensor* kv_pool,

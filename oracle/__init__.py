@@ -11,5 +11,7 @@ from .sparse_mla_oracle import (  # noqa: F401
     lse_combine,
     softmax_weights,
     sparse_mla_fwd,
+    sparse_mla_fwd_2seg,
+    sparse_mla_fwd_2seg_torch,
     sparse_mla_fwd_torch,
 )

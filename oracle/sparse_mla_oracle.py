@@ -44,7 +44,12 @@ Parity pins (tests/test_oracle.py, all CPU): brute-force dense attention via
 torch's scaled_dot_product_attention in fp64 over the same gathered rows,
 softmax weights summing to 1, all-invalid rows, slot-permutation and
 compaction invariance, closed-form special cases, the e4m3fn table against
-torch's own float8 conversion, and the fp8 scale-folding identity.
+torch's own float8 conversion, and the fp8 scale-folding identity. The
+two-segment forward is pinned to the one-segment one: with equal scales it
+equals attention over the concatenated pools, with a power-of-two scale ratio
+it equals attention over one bf16 pool holding the rescaled codes exactly
+(scale folding), an all-invalid segment leaves the other segment's result,
+and brute force covers it directly.
 """
 
 from __future__ import annotations
@@ -185,6 +190,76 @@ def sparse_mla_fwd_torch(q, pool, kv_scale, indices, sm_scale, rows=None):
     else:
         raise ValueError(f"unsupported pool dtype {pool.dtype}")
     return sparse_mla_fwd(q_bits, raw, kv_dtype, s, indices.numpy(), sm_scale, rows=rows)
+
+
+# ------------------------------------------------------------ two segments ---
+
+def sparse_mla_fwd_2seg(q_bits: np.ndarray, pool_raw: np.ndarray, kv_dtype: str,
+                        kv_scale: float | None, indices: np.ndarray,
+                        extra_raw: np.ndarray, extra_scale: float | None,
+                        extra_indices: np.ndarray, sm_scale: float,
+                        rows: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Two-segment sparse MLA forward in fp64.
+
+    After "[Triton/Gluon] GFX950 sparse mla optimizations" (aiter PR 6159),
+    commit notes on the per-tensor fp8 two-loop route: a row attends under
+    one softmax to the valid slots of its main indices (into pool_raw, value =
+    code * kv_scale for fp8) and of its extra indices (into extra_raw, value =
+    code * extra_scale; the extra scale defaults to kv_scale). Written as the
+    plain definition: the gathered rows of both segments, each decoded with
+    its own scale, form one set of slots. Both pools have the same dtype.
+
+    Returns (out fp64 [len(rows), H, 512], lse fp64 [len(rows), H]).
+    """
+    q_bits = np.asarray(q_bits)
+    indices = np.asarray(indices)
+    extra_indices = np.asarray(extra_indices)
+    R, H, d_qk = q_bits.shape
+    if d_qk < D_V:
+        raise ValueError("D_qk must be at least 512")
+    if kv_dtype == "fp8" and extra_scale is None:
+        extra_scale = kv_scale
+    sm = float(np.float32(sm_scale))
+    sel = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(sel), H, D_V), dtype=np.float64)
+    lse = np.full((len(sel), H), -np.inf, dtype=np.float64)
+    for i, r in enumerate(sel):
+        parts = []
+        for raw, scale, idx in ((pool_raw, kv_scale, indices[r]),
+                                (extra_raw, extra_scale, extra_indices[r])):
+            valid = idx[idx >= 0].astype(np.int64)
+            if valid.size == 0:
+                continue
+            if valid.max() >= raw.shape[0]:
+                raise IndexError(f"row {r}: index {int(valid.max())} >= pool rows {raw.shape[0]}")
+            parts.append(decode_rows(raw, valid, d_qk, kv_dtype, scale))
+        if not parts:
+            continue
+        out[i], lse[i] = attend_row(bf16_bits_to_f64(q_bits[r]), np.concatenate(parts), sm)
+    return out, lse
+
+
+def sparse_mla_fwd_2seg_torch(q, pool, kv_scale, indices, extra_pool, extra_scale,
+                              extra_indices, sm_scale, rows=None):
+    """Wrapper of ``sparse_mla_fwd_2seg`` taking CPU torch tensors. Only views
+    raw bytes; all arithmetic is in ``sparse_mla_fwd_2seg``."""
+    import torch  # local: the oracle itself is numpy-only
+
+    q_bits = q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    if pool.dtype == torch.bfloat16:
+        kv_dtype = "bf16"
+        raw = pool.view(torch.int16).numpy().view(np.uint16)
+        xraw = extra_pool.view(torch.int16).numpy().view(np.uint16)
+        s1 = s2 = None
+    elif pool.dtype == torch.float8_e4m3fn:
+        kv_dtype = "fp8"
+        raw, xraw = pool.view(torch.uint8).numpy(), extra_pool.view(torch.uint8).numpy()
+        s1 = float(kv_scale.reshape(-1)[0])
+        s2 = None if extra_scale is None else float(extra_scale.reshape(-1)[0])
+    else:
+        raise ValueError(f"unsupported pool dtype {pool.dtype}")
+    return sparse_mla_fwd_2seg(q_bits, raw, kv_dtype, s1, indices.numpy(), xraw, s2,
+                               extra_indices.numpy(), sm_scale, rows=rows)
 
 
 # ----------------------------------------------------- split combination ---

@@ -9,10 +9,13 @@ synthetic input generators (inputs.py).
 from ._lib import (  # noqa: F401
     SparseMLAError,
     forward,
+    forward2,
     load,
     sparse_mla_fwd,
+    sparse_mla_fwd2,
     sparse_mla_fwd_ex,
     sparse_mla_is_supported,
     sparse_mla_plan,
+    sparse_mla_plan2,
     sparse_mla_work_of,
 )

@@ -21,8 +21,9 @@ STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTE
 UNKNOWN_DTYPE = 1000  # any dtype the library does not know (e.g. float8_e4m3fnuz)
 
 EXPORTED = (
-    "sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_is_supported", "sparse_mla_plan",
-    "sparse_mla_work_of", "sparse_mla_last_error", "sparse_mla_version",
+    "sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_fwd2", "sparse_mla_is_supported",
+    "sparse_mla_plan", "sparse_mla_plan2", "sparse_mla_work_of", "sparse_mla_last_error",
+    "sparse_mla_version",
 )
 
 
@@ -70,6 +71,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_fwd_ex.argtypes = [T, T, T, T, ctypes.c_float, T, T, ctypes.c_void_p,
                                       ctypes.POINTER(SmlaOptions)]
     lib.sparse_mla_fwd_ex.restype = ctypes.c_int
+    lib.sparse_mla_fwd2.argtypes = [T, T, T, T, T, T, T, ctypes.c_float, T, T, ctypes.c_void_p,
+                                    ctypes.POINTER(SmlaOptions)]
+    lib.sparse_mla_fwd2.restype = ctypes.c_int
+    lib.sparse_mla_plan2.argtypes = [T, T, T, T, T, ctypes.POINTER(SmlaOptions), ctypes.c_int32,
+                                     ctypes.POINTER(SmlaPlan), ctypes.POINTER(SmlaPlan),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.sparse_mla_plan2.restype = ctypes.c_int
     lib.sparse_mla_is_supported.argtypes = [T, T, T]
     lib.sparse_mla_is_supported.restype = ctypes.c_int
     lib.sparse_mla_plan.argtypes = [T, T, T, ctypes.POINTER(SmlaOptions), ctypes.c_int32,
@@ -175,6 +183,16 @@ def status_of_fwd(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None
                               float(sm_scale), _ptr(ds[4]), _ptr(ds[5]), stream)
 
 
+def status_of_fwd2(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices,
+                   sm_scale, out, lse, stream=None) -> int:
+    """Raw status of sparse_mla_fwd2 with no options (for tests of the error paths)."""
+    lib = load()
+    ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale,
+                                extra_indices, out, lse)]
+    return lib.sparse_mla_fwd2(*[_ptr(d) for d in ds[:7]], float(sm_scale), _ptr(ds[7]),
+                               _ptr(ds[8]), stream, None)
+
+
 def sparse_mla_is_supported(q, kv_pool, indices) -> bool:
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, indices)]
@@ -192,6 +210,34 @@ def sparse_mla_plan(q, kv_pool, indices, head_block=0, splits=0, remap=0, num_cu
     return {name: getattr(plan, name) for name, _ in SmlaPlan._fields_ if name != "reserved"}
 
 
+def sparse_mla_fwd2(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices,
+                    sm_scale, out, lse, stream=None, head_block=0, splits=0, remap=0,
+                    workspace=None, workspace_bytes=None, variant=0) -> None:
+    """Two-segment forward: one softmax over the valid slots of `indices` into
+    kv_pool (scale kv_scale) and of `extra_indices` into extra_pool (scale
+    extra_kv_scale, or kv_scale when None for fp8 pools)."""
+    lib = load()
+    ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale,
+                                extra_indices, out, lse)]
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant)
+    st = _stream_handle(stream, q, out)
+    _check(lib.sparse_mla_fwd2(*[_ptr(d) for d in ds[:7]], float(sm_scale), _ptr(ds[7]),
+                               _ptr(ds[8]), st, ctypes.byref(opt)))
+
+
+def sparse_mla_plan2(q, kv_pool, indices, extra_pool, extra_indices, head_block=0, splits=0,
+                     remap=0, num_cus=0, variant=0) -> tuple[dict, dict, int]:
+    """Plans of both segments of sparse_mla_fwd2 and its workspace bytes."""
+    lib = load()
+    ds = [describe(t) for t in (q, kv_pool, indices, extra_pool, extra_indices)]
+    opt = _options(head_block, splits, remap, variant=variant)
+    p1, p2, ws = SmlaPlan(), SmlaPlan(), ctypes.c_int64(0)
+    _check(lib.sparse_mla_plan2(*[_ptr(d) for d in ds], ctypes.byref(opt), int(num_cus),
+                                ctypes.byref(p1), ctypes.byref(p2), ctypes.byref(ws)))
+    as_dict = lambda pl: {n: getattr(pl, n) for n, _ in SmlaPlan._fields_ if n != "reserved"}
+    return as_dict(p1), as_dict(p2), int(ws.value)
+
+
 def sparse_mla_work_of(pid: int, grid: int, remap: int) -> int:
     return int(load().sparse_mla_work_of(pid, grid, remap))
 
@@ -206,4 +252,16 @@ def forward(q, kv_pool, kv_scale, indices, sm_scale, **options):
         sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, **options)
     else:
         sparse_mla_fwd(q, kv_pool, kv_scale, indices, sm_scale, out, lse)
+    return out, lse
+
+
+def forward2(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices, sm_scale,
+             **options):
+    """Allocate out/lse on q's device and run the two-segment forward."""
+    import torch
+    R, H = q.shape[0], q.shape[1]
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((R, H), dtype=torch.float32, device=q.device)
+    sparse_mla_fwd2(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices,
+                    sm_scale, out, lse, **options)
     return out, lse

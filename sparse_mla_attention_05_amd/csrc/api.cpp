@@ -236,6 +236,107 @@ int device_cus(int dev) {
   return g_cu_count[dev];
 }
 
+// Kernel parameters of one segment: q/out/lse of the call, pool/scale/indices
+// of the segment, its plan's launch shape.
+FwdParams segment_params(const smla_tensor* q, const smla_tensor* pool, const float* scale,
+                         const smla_tensor* idx, const Checked& c, const smla_plan& plan,
+                         float sm_scale, smla_tensor* out, smla_tensor* lse) {
+  FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.q_rs = q->stride[0];
+  p.q_hs = q->stride[1];
+  p.pool = static_cast<const uint8_t*>(pool->data);
+  p.pool_rs_bytes = pool->stride[0] * elem_size(pool->dtype);
+  p.pool_bytes = uint32_t(std::min<int64_t>(c.pb.pool_bytes, kMaxBufferBytes));
+  p.kv_scale = c.fp8 ? scale : nullptr;
+  p.idx = static_cast<const int32_t*>(idx->data);
+  p.idx_rs = idx->stride[0];
+  p.out = static_cast<uint16_t*>(out->data);
+  p.out_rs = out->stride[0];
+  p.out_hs = out->stride[1];
+  p.lse = static_cast<float*>(lse->data);
+  p.lse_rs = lse->stride[0];
+  p.lse_hs = lse->stride[1];
+  p.rows = c.pb.rows;
+  p.heads = c.pb.heads;
+  p.topk = c.pb.topk;
+  p.splits = plan.splits;
+  p.tiles_per_split = plan.tiles_per_split;
+  p.head_blocks = plan.head_blocks;
+  p.remap = plan.remap;
+  p.grid = plan.grid;
+  p.sm_log2 = sm_scale * 1.4426950408889634f;
+  return p;
+}
+
+// Bytes of split partials for `splits` partial results of R x H rows: the
+// fp32 outputs, then (256-byte aligned) the fp32 LSEs.
+int64_t partial_bytes(int64_t splits, int64_t rows, int64_t heads, int64_t* lse_offset) {
+  const int64_t o_bytes = splits * rows * heads * kDv * 4;
+  const int64_t off = (o_bytes + 255) / 256 * 256;
+  if (lse_offset) *lse_offset = off;
+  return off + splits * rows * heads * 4;
+}
+
+// The caller's workspace when given (checked), else the device's own.
+int get_workspace(int dev, const smla_options* opt, int64_t need, void** ws) {
+  if (opt && opt->workspace) {
+    if (opt->workspace_bytes < need)
+      return fail(SMLA_ERR_INVALID_ARG,
+                  "workspace smaller than the plan needs (" + std::to_string(need) + " bytes)");
+    if (!aligned16(opt->workspace)) return fail(SMLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    *ws = opt->workspace;
+    return SMLA_OK;
+  }
+  return device_workspace(dev, need, ws);
+}
+
+// Validation of the extra segment of a two-segment call: same q, same pool
+// dtype; for fp8 its own scale or, when none is given, the main one.
+int validate_extra(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
+                   const smla_tensor* extra_pool, const smla_tensor* extra_scale,
+                   const smla_tensor* extra_idx, const smla_tensor* out, const smla_tensor* lse,
+                   Checked* c2, const float** scale2) {
+  int s;
+  if ((s = validate_inputs(q, extra_pool, extra_idx, c2)))
+    return fail(s, "extra segment: " + g_last_error);
+  if (extra_pool->dtype != kv_pool->dtype)
+    return fail(SMLA_ERR_UNSUPPORTED, "extra_pool: dtype must match kv_pool");
+  *scale2 = nullptr;
+  if (c2->fp8) {
+    if (extra_scale && extra_scale->data) {
+      if ((s = check_tensor(extra_scale, "extra_kv_scale", 1, SMLA_FP32))) return s;
+      if (extra_scale->shape[0] < 1) return fail(SMLA_ERR_INVALID_ARG, "extra_kv_scale: empty");
+      *scale2 = static_cast<const float*>(extra_scale->data);
+    } else {
+      *scale2 = static_cast<const float*>(kv_scale->data);
+    }
+  } else if (extra_scale && extra_scale->data) {
+    return fail(SMLA_ERR_INVALID_ARG, "extra_kv_scale: must be NULL for a bf16 pool");
+  }
+  if (c2->pb.rows > 0) {
+    const smla_tensor* ins[3] = {extra_pool, extra_idx,
+                                 (c2->fp8 && extra_scale && extra_scale->data) ? extra_scale : nullptr};
+    for (const smla_tensor* in : ins) {
+      if (!in) continue;
+      if (overlap(out, in) || overlap(lse, in))
+        return fail(SMLA_ERR_INVALID_ARG, "out/lse must not alias an input");
+    }
+  }
+  return SMLA_OK;
+}
+
+// Plans of both segments of a two-segment call and their workspace.
+int plan_two(const Checked& c1, const Checked& c2, const smla_options* opt, int num_cus,
+             smla_plan* p1, smla_plan* p2, int64_t* ws_bytes) {
+  const char* perr = nullptr;
+  int s;
+  if ((s = make_plan(c1.pb, opt, num_cus, p1, &perr))) return fail(s, perr);
+  if ((s = make_plan(c2.pb, opt, num_cus, p2, &perr))) return fail(s, perr);
+  *ws_bytes = partial_bytes(int64_t(p1->splits) + p2->splits, c1.pb.rows, c1.pb.heads, nullptr);
+  return SMLA_OK;
+}
+
 }  // namespace
 }  // namespace smla
 
@@ -259,53 +360,88 @@ int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
   const char* perr = nullptr;
   if ((s = make_plan(c.pb, opt, device_cus(dev), &plan, &perr))) return fail(s, perr);
 
-  FwdParams p{};
-  p.q = static_cast<const uint16_t*>(q->data);
-  p.q_rs = q->stride[0];
-  p.q_hs = q->stride[1];
-  p.pool = static_cast<const uint8_t*>(kv_pool->data);
-  p.pool_rs_bytes = kv_pool->stride[0] * elem_size(kv_pool->dtype);
-  p.pool_bytes = uint32_t(std::min<int64_t>(c.pb.pool_bytes, kMaxBufferBytes));
-  p.kv_scale = c.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr;
-  p.idx = static_cast<const int32_t*>(indices->data);
-  p.idx_rs = indices->stride[0];
-  p.out = static_cast<uint16_t*>(out->data);
-  p.out_rs = out->stride[0];
-  p.out_hs = out->stride[1];
-  p.lse = static_cast<float*>(lse->data);
-  p.lse_rs = lse->stride[0];
-  p.lse_hs = lse->stride[1];
-  p.rows = c.pb.rows;
-  p.heads = c.pb.heads;
-  p.topk = c.pb.topk;
-  p.splits = plan.splits;
-  p.tiles_per_split = plan.tiles_per_split;
-  p.head_blocks = plan.head_blocks;
-  p.remap = plan.remap;
-  p.grid = plan.grid;
-  p.sm_log2 = sm_scale * 1.4426950408889634f;
-
+  FwdParams p = segment_params(q, kv_pool, c.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
+                               indices, c, plan, sm_scale, out, lse);
   if (plan.splits > 1) {
     void* ws = nullptr;
-    if (opt && opt->workspace) {
-      if (opt->workspace_bytes < plan.workspace_bytes)
-        return fail(SMLA_ERR_INVALID_ARG, "workspace smaller than the plan needs (" +
-                                              std::to_string(plan.workspace_bytes) + " bytes)");
-      if (!aligned16(opt->workspace))
-        return fail(SMLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-      ws = opt->workspace;
-    } else if ((s = device_workspace(dev, plan.workspace_bytes, &ws))) {
-      return s;
-    }
-    const int64_t o_bytes = int64_t(plan.splits) * c.pb.rows * c.pb.heads * kDv * 4;
+    int64_t lse_off = 0;
+    const int64_t need = partial_bytes(plan.splits, c.pb.rows, c.pb.heads, &lse_off);
+    if ((s = get_workspace(dev, opt, std::max(need, plan.workspace_bytes), &ws))) return s;
     p.part_o = static_cast<float*>(ws);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + (o_bytes + 255) / 256 * 256);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_off);
   }
   const int le = launch_forward(p, plan, c.pb.dqk, c.fp8, stream);
   if (le != 0)
     return fail(SMLA_ERR_HIP, std::string("kernel launch: ") +
                                   hipGetErrorString(static_cast<hipError_t>(le)));
   return SMLA_OK;
+}
+
+int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
+                    const smla_tensor* indices, const smla_tensor* extra_pool,
+                    const smla_tensor* extra_kv_scale, const smla_tensor* extra_indices,
+                    float sm_scale, smla_tensor* out, smla_tensor* lse, void* stream,
+                    const smla_options* opt) {
+  if (!extra_indices)
+    return sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream, opt);
+  Checked c1, c2;
+  int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c1);
+  if (s) return s;
+  const float* scale2 = nullptr;
+  if ((s = validate_extra(q, kv_pool, kv_scale, extra_pool, extra_kv_scale, extra_indices, out, lse,
+                          &c2, &scale2)))
+    return s;
+  if (c1.pb.rows == 0) return SMLA_OK;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  smla_plan plan1, plan2;
+  int64_t need = 0;
+  if ((s = plan_two(c1, c2, opt, device_cus(dev), &plan1, &plan2, &need))) return s;
+  void* ws = nullptr;
+  if ((s = get_workspace(dev, opt, need, &ws))) return s;
+  const int64_t S = int64_t(plan1.splits) + plan2.splits;
+  int64_t lse_off = 0;
+  partial_bytes(S, c1.pb.rows, c1.pb.heads, &lse_off);
+  float* part_o = static_cast<float*>(ws);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_off);
+  const int64_t per_split = c1.pb.rows * c1.pb.heads;
+
+  // Each segment writes its normalised partials with its own scale folded in;
+  // the combine kernel's LSE-weighted merge is then the softmax over the
+  // union of both segments' slots.
+  FwdParams p1 = segment_params(q, kv_pool, c1.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
+                                indices, c1, plan1, sm_scale, out, lse);
+  p1.part_o = part_o;
+  p1.part_lse = part_lse;
+  FwdParams p2 = segment_params(q, extra_pool, scale2, extra_indices, c2, plan2, sm_scale, out, lse);
+  p2.part_o = part_o + int64_t(plan1.splits) * per_split * kDv;
+  p2.part_lse = part_lse + int64_t(plan1.splits) * per_split;
+  FwdParams pc = p1;
+  pc.splits = int32_t(S);
+  int le = launch_attention(p1, plan1, c1.pb.dqk, c1.fp8, stream);
+  if (le == 0) le = launch_attention(p2, plan2, c2.pb.dqk, c2.fp8, stream);
+  if (le == 0) le = launch_combine(pc, stream);
+  if (le != 0)
+    return fail(SMLA_ERR_HIP, std::string("kernel launch: ") +
+                                  hipGetErrorString(static_cast<hipError_t>(le)));
+  return SMLA_OK;
+}
+
+int sparse_mla_plan2(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* indices,
+                     const smla_tensor* extra_pool, const smla_tensor* extra_indices,
+                     const smla_options* opt, int32_t num_cus, smla_plan* plan_main,
+                     smla_plan* plan_extra, int64_t* workspace_bytes) {
+  if (!plan_main || !plan_extra || !workspace_bytes)
+    return fail(SMLA_ERR_INVALID_ARG, "plan2: null output");
+  Checked c1, c2;
+  int s = validate_inputs(q, kv_pool, indices, &c1);
+  if (s) return s;
+  if ((s = validate_inputs(q, extra_pool, extra_indices, &c2))) return s;
+  if (extra_pool->dtype != kv_pool->dtype)
+    return fail(SMLA_ERR_UNSUPPORTED, "extra_pool: dtype must match kv_pool");
+  return plan_two(c1, c2, opt, num_cus, plan_main, plan_extra, workspace_bytes);
 }
 
 int sparse_mla_fwd(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,

@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
 
   // 16 heads x 64 chunks of 8 columns; thread t takes chunk t % 64 of heads
   // t / 64 + 4k, so consecutive threads store consecutive 16-byte pieces.
-  const bool split_mode = p.splits > 1;
+  const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
   const float* parts = reinterpret_cast<const float*>(smem);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

@@ -35,9 +35,10 @@
 //    all HB heads and runs O += P V on 16x16x32 MFMAs, V being the first 512
 //    columns of the same staged tile (no second gather).
 //  * Epilogue: O / l (times the fp8 scale) rounded to bf16 and LSE = ln 2 *
-//    (m + log2 l); a head with no valid slot gets O = 0 and LSE = -inf. With
-//    splits > 1 the normalised fp32 O and the LSE go to a workspace and the
-//    combine kernel merges them.
+//    (m + log2 l); a head with no valid slot gets O = 0 and LSE = -inf. Given
+//    a workspace (splits > 1, or a segment of a two-segment call), the
+//    normalised fp32 O and the LSE go there and the combine kernel merges
+//    them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -315,7 +316,7 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   if (kg == 0 && g == 0) mfin_s[hg * 16 + l16] = m_run;
   __syncthreads();
 
-  const bool split_mode = p.splits > 1;
+  const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
 #pragma unroll
   for (int a = 0; a < NHG; ++a) {
 #pragma unroll
@@ -463,7 +464,7 @@ KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant) {
   }
 }
 
-int launch_forward(const FwdParams& p, const smla_plan& plan, int dqk, bool fp8, void* stream) {
+int launch_attention(const FwdParams& p, const smla_plan& plan, int dqk, bool fp8, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dqk == 576)
@@ -472,12 +473,19 @@ int launch_forward(const FwdParams& p, const smla_plan& plan, int dqk, bool fp8,
   else
     e = fp8 ? launch_by_head_block<512, true>(plan.head_block, plan.variant, p, st)
             : launch_by_head_block<512, false>(plan.head_block, plan.variant, p, st);
-  if (e != hipSuccess) return int(e);
-  if (plan.splits > 1) {
-    hipLaunchKernelGGL(combine_kernel, dim3(uint32_t(p.rows * p.heads)), dim3(128), 0, st, p);
-    e = hipGetLastError();
-  }
   return int(e);
+}
+
+int launch_combine(const FwdParams& p, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(combine_kernel, dim3(uint32_t(p.rows * p.heads)), dim3(128), 0, st, p);
+  return int(hipGetLastError());
+}
+
+int launch_forward(const FwdParams& p, const smla_plan& plan, int dqk, bool fp8, void* stream) {
+  const int e = launch_attention(p, plan, dqk, fp8, stream);
+  if (e != 0 || plan.splits <= 1) return e;
+  return launch_combine(p, stream);
 }
 
 }  // namespace smla

@@ -28,7 +28,7 @@ struct FwdParams {
   int64_t out_rs, out_hs;
   float* lse;               // fp32 [R, H]
   int64_t lse_rs, lse_hs;
-  float* part_o;            // fp32 [S, R, H, 512] when splits > 1
+  float* part_o;            // fp32 [S, R, H, 512]; non-null: write split partials
   float* part_lse;          // fp32 [S, R, H]
   int64_t rows;
   int32_t heads;
@@ -91,5 +91,11 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
 // Launches the attention kernel (and the combine kernel when splits > 1) on
 // `stream`. Returns 0 or a hipError_t value.
 int launch_forward(const FwdParams& p, const smla_plan& plan, int dqk, bool fp8, void* stream);
+
+// The two halves of launch_forward: the attention kernel alone (it writes
+// partials iff p.part_o is set), and the combine kernel over p.splits
+// partials.
+int launch_attention(const FwdParams& p, const smla_plan& plan, int dqk, bool fp8, void* stream);
+int launch_combine(const FwdParams& p, void* stream);
 
 }  // namespace smla

@@ -313,7 +313,7 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   if (g == 0) red[kg * HB + hg * 16 + l16] = l_head;
   if (kg == 0 && g == 0) mfin_s[hg * 16 + l16] = m_ref;
   __syncthreads();
-  const bool split_mode = p.splits > 1;
+  const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
 #pragma unroll
   for (int a = 0; a < NHG; ++a) {
 #pragma unroll

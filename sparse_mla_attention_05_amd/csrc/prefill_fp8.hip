@@ -475,7 +475,7 @@ prefill_fp8_kernel(const FwdParams p) {
   __syncthreads();
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) lt[hb] += xf[(partner * 2 + hb) * 64 + lane];
-  const bool split_mode = p.splits > 1;
+  const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int h = h0 + 16 * hb + l16;

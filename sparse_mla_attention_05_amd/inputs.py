@@ -224,6 +224,62 @@ def make_inputs(w: Workload | str, rows: int | None = None) -> Inputs:
     return Inputs(q=q, pool=pool, kv_scale=kv_scale, indices=idx, sm_scale=w.scale, workload=w)
 
 
+@dataclass
+class ExtraSegment:
+    """The second segment of a two-segment call: its own pool (same dtype as
+    the main one), its own fp8 scale (None for bf16) and its indices."""
+    pool: torch.Tensor
+    kv_scale: torch.Tensor | None
+    indices: torch.Tensor  # int32 [R, window]
+
+
+def window_ends(w: Workload) -> torch.Tensor:
+    """Position of each query row in its own context, as the index modes
+    place it: "request" rows are the last rows_per_request positions of their
+    request's context slice, "causal" rows sit at first_pos + r, "uniform"
+    rows at the end of the pool."""
+    r = torch.arange(w.rows, dtype=torch.int64)
+    if w.index_mode == "request":
+        b = r // w.rows_per_request
+        return b * w.ctx_per_request + (w.ctx_per_request - w.rows_per_request) + r % w.rows_per_request
+    if w.index_mode == "causal":
+        return w.first_pos + r
+    return torch.full((w.rows,), w.pool_rows - 1, dtype=torch.int64)
+
+
+def make_extra_segment(inp: Inputs, window: int, seed: int, value_std: float = 1.0,
+                       invalid_per_row: int = 0, rows: int | None = None) -> ExtraSegment:
+    """A sliding-window segment for ``inp``: an extra pool of the same shape
+    and dtype as inp.pool, drawn N(0, value_std^2) (fp8: quantised with its
+    own per-tensor scale), and for each query row the ``window`` consecutive
+    pool rows ending at the row's position (window_ends). Positions before a
+    request's context start (or below 0) are -1; ``invalid_per_row`` more
+    slots per row are set to -1 at random. Seeded on its own generator."""
+    w = inp.workload
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn((w.pool_rows, w.d_qk), generator=gen, dtype=torch.float32) * value_std
+    if w.kv_dtype == "bf16":
+        vals, scale = x.to(torch.bfloat16), None
+    else:
+        vals, scale = quantize_fp8(x)
+    del x
+    if w.pitch != w.d_qk:
+        pool = torch.zeros((w.pool_rows, w.pitch), dtype=vals.dtype)
+        pool[:, : w.d_qk] = vals
+    else:
+        pool = vals
+    end = window_ends(w)
+    if w.index_mode == "request":
+        start = (torch.arange(w.rows, dtype=torch.int64) // w.rows_per_request) * w.ctx_per_request
+    else:
+        start = torch.zeros(w.rows, dtype=torch.int64)
+    pos = end[:, None] - torch.arange(window - 1, -1, -1, dtype=torch.int64)[None, :]
+    idx = torch.where(pos >= start[:, None], pos, torch.full_like(pos, -1)).to(torch.int32)
+    idx = set_invalid(idx, invalid_per_row, gen)
+    n = inp.q.shape[0] if rows is None else rows
+    return ExtraSegment(pool=pool, kv_scale=scale, indices=idx[:n].contiguous())
+
+
 def custom_workload(name: str = "custom", **kw) -> Workload:
     """A Workload with the given fields (for tests of edge shapes)."""
     base = dict(name=name, rows=4, heads=16, d_qk=576, pool_rows=4096, topk=128,

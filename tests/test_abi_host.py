@@ -162,3 +162,63 @@ def test_xcd_work_order_is_contiguous_bijection(grid):
         assert mine == list(range(mine[0], mine[0] + len(mine))) if mine else True
     assert [_lib.sparse_mla_work_of(pid, grid, 0) for pid in range(grid)] == list(range(grid))
     assert _lib.sparse_mla_work_of(grid, grid, 1) == -1
+
+
+# ------------------------------------------------------------ two segments
+
+def _args2(pool_dtype=torch.float8_e4m3fn, K2=32, D=576, N2=128):
+    a = _args(pool_dtype=pool_dtype, D=D)
+    a["extra_pool"] = torch.zeros(N2, D, dtype=pool_dtype)
+    a["extra_kv_scale"] = torch.ones(1) if pool_dtype == torch.float8_e4m3fn else None
+    a["extra_indices"] = torch.zeros(a["q"].shape[0], K2, dtype=torch.int32)
+    return a
+
+
+def _status2(a):
+    return _lib.status_of_fwd2(a["q"], a["kv_pool"], a["kv_scale"], a["indices"], a["extra_pool"],
+                               a["extra_kv_scale"], a["extra_indices"], a["sm_scale"], a["out"],
+                               a["lse"])
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: a.update(extra_pool=torch.zeros(128, 576, dtype=torch.bfloat16)), UNSUP),  # dtype mismatch
+    (lambda a: a.update(extra_pool=torch.zeros(128, 500, dtype=torch.float8_e4m3fn)), INVALID),  # too narrow
+    (lambda a: a.update(extra_indices=torch.zeros(5, 32, dtype=torch.int32)), INVALID),  # rows
+    (lambda a: a.update(extra_indices=torch.zeros(4, 32, dtype=torch.int64)), UNSUP),  # dtype
+    (lambda a: a.update(extra_kv_scale=torch.ones(1, dtype=torch.float64)), UNSUP),
+])
+def test_two_segment_validation(mutate, expected):
+    a = _args2()
+    mutate(a)
+    assert _status2(a) == expected, _lib.last_error()
+
+
+def test_two_segment_bf16_rejects_extra_scale():
+    a = _args2(pool_dtype=torch.bfloat16)
+    a["extra_kv_scale"] = torch.ones(1)
+    assert _status2(a) == INVALID
+
+
+def test_two_segment_fp8_extra_scale_defaults_to_main():
+    a = _args2()
+    a["extra_kv_scale"] = None
+    for k in ("q", "indices", "extra_indices", "out", "lse"):
+        a[k] = a[k][:0]
+    assert _status2(a) == 0
+
+
+@pytest.mark.parametrize("H,K1,K2,dtype", [(16, 512, 128, torch.float8_e4m3fn),
+                                            (64, 512, 128, torch.bfloat16),
+                                            (64, 2048, 128, torch.float8_e4m3fn)])
+def test_plan2_workspace_covers_both_segments(H, K1, K2, dtype):
+    R = 192
+    q = torch.zeros(R, H, 576, dtype=torch.bfloat16)
+    pool = torch.zeros(1024, 576, dtype=dtype)
+    i1 = torch.zeros(R, K1, dtype=torch.int32)
+    i2 = torch.zeros(R, K2, dtype=torch.int32)
+    p1, p2, ws = _lib.sparse_mla_plan2(q, pool, i1, pool, i2)
+    assert p1 == _lib.sparse_mla_plan(q, pool, i1)
+    assert p2 == _lib.sparse_mla_plan(q, pool, i2)
+    S = p1["splits"] + p2["splits"]
+    o_bytes = S * R * H * 512 * 4
+    assert ws == (o_bytes + 255) // 256 * 256 + S * R * H * 4

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from oracle import sparse_mla_oracle as orc
-from sparse_mla_attention_05_amd.inputs import custom_workload, make_inputs
+from sparse_mla_attention_05_amd.inputs import custom_workload, make_extra_segment, make_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_form_cases.json")
 
@@ -294,6 +294,111 @@ def test_padded_pitch_pool_same_result():
     inp2.pool = inp.pool[:, :576].contiguous()
     out2, lse2 = _run(inp2)
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+# --------------------------------------------------------- two segments
+
+def _two_seg(kv_dtype="fp8", d_qk=576, window=40, invalid=3, extra_invalid=2, std=1.7, seed=21):
+    inp = _small(kv_dtype, d_qk, invalid=invalid, seed=seed)
+    w = inp.workload
+    inp.workload = custom_workload(**{**w.__dict__, "index_mode": "uniform"})
+    ex = make_extra_segment(inp, window, seed=seed + 1, value_std=std, invalid_per_row=extra_invalid)
+    return inp, ex
+
+
+def _run2(inp, ex, extra_scale="own"):
+    es = ex.kv_scale if extra_scale == "own" else extra_scale
+    return oracle.sparse_mla_fwd_2seg_torch(inp.q, inp.pool, inp.kv_scale, inp.indices, ex.pool, es,
+                                            ex.indices, inp.sm_scale)
+
+
+def _concat(inp, ex, pool):
+    """One-segment inputs over [main pool; extra pool] with the extra indices
+    shifted past the main pool (invalid slots stay -1)."""
+    n1 = inp.pool.shape[0]
+    shifted = torch.where(ex.indices >= 0, ex.indices + n1, ex.indices)
+    c = make_inputs(custom_workload(rows=1))
+    c.q, c.sm_scale = inp.q, inp.sm_scale
+    c.indices = torch.cat([inp.indices, shifted], dim=1).contiguous()
+    c.pool = pool
+    return c
+
+
+def test_two_segment_equal_scales_is_one_concatenated_pool():
+    """Extra scale left out (it defaults to kv_scale): the same as attention
+    over the concatenated fp8 pools with all slots in one index row."""
+    inp, ex = _two_seg("fp8")
+    out2, lse2 = _run2(inp, ex, extra_scale=None)
+    c = _concat(inp, ex, torch.cat([inp.pool, ex.pool]))
+    c.kv_scale = inp.kv_scale
+    out1, lse1 = _run(c)
+    assert np.max(np.abs(out2 - out1)) < 1e-15 and np.max(np.abs(lse2 - lse1)) < 1e-13
+
+
+@pytest.mark.parametrize("d_qk", [576, 512])
+def test_two_segment_scale_folding(d_qk):
+    """Scales 2^-6 (main) and 2^-4 (extra), sm = 2^-4: the two-segment result
+    is 2^-6 times one-segment attention over one bf16 pool holding the main
+    codes and 4x the extra codes (all exact in bf16), with sm * 2^-6."""
+    inp, ex = _two_seg("fp8", d_qk=d_qk)
+    inp.kv_scale = torch.tensor([2.0 ** -6], dtype=torch.float32)
+    ex.kv_scale = torch.tensor([2.0 ** -4], dtype=torch.float32)
+    inp.sm_scale = 2.0 ** -4
+    out2, lse2 = _run2(inp, ex)
+    main = inp.pool.to(torch.float32)
+    extra = ex.pool.to(torch.float32) * 4
+    pool = torch.cat([main, extra]).to(torch.bfloat16)
+    assert torch.equal(pool.to(torch.float32), torch.cat([main, extra]))
+    c = _concat(inp, ex, pool)
+    c.kv_scale = None
+    c.sm_scale = 2.0 ** -10
+    out1, lse1 = _run(c)
+    assert np.max(np.abs(out2 - 2.0 ** -6 * out1)) < 1e-15
+    assert np.max(np.abs(lse2 - lse1)) < 1e-13
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_two_segment_empty_segment_leaves_the_other(kv_dtype):
+    inp, ex = _two_seg(kv_dtype)
+    main_out, main_lse = _run(inp)
+    none = torch.full_like(ex.indices, -1)
+    ex_empty = type(ex)(pool=ex.pool, kv_scale=ex.kv_scale, indices=none)
+    out, lse = _run2(inp, ex_empty)
+    assert np.array_equal(out, main_out) and np.array_equal(lse, main_lse)
+    only = make_inputs(custom_workload(rows=1))
+    only.q, only.pool, only.kv_scale, only.indices, only.sm_scale = (
+        inp.q, ex.pool, ex.kv_scale, ex.indices, inp.sm_scale)
+    ex_out, ex_lse = _run(only)
+    inp_empty = make_inputs(custom_workload(rows=1))
+    inp_empty.q, inp_empty.pool, inp_empty.kv_scale, inp_empty.sm_scale = inp.q, inp.pool, inp.kv_scale, inp.sm_scale
+    inp_empty.indices = torch.full_like(inp.indices, -1)
+    out, lse = _run2(inp_empty, ex)
+    assert np.array_equal(out, ex_out) and np.array_equal(lse, ex_lse)
+    both = type(ex)(pool=ex.pool, kv_scale=ex.kv_scale, indices=none)
+    out, lse = _run2(inp_empty, both)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+def test_two_segment_matches_dense_sdpa():
+    """Brute force with torch's own conversions over the union of both
+    segments' gathered rows, each pool scaled by its own factor."""
+    inp, ex = _two_seg("fp8", std=0.6)
+    out2, lse2 = _run2(inp, ex)
+    sm = float(np.float32(inp.sm_scale))
+    D = inp.q.shape[2]
+    p1 = inp.pool[:, :D].to(torch.float64) * float(inp.kv_scale[0])
+    p2 = ex.pool[:, :D].to(torch.float64) * float(ex.kv_scale[0])
+    for r in range(inp.q.shape[0]):
+        i1 = inp.indices[r].to(torch.int64)
+        i2 = ex.indices[r].to(torch.int64)
+        g = torch.cat([p1[i1[i1 >= 0]], p2[i2[i2 >= 0]]])
+        qr = inp.q[r].to(torch.float64)
+        H = qr.shape[0]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qr[:, None, :], g[None].expand(H, -1, -1), g[None, :, :512].expand(H, -1, -1), scale=sm)
+        assert _rel(out2[r], o[:, 0, :].numpy()) < 1e-12
+        l_ = torch.logsumexp(sm * torch.mm(qr, g.t()), dim=1).numpy()
+        assert np.max(np.abs(lse2[r] - l_)) < 1e-12
 
 
 # --------------------------------------------------------------- golden
