@@ -14,7 +14,10 @@ launches on. Rank 0 prints one JSON line.
 Headline workload: fp8 decode, 128 requests x (5+1) rows = 768 rows, 16 heads,
 576-wide rows, pool 262144 x 576 e4m3fn + per-tensor scale, top-k 2048 (the
 decode shape the HBM-roofline target is set on). The two 64-head prefill
-workloads are timed too and reported under "prefill" with their MFMA fraction.
+workloads are timed too and reported under "prefill" with their MFMA fraction,
+and the two decode workloads again as two-segment calls (a seeded 128-slot
+sliding window over a second pool with its own scale, next to the same
+workload's one-segment time) under "two_segment".
 """
 
 from __future__ import annotations
@@ -56,6 +59,10 @@ def parse():
     ap.add_argument("--workload", default="decode_fp8")
     ap.add_argument("--prefill", default="prefill_fp8,prefill_glm",
                     help="comma list of extra workloads to time ('' for none)")
+    ap.add_argument("--two-segment", default="decode_bf16,decode_fp8",
+                    help="comma list of workloads also timed with a sliding-window second "
+                         "segment ('' for none)")
+    ap.add_argument("--window", type=int, default=128, help="slots of that second segment")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
@@ -116,10 +123,12 @@ def traffic_from_profiles(kernel_src, workload):
         return None
 
 
-def time_workload(name, steps, warmup, cold):
+def time_workload(name, steps, warmup, cold, window=0):
+    """Time one workload; with `window` > 0 as a two-segment call whose second
+    segment is a seeded sliding window of that many slots over its own pool."""
     import torch
     from sparse_mla_attention_05_amd import _lib
-    from sparse_mla_attention_05_amd.inputs import make_inputs
+    from sparse_mla_attention_05_amd.inputs import make_extra_segment, make_inputs
 
     inp = make_inputs(name)
     dev = torch.device("cuda:0")
@@ -128,12 +137,24 @@ def time_workload(name, steps, warmup, cold):
     R, H = q.shape[0], q.shape[1]
     out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((R, H), dtype=torch.float32, device=dev)
-    plan = _lib.sparse_mla_plan(q, pool, idx)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if cold else None  # 1 GiB
     stream = torch.cuda.current_stream(dev)
+    ex = None
+    if window > 0:
+        ex = make_extra_segment(inp, window, seed=1000 + inp.workload.seed, value_std=0.7)
+        xpool, xidx = ex.pool.to(dev), ex.indices.to(dev)
+        xscale = ex.kv_scale.to(dev) if ex.kv_scale is not None else None
+        p1, p2, _ = _lib.sparse_mla_plan2(q, pool, idx, xpool, xidx)
+        plan = {"main": p1, "extra": p2}
 
-    def call():
-        _lib.sparse_mla_fwd(q, pool, scale, idx, inp.sm_scale, out, lse, stream=stream)
+        def call():
+            _lib.sparse_mla_fwd2(q, pool, scale, idx, xpool, xscale, xidx, inp.sm_scale, out, lse,
+                                 stream=stream)
+    else:
+        plan = _lib.sparse_mla_plan(q, pool, idx)
+
+        def call():
+            _lib.sparse_mla_fwd(q, pool, scale, idx, inp.sm_scale, out, lse, stream=stream)
 
     for _ in range(warmup):
         call()
@@ -162,6 +183,13 @@ def time_workload(name, steps, warmup, cold):
     torch.cuda.synchronize()
     warm_us = e0.elapsed_time(e1) * 1e3 / steps
     alg = algorithmic(inp)
+    if ex is not None:
+        eb = 1 if inp.workload.kv_dtype == "fp8" else 2
+        xv = int((ex.indices >= 0).sum())
+        xk = xv * inp.workload.d_qk * eb
+        alg = dict(kv_bytes=alg["kv_bytes"] + xk, bytes=alg["bytes"] + xk + ex.indices.numel() * 4,
+                   flops=alg["flops"] + 2 * H * xv * (inp.workload.d_qk + 512),
+                   valid_slots=alg["valid_slots"] + xv)
     return dict(inp=inp, plan=plan, times=times, wall=wall, warm_us=warm_us, alg=alg)
 
 
@@ -272,6 +300,20 @@ def main():
         del r
     if prefill:
         line["prefill"] = prefill
+    two = []
+    for name in [s for s in args.two_segment.split(",") if s]:
+        r = time_workload(name, args.steps, 3, cold, window=args.window)
+        one = time_workload(name, args.steps, 3, cold)
+        tus = statistics.median(r["times"])
+        ous = statistics.median(one["times"])
+        two.append({"workload": name, "window": args.window, "us_per_call": round(tus, 1),
+                    "one_segment_us_per_call": round(ous, 1),
+                    "gathered_kv_tbs": round(r["alg"]["kv_bytes"] / (tus * 1e-6) / 1e12, 2),
+                    "hbm_frac": round(r["alg"]["bytes"] / (tus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "warm_us_per_call": round(r["warm_us"], 1), "plan": r["plan"]})
+        del r, one
+    if two:
+        line["two_segment"] = two
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head["inp"], args.cpu_seconds)
     print(json.dumps(line), flush=True)

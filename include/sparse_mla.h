@@ -160,8 +160,12 @@ SMLA_API int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
  *                  holds both segments' partials (sparse_mla_plan2 gives its
  *                  size); without one the library's per-device buffer is used.
  *
- * Each segment's kernel writes normalised partials with its own scale, and
- * the split-combine kernel merges them (exact in real arithmetic). Every
+ * When the plan of the whole call (both segments' slots) launches the
+ * 16-head fp8 decode kernel, that kernel walks the main slots and then the
+ * extra ones, rebasing its accumulator from kv_scale onto extra_kv_scale
+ * between them (acc *= kv_scale / extra_kv_scale, as the pages do). Otherwise
+ * each segment's kernel writes normalised partials with its own scale and the
+ * split-combine kernel merges them. Both are exact in real arithmetic. Every
  * other rule is sparse_mla_fwd's; out and lse must not alias any input.
  */
 SMLA_API int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool,
@@ -170,8 +174,10 @@ SMLA_API int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool,
                     const smla_tensor* extra_indices, float sm_scale, smla_tensor* out,
                     smla_tensor* lse, void* stream, const smla_options* opt);
 
-/* The launches sparse_mla_fwd2 would make: each segment's plan and the bytes
- * of workspace for both segments' partials. Host-only; makes no HIP call. */
+/* The launches sparse_mla_fwd2 would make and the bytes of workspace they
+ * need: each segment's plan, or, when one decode-kernel launch walks both
+ * segments, that launch's plan in plan_main and grid 0 in plan_extra.
+ * Host-only; makes no HIP call. */
 SMLA_API int sparse_mla_plan2(const smla_tensor* q, const smla_tensor* kv_pool,
                      const smla_tensor* indices, const smla_tensor* extra_pool,
                      const smla_tensor* extra_indices, const smla_options* opt,

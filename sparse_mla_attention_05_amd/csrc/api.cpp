@@ -326,11 +326,24 @@ int validate_extra(const smla_tensor* q, const smla_tensor* kv_pool, const smla_
   return SMLA_OK;
 }
 
-// Plans of both segments of a two-segment call and their workspace.
+// Plans of a two-segment call and their workspace. When the plan of the
+// combined problem (both segments' slots, the larger pool range) launches the
+// decode kernel, that kernel walks both segments in one launch: *p1 is that
+// plan and *p2 has grid 0. Otherwise each segment gets its own plan and the
+// workspace holds both segments' partials for the combine kernel.
 int plan_two(const Checked& c1, const Checked& c2, const smla_options* opt, int num_cus,
              smla_plan* p1, smla_plan* p2, int64_t* ws_bytes) {
   const char* perr = nullptr;
   int s;
+  Problem tot = c1.pb;
+  tot.topk = c1.pb.topk + c2.pb.topk;
+  tot.pool_bytes = std::max(c1.pb.pool_bytes, c2.pb.pool_bytes);
+  if ((s = make_plan(tot, opt, num_cus, p1, &perr))) return fail(s, perr);
+  if (uses_decode_kernel(p1->head_block, c1.fp8, p1->variant)) {
+    *p2 = smla_plan{};
+    *ws_bytes = p1->splits > 1 ? partial_bytes(p1->splits, c1.pb.rows, c1.pb.heads, nullptr) : 0;
+    return SMLA_OK;
+  }
   if ((s = make_plan(c1.pb, opt, num_cus, p1, &perr))) return fail(s, perr);
   if ((s = make_plan(c2.pb, opt, num_cus, p2, &perr))) return fail(s, perr);
   *ws_bytes = partial_bytes(int64_t(p1->splits) + p2->splits, c1.pb.rows, c1.pb.heads, nullptr);
@@ -399,6 +412,32 @@ int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool, const smla
   smla_plan plan1, plan2;
   int64_t need = 0;
   if ((s = plan_two(c1, c2, opt, device_cus(dev), &plan1, &plan2, &need))) return s;
+  if (plan2.grid == 0) {
+    // One launch walks both segments (the combine kernel follows only when
+    // the plan splits).
+    FwdParams p = segment_params(q, kv_pool, static_cast<const float*>(kv_scale->data), indices, c1,
+                                 plan1, sm_scale, out, lse);
+    p.pool2 = static_cast<const uint8_t*>(extra_pool->data);
+    p.pool2_rs_bytes = extra_pool->stride[0] * elem_size(extra_pool->dtype);
+    p.pool2_bytes = uint32_t(std::min<int64_t>(c2.pb.pool_bytes, kMaxBufferBytes));
+    p.kv_scale2 = scale2;
+    p.idx2 = static_cast<const int32_t*>(extra_indices->data);
+    p.idx2_rs = extra_indices->stride[0];
+    p.topk2 = c2.pb.topk;
+    if (plan1.splits > 1) {
+      void* ws = nullptr;
+      int64_t lse_off = 0;
+      partial_bytes(plan1.splits, c1.pb.rows, c1.pb.heads, &lse_off);
+      if ((s = get_workspace(dev, opt, need, &ws))) return s;
+      p.part_o = static_cast<float*>(ws);
+      p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_off);
+    }
+    const int le = launch_forward(p, plan1, c1.pb.dqk, c1.fp8, stream);
+    if (le != 0)
+      return fail(SMLA_ERR_HIP, std::string("kernel launch: ") +
+                                    hipGetErrorString(static_cast<hipError_t>(le)));
+    return SMLA_OK;
+  }
   void* ws = nullptr;
   if ((s = get_workspace(dev, opt, need, &ws))) return s;
   const int64_t S = int64_t(plan1.splits) + plan2.splits;

@@ -100,12 +100,14 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
     }
   }
   const float kv_scale = *p.kv_scale;
-  const float c = p.sm_log2 * kv_scale;  // raw dot -> log2-domain score
+  float c = p.sm_log2 * kv_scale;  // raw dot -> log2-domain score (per segment)
+  float vs = kv_scale;             // scale of the V codes O is accumulated in
 
-  // This split's slots, walked in chunks whose indices are staged in LDS.
+  // This split's slots of the virtual list [main top-k | second segment],
+  // walked segment by segment in chunks whose indices are staged in LDS.
+  const int ktot = p.topk + (p.idx2 ? p.topk2 : 0);
   const int kbeg = split * p.tiles_per_split * kDecStep;
-  const int kend = min(p.topk, kbeg + p.tiles_per_split * kDecStep);
-  const int32_t* idx_row = p.idx + r * p.idx_rs;
+  const int kend = min(ktot, kbeg + p.tiles_per_split * kDecStep);
   int32_t* idx_s = reinterpret_cast<int32_t*>(smem + kIdxOffset);
 
   // Every global load in the walk is unconditional and its result is only
@@ -113,13 +115,11 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
   // copied between iterations, make the compiler wait for all outstanding
   // loads. An invalid slot's row is read at an offset past the end of the
   // pool's buffer range, which returns zeros without touching memory.
-  const __amdgpu_buffer_rsrc_t pool_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.pool), 0, p.pool_bytes, kBufferWord3);
-  auto gather = [&](u32x4 (&kr)[NI], int id) {
-    const uint32_t off = id >= 0 ? uint32_t(id) * uint32_t(p.pool_rs_bytes) + 16u * g : kOutOfRange;
+  auto gather = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t rs_bytes, u32x4 (&kr)[NI], int id) {
+    const uint32_t off = id >= 0 ? uint32_t(id) * rs_bytes + 16u * g : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pool_rsrc, off + 64u * i, 0, 0));
+      kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 64u * i, 0, 0));
   };
 
   uint8_t* vst = smem + wave * kVWave;
@@ -198,44 +198,76 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
     }
   };
 
-  for (int c0 = kbeg; c0 < kend; c0 += kIdxChunk) {
-    const int c1 = min(kend, c0 + kIdxChunk);
-    __syncthreads();  // every wave is done with the previous chunk's indices
-    for (int t = tid; t < c1 - c0; t += kDecWaves * 64) idx_s[t] = idx_row[c0 + t];
-    __syncthreads();
-    const int nst = (c1 - c0 + kDecStep - 1) / kDecStep;
-    const int nj = nst > wave ? (nst - wave + kDecWaves - 1) / kDecWaves : 0;
-    // Index of this lane's slot in the wave's step j, -1 when out of range.
-    auto slot_idx = [&](int j) -> int {
-      const int t = kDecStep * (wave + kDecWaves * j) + l16;
-      return (j < nj && t < c1 - c0) ? idx_s[t] : -1;
-    };
-    if (nj > 0) {
-      // kDecBufs steps of gathers in flight; the walk is unrolled by kDecBufs
-      // so each buffer keeps its registers, and runs a multiple of kDecBufs
-      // steps with no condition inside (steps past nj have no valid slot:
-      // their loads return zeros and their scores are -inf).
-      u32x4 kr[kDecBufs][NI];
-      int idb[kDecBufs];
-#pragma unroll
-      for (int u = 0; u < kDecBufs; ++u) {
-        idb[u] = slot_idx(u);
-        gather(kr[u], idb[u]);
-      }
-      const int nj_pad = (nj + kDecBufs - 1) / kDecBufs * kDecBufs;
-      for (int j = 0; j < nj_pad; j += kDecBufs) {
+  // Slots [lo, hi) of the virtual list, all in the segment that starts at
+  // virtual slot sb, whose rows come from `rsrc` (row stride rs_bytes) and
+  // whose indices are idx_seg[0..).
+  auto walk_range = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t rs_bytes,
+                        const int32_t* idx_seg, int lo, int hi, int sb) {
+    for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
+      const int c1 = min(hi, c0 + kIdxChunk);
+      __syncthreads();  // every wave is done with the previous chunk's indices
+      for (int t = tid; t < c1 - c0; t += kDecWaves * 64) idx_s[t] = idx_seg[c0 - sb + t];
+      __syncthreads();
+      const int nst = (c1 - c0 + kDecStep - 1) / kDecStep;
+      const int nj = nst > wave ? (nst - wave + kDecWaves - 1) / kDecWaves : 0;
+      // Index of this lane's slot in the wave's step j, -1 when out of range.
+      auto slot_idx = [&](int j) -> int {
+        const int t = kDecStep * (wave + kDecWaves * j) + l16;
+        return (j < nj && t < c1 - c0) ? idx_s[t] : -1;
+      };
+      if (nj > 0) {
+        // kDecBufs steps of gathers in flight; the walk is unrolled by
+        // kDecBufs so each buffer keeps its registers, and runs a multiple of
+        // kDecBufs steps with no condition inside (steps past nj have no
+        // valid slot: their loads return zeros and their scores are -inf).
+        u32x4 kr[kDecBufs][NI];
+        int idb[kDecBufs];
 #pragma unroll
         for (int u = 0; u < kDecBufs; ++u) {
-          step(kr[u], idb[u]);
-          idb[u] = slot_idx(j + u + kDecBufs);
-          gather(kr[u], idb[u]);
+          idb[u] = slot_idx(u);
+          gather(rsrc, rs_bytes, kr[u], idb[u]);
+        }
+        const int nj_pad = (nj + kDecBufs - 1) / kDecBufs * kDecBufs;
+        for (int j = 0; j < nj_pad; j += kDecBufs) {
+#pragma unroll
+          for (int u = 0; u < kDecBufs; ++u) {
+            step(kr[u], idb[u]);
+            idb[u] = slot_idx(j + u + kDecBufs);
+            gather(rsrc, rs_bytes, kr[u], idb[u]);
+          }
         }
       }
     }
+  };
+  // Segment 0 is the main top-k; segment 1, when given, the second one with
+  // its own rows and scale. Before segment 1, O (so far in units of the main
+  // scale) is rebased onto the second scale so one O serves both (exact in
+  // real arithmetic, like any rescale of the online softmax). The walk code
+  // is emitted once.
+  const int nseg = (p.idx2 && kend > p.topk) ? 2 : 1;
+#pragma clang loop unroll(disable)
+  for (int seg = 0; seg < nseg; ++seg) {
+    const bool second = seg == 1;
+    if (second) {
+      const float s2 = *p.kv_scale2;
+      const float rebase = vs / s2;
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) o[nb] *= rebase;
+      vs = s2;
+      c = p.sm_log2 * s2;
+    }
+    const int sb = second ? p.topk : 0;
+    const int lo = max(kbeg, sb), hi = min(kend, second ? ktot : p.topk);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(second ? p.pool2 : p.pool), 0, second ? p.pool2_bytes : p.pool_bytes,
+        kBufferWord3);
+    const uint32_t rs_bytes = uint32_t(second ? p.pool2_rs_bytes : p.pool_rs_bytes);
+    const int32_t* idx_seg = second ? p.idx2 + r * p.idx2_rs : p.idx + r * p.idx_rs;
+    walk_range(rsrc, rs_bytes, idx_seg, lo, hi, sb);
   }
 
   // ---- merge the four waves: M = max_w m_w, L = sum_w 2^(m_w - M) l_w,
-  // out = sum_w 2^(m_w - M) O_w * kv_scale / L, summed in wave order.
+  // out = sum_w 2^(m_w - M) O_w * vs / L, summed in wave order.
   float l_head = l_part;
   l_head += __shfl_xor(l_head, 16);
   l_head += __shfl_xor(l_head, 32);
@@ -259,7 +291,7 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
       L += mw == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mw - M) * red_l[w * 16 + head];
     }
     const float mine = red_m[wave * 16 + head];
-    const float f = (L > 0.f && mine != kNegInf) ? __builtin_amdgcn_exp2f(mine - M) * kv_scale / L : 0.f;
+    const float f = (L > 0.f && mine != kNegInf) ? __builtin_amdgcn_exp2f(mine - M) * vs / L : 0.f;
     float* prow = part + head * kOPitch + l16;
 #pragma unroll
     for (int nb = 0; nb < 32; ++nb) prow[16 * nb] = o[nb][i] * f;

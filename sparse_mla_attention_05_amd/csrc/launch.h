@@ -39,6 +39,16 @@ struct FwdParams {
   int32_t remap;
   int64_t grid;
   float sm_log2;            // sm_scale * log2(e)
+  // Second segment of a two-segment call walked inside the kernel (decode
+  // kernel only): its slots follow the topk main slots in one virtual list of
+  // topk + topk2 slots that the splits partition. idx2 == nullptr: none.
+  const uint8_t* pool2;
+  int64_t pool2_rs_bytes;
+  uint32_t pool2_bytes;
+  const float* kv_scale2;
+  const int32_t* idx2;
+  int64_t idx2_rs;
+  int32_t topk2;
 };
 
 struct Problem {
@@ -79,6 +89,12 @@ int launch_prefill_fp8(const FwdParams& p, int dqk, void* stream);
 // True when the (head block, pool dtype, variant) instance addresses the pool
 // through a buffer descriptor with 32-bit offsets (pools up to
 // kMaxBufferBytes); the other instances use 64-bit addresses.
+// The plan launches the 16-head fp8 decode kernel (decode.hip), the one
+// kernel that walks a second segment itself.
+inline bool uses_decode_kernel(int head_block, bool fp8, int variant) {
+  return head_block == 16 && fp8 && variant == 0;
+}
+
 inline bool uses_buffer_range(int head_block, bool fp8, int variant) {
   return (head_block == 16 && fp8 && variant == 0) || (head_block == 64 && variant != 1);
 }

@@ -217,8 +217,15 @@ def test_plan2_workspace_covers_both_segments(H, K1, K2, dtype):
     i1 = torch.zeros(R, K1, dtype=torch.int32)
     i2 = torch.zeros(R, K2, dtype=torch.int32)
     p1, p2, ws = _lib.sparse_mla_plan2(q, pool, i1, pool, i2)
-    assert p1 == _lib.sparse_mla_plan(q, pool, i1)
-    assert p2 == _lib.sparse_mla_plan(q, pool, i2)
-    S = p1["splits"] + p2["splits"]
+    whole = _lib.sparse_mla_plan(q, pool, torch.zeros(R, K1 + K2, dtype=torch.int32))
+    if H == 16 and dtype == torch.float8_e4m3fn:
+        # the decode kernel walks both segments in one launch
+        assert whole["head_block"] == 16 and whole["variant"] == 0
+        assert p1 == whole and p2["grid"] == 0
+        S = p1["splits"] if p1["splits"] > 1 else 0
+    else:
+        assert p1 == _lib.sparse_mla_plan(q, pool, i1)
+        assert p2 == _lib.sparse_mla_plan(q, pool, i2)
+        S = p1["splits"] + p2["splits"]
     o_bytes = S * R * H * 512 * 4
-    assert ws == (o_bytes + 255) // 256 * 256 + S * R * H * 4
+    assert ws == ((o_bytes + 255) // 256 * 256 + S * R * H * 4 if S else 0)

@@ -69,6 +69,12 @@ CASES = [
     ("fp8", 576, 16, 1000, 128, "request", dict(head_block=16, splits=3)),
     ("bf16", 576, 64, 512, 128, "request", dict(head_block=64, splits=2)),
     ("fp8", 576, 80, 512, 128, "request", {}),
+    # 16-head fp8 decode kernel walking both segments, splits across the
+    # segment boundary and one split holding only second-segment slots
+    ("fp8", 576, 16, 512, 128, "uniform", dict(head_block=16, splits=5)),
+    ("fp8", 512, 16, 2048, 128, "causal", {}),
+    # the same shape through the composition (another 16-head instance)
+    ("fp8", 576, 16, 512, 128, "request", dict(variant=1)),
 ]
 
 
