@@ -78,7 +78,8 @@ typedef struct smla_options {
                               kernel with two tiles of gathers in flight. 64-head: 1 =
                               single-buffered staged-tile kernel, 2 = 8-wave
                               double-buffered kernel (the default over bf16 pools; the
-                              fp8 default is the 4-wave kernel) */
+                              fp8 default is the 4-wave kernel), 3 = fp8 only: 8 waves
+                              with the QK and PV work on separate wavefronts */
   void* workspace;         /* optional caller device buffer for split partials */
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
 } smla_options;

@@ -441,6 +441,7 @@ hipError_t launch_by_head_block(int head_block, int variant, const FwdParams& p,
     case 64:
       if (variant == 1) return launch_inst<64, 0, DQK, FP8>(p, st);
       if (FP8 && variant == 0) return static_cast<hipError_t>(launch_prefill_fp8(p, DQK, st));
+      if (FP8 && variant == 3) return static_cast<hipError_t>(launch_prefill_pp(p, DQK, st));
       return static_cast<hipError_t>(launch_prefill(p, DQK, FP8, st));
     default: return hipErrorInvalidValue;
   }
@@ -459,6 +460,7 @@ KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant) {
     case 64:
       if (variant == 1) return fp8 ? shape_of<64, true, 0>(dqk) : shape_of<64, false, 0>(dqk);
       if (fp8 && variant == 0) return prefill_fp8_shape(dqk);
+      if (fp8 && variant == 3) return prefill_pp_shape(dqk);
       return prefill_shape(dqk, fp8);
     default: return KernelShape{};
   }

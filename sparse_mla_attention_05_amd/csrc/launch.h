@@ -86,6 +86,10 @@ int launch_prefill(const FwdParams& p, int dqk, bool fp8, void* stream);
 KernelShape prefill_fp8_shape(int dqk);
 int launch_prefill_fp8(const FwdParams& p, int dqk, void* stream);
 
+// 64 heads, fp8 pools, QK and PV on separate wavefronts (prefill_pp.hip).
+KernelShape prefill_pp_shape(int dqk);
+int launch_prefill_pp(const FwdParams& p, int dqk, void* stream);
+
 // True when the (head block, pool dtype, variant) instance addresses the pool
 // through a buffer descriptor with 32-bit offsets (pools up to
 // kMaxBufferBytes); the other instances use 64-bit addresses.

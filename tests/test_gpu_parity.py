@@ -282,14 +282,17 @@ def test_decode_fp8_variants(variant, topk, splits):
     _check(inp, variant=variant, splits=splits)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 @pytest.mark.parametrize("d_qk,kv,heads", [(576, "fp8", 64), (512, "fp8", 80), (576, "bf16", 64)])
 @pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (17, 1), (1000, 3)])
 def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
     """The 64-head kernels (variant 0: the 4-wave kernel over fp8 pools, the
     8-wave kernel over bf16 pools; 1: the single-buffered staged-tile kernel;
-    2: the 8-wave kernel) on ragged top-k, odd tile counts, a partial head
-    block, leading invalid tiles and an empty row, with and without splits."""
+    2: the 8-wave kernel; 3: the kernel with separate QK and PV waves, fp8
+    only) on ragged top-k, odd tile counts, a partial head block, leading
+    invalid tiles and an empty row, with and without splits."""
+    if variant == 3 and kv != "fp8":
+        pytest.skip("variant 3 is the fp8 kernel only")
     inp = _case(rows=5, heads=heads, d_qk=d_qk, topk=topk, pool_rows=8192, kv_dtype=kv,
                 invalid_per_row=29, seed=topk + splits + d_qk)
     idx = inp.indices.clone()
@@ -301,9 +304,9 @@ def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
     _check(inp, variant=variant, splits=splits, head_block=64)
 
 
-@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("kv,variant", [("fp8", 0), ("bf16", 0), ("fp8", 3)])
 @pytest.mark.parametrize("splits", [1, 2])
-def test_score_jump_after_first_tile(kv, splits):
+def test_score_jump_after_first_tile(kv, variant, splits):
     """Every head's first 64 slots point at near-zero keys and later slots at
     keys whose scores are ~138 higher in the log2 domain, so a reference max
     taken from the first tile would overflow P: the kernels must move their
@@ -326,5 +329,5 @@ def test_score_jump_after_first_tile(kv, splits):
         idx[r, 64:] = (300 + torch.randperm(N - 300, generator=g)[: K - 64]).to(torch.int32)
     idx[1, 100:110] = -1
     inp.indices = idx
-    print(f"\n[parity] score jump kv={kv} splits={splits}", flush=True)
-    _check(inp, splits=splits)
+    print(f"\n[parity] score jump kv={kv} variant={variant} splits={splits}", flush=True)
+    _check(inp, splits=splits, **({"variant": variant, "head_block": 64} if variant else {}))
