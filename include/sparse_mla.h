@@ -164,7 +164,9 @@ SMLA_API int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
  * When the plan of the whole call (both segments' slots) launches the
  * 16-head fp8 decode kernel, that kernel walks the main slots and then the
  * extra ones, rebasing its accumulator from kv_scale onto extra_kv_scale
- * between them (acc *= kv_scale / extra_kv_scale, as the pages do). Otherwise
+ * between them (acc *= kv_scale / extra_kv_scale, as the pages do); the
+ * 64-head kernel over bf16 pools likewise walks the extra slots after the
+ * main ones (no scale to rebase). Otherwise
  * each segment's kernel writes normalised partials with its own scale and the
  * split-combine kernel merges them. Both are exact in real arithmetic. Every
  * other rule is sparse_mla_fwd's; out and lse must not alias any input.
@@ -176,8 +178,8 @@ SMLA_API int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool,
                     smla_tensor* lse, void* stream, const smla_options* opt);
 
 /* The launches sparse_mla_fwd2 would make and the bytes of workspace they
- * need: each segment's plan, or, when one decode-kernel launch walks both
- * segments, that launch's plan in plan_main and grid 0 in plan_extra.
+ * need: each segment's plan, or, when one launch walks both segments, that
+ * launch's plan in plan_main and grid 0 in plan_extra.
  * Host-only; makes no HIP call. */
 SMLA_API int sparse_mla_plan2(const smla_tensor* q, const smla_tensor* kv_pool,
                      const smla_tensor* indices, const smla_tensor* extra_pool,

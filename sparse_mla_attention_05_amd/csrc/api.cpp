@@ -327,9 +327,10 @@ int validate_extra(const smla_tensor* q, const smla_tensor* kv_pool, const smla_
 }
 
 // Plans of a two-segment call and their workspace. When the plan of the
-// combined problem (both segments' slots, the larger pool range) launches the
-// decode kernel, that kernel walks both segments in one launch: *p1 is that
-// plan and *p2 has grid 0. Otherwise each segment gets its own plan and the
+// combined problem (both segments' slots, the larger pool range) launches a
+// kernel that walks a second segment (the 16-head fp8 decode kernel, the
+// 64-head bf16 kernel), that kernel walks both segments in one launch: *p1 is
+// that plan and *p2 has grid 0. Otherwise each segment gets its own plan and the
 // workspace holds both segments' partials for the combine kernel.
 int plan_two(const Checked& c1, const Checked& c2, const smla_options* opt, int num_cus,
              smla_plan* p1, smla_plan* p2, int64_t* ws_bytes) {
@@ -339,7 +340,13 @@ int plan_two(const Checked& c1, const Checked& c2, const smla_options* opt, int 
   tot.topk = c1.pb.topk + c2.pb.topk;
   tot.pool_bytes = std::max(c1.pb.pool_bytes, c2.pb.pool_bytes);
   if ((s = make_plan(tot, opt, num_cus, p1, &perr))) return fail(s, perr);
-  if (uses_decode_kernel(p1->head_block, c1.fp8, p1->variant)) {
+  if (walks_second_segment(p1->head_block, c1.fp8, p1->variant)) {
+    if (!uses_decode_kernel(p1->head_block, c1.fp8, p1->variant)) {
+      // Tiled walk: the second segment starts at a whole tile.
+      const int tile = std::max(1, p1->tile_slots);
+      tot.topk = (c1.pb.topk + tile - 1) / tile * tile + c2.pb.topk;
+      if ((s = make_plan(tot, opt, num_cus, p1, &perr))) return fail(s, perr);
+    }
     *p2 = smla_plan{};
     *ws_bytes = p1->splits > 1 ? partial_bytes(p1->splits, c1.pb.rows, c1.pb.heads, nullptr) : 0;
     return SMLA_OK;
@@ -415,8 +422,9 @@ int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool, const smla
   if (plan2.grid == 0) {
     // One launch walks both segments (the combine kernel follows only when
     // the plan splits).
-    FwdParams p = segment_params(q, kv_pool, static_cast<const float*>(kv_scale->data), indices, c1,
-                                 plan1, sm_scale, out, lse);
+    FwdParams p = segment_params(q, kv_pool,
+                                 c1.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
+                                 indices, c1, plan1, sm_scale, out, lse);
     p.pool2 = static_cast<const uint8_t*>(extra_pool->data);
     p.pool2_rs_bytes = extra_pool->stride[0] * elem_size(extra_pool->dtype);
     p.pool2_bytes = uint32_t(std::min<int64_t>(c2.pb.pool_bytes, kMaxBufferBytes));

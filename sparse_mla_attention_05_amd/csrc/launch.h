@@ -93,10 +93,17 @@ int launch_prefill_pp(const FwdParams& p, int dqk, void* stream);
 // True when the (head block, pool dtype, variant) instance addresses the pool
 // through a buffer descriptor with 32-bit offsets (pools up to
 // kMaxBufferBytes); the other instances use 64-bit addresses.
-// The plan launches the 16-head fp8 decode kernel (decode.hip), the one
-// kernel that walks a second segment itself.
+// The plan launches the 16-head fp8 decode kernel (decode.hip).
 inline bool uses_decode_kernel(int head_block, bool fp8, int variant) {
   return head_block == 16 && fp8 && variant == 0;
+}
+
+// The plan launches a kernel that walks a second segment itself: the decode
+// kernel (its walk splits at the segment boundary) or the 64-head kernel of
+// prefill.hip over bf16 pools (the main segment padded to whole tiles).
+inline bool walks_second_segment(int head_block, bool fp8, int variant) {
+  return uses_decode_kernel(head_block, fp8, variant) ||
+         (head_block == 64 && !fp8 && (variant == 0 || variant == 2));
 }
 
 inline bool uses_buffer_range(int head_block, bool fp8, int variant) {

@@ -92,7 +92,12 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   const int64_t r = work / p.splits;
   const int h0 = hb * HB;
 
-  const int ntiles = (p.topk + TK - 1) / TK;
+  // Tiles [0, T1) hold the main top-k, tiles [T1, ntiles) a second segment
+  // when one is given (bf16 pools: its rows need no scale of their own); the
+  // main segment is padded to whole tiles with invalid slots.
+  const bool two = p.idx2 != nullptr;
+  const int T1 = (p.topk + TK - 1) / TK;
+  const int ntiles = two ? T1 + (p.topk2 + TK - 1) / TK : T1;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(ntiles, t_begin + p.tiles_per_split);
 
@@ -122,21 +127,31 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   // Gather role: slot gk of a tile, 16-byte chunks gp, gp + 8, ...
   const int gk = tid / TPK, gp = tid % TPK;
   const int32_t* idx_row = p.idx + r * p.idx_rs;
-  const int last_slot = min(p.topk, t_end * TK) - 1;
+  const int32_t* idx2_row = two ? p.idx2 + r * p.idx2_rs : idx_row;
+  // Index of slot gk of tile t (-1: invalid, padding or past the split).
   auto load_idx = [&](int t) -> int {
-    const int j = t * TK + gk;
-    const int v = idx_row[min(j, last_slot)];
-    return v | -int(!(t < t_end && j <= last_slot));
+    const bool seg2 = two && t >= T1;
+    const int j = (seg2 ? t - T1 : t) * TK + gk;
+    const int kseg = seg2 ? p.topk2 : p.topk;
+    const int v = (seg2 ? idx2_row : idx_row)[min(j, kseg - 1)];
+    return v | -int(!(t < t_end && j < kseg));
   };
   const __amdgpu_buffer_rsrc_t pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.pool), 0, p.pool_bytes, kPreBufferWord3);
-  auto gather = [&](u32x4 (&pre)[LPT], int id) {
-    const uint32_t off = id >= 0 ? uint32_t(id) * uint32_t(p.pool_rs_bytes) : kPreOutOfRange;
+  const __amdgpu_buffer_rsrc_t pool2_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(two ? p.pool2 : p.pool), 0, two ? p.pool2_bytes : p.pool_bytes,
+      kPreBufferWord3);
+  // Rows of tile t, whose slot gk holds index `id`.
+  auto gather = [&](u32x4 (&pre)[LPT], int id, int t) {
+    const bool seg2 = two && t >= T1;
+    const __amdgpu_buffer_rsrc_t rsrc = seg2 ? pool2_rsrc : pool_rsrc;
+    const uint32_t rs = uint32_t(seg2 ? p.pool2_rs_bytes : p.pool_rs_bytes);
+    const uint32_t off = id >= 0 ? uint32_t(id) * rs : kPreOutOfRange;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = min(gp + TPK * i, CH - 1);
       pre[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(pool_rsrc, off + 16u * uint32_t(c), 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16u * uint32_t(c), 0, 0));
     }
   };
   auto stage = [&](const u32x4 (&pre)[LPT], int id, int buf) {
@@ -266,10 +281,10 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   if (t_begin < t_end) {
     u32x4 pre[LPT];
     int id_a = load_idx(t_begin);
-    gather(pre, id_a);
+    gather(pre, id_a, t_begin);
     int id_b = load_idx(t_begin + 1);
     stage(pre, id_a, 0);
-    gather(pre, id_b);
+    gather(pre, id_b, t_begin + 1);
     int id_n = load_idx(t_begin + 2);
     __syncthreads();  // tile t_begin visible
     qk(0);
@@ -279,7 +294,7 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
     if (t_begin + 1 < t_end) {
       stage(pre, id_b, 1);
       id_b = id_n;
-      gather(pre, id_b);
+      gather(pre, id_b, t_begin + 2);
       id_n = load_idx(t_begin + 3);
     }
     __syncthreads();  // B: P(t_begin), tile t_begin+1 visible
@@ -297,7 +312,7 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
         if (t + 2 < t_end) {
           stage(pre, id_b, buf);
           id_b = id_n;
-          gather(pre, id_b);
+          gather(pre, id_b, t + 3);
           id_n = load_idx(t + 4);
         }
       }

@@ -223,6 +223,12 @@ def test_plan2_workspace_covers_both_segments(H, K1, K2, dtype):
         assert whole["head_block"] == 16 and whole["variant"] == 0
         assert p1 == whole and p2["grid"] == 0
         S = p1["splits"] if p1["splits"] > 1 else 0
+    elif dtype == torch.bfloat16:
+        # the 64-head bf16 kernel walks them too, the main top-k padded to tiles
+        K1p = (K1 + whole["tile_slots"] - 1) // whole["tile_slots"] * whole["tile_slots"]
+        padded = _lib.sparse_mla_plan(q, pool, torch.zeros(R, K1p + K2, dtype=torch.int32))
+        assert p1 == padded and p2["grid"] == 0
+        S = p1["splits"] if p1["splits"] > 1 else 0
     else:
         assert p1 == _lib.sparse_mla_plan(q, pool, i1)
         assert p2 == _lib.sparse_mla_plan(q, pool, i2)

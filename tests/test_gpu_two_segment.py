@@ -75,6 +75,11 @@ CASES = [
     ("fp8", 512, 16, 2048, 128, "causal", {}),
     # the same shape through the composition (another 16-head instance)
     ("fp8", 576, 16, 512, 128, "request", dict(variant=1)),
+    # 64-head bf16 kernel walking both segments: main top-k padded to whole
+    # tiles, splits across the boundary; and the composition for comparison
+    ("bf16", 576, 64, 300, 100, "causal", {}),
+    ("bf16", 512, 64, 1000, 128, "uniform", dict(head_block=64, splits=3)),
+    ("bf16", 576, 64, 512, 128, "request", dict(variant=1)),
 ]
 
 
