@@ -15,3 +15,4 @@ from .sparse_mla_oracle import (  # noqa: F401
     sparse_mla_fwd_2seg_torch,
     sparse_mla_fwd_torch,
 )
+from . import out_epilogue  # noqa: F401,E402  (inverse RoPE + MXFP8 output epilogue)

@@ -293,3 +293,55 @@ def tensor_digest(t: torch.Tensor) -> str:
     t = t.contiguous()
     b = t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16 if t.element_size() == 2 else torch.int32)
     return hashlib.sha256(b.numpy().tobytes()).hexdigest()
+
+
+# ------------------------------------------------------ output epilogue ---
+
+@dataclass
+class EpilogueInputs:
+    """Inputs of the output epilogue: a position per query row and a cos/sin
+    cache. ``cos_sin`` is fp32 [max_pos, 64]: row p holds the cosines of the
+    32 pair angles at position p, then their sines (the layout of a serving
+    stack's rotary cache); the angles are p * base^(-2j/64)."""
+    positions: torch.Tensor   # int32 [R]
+    cos_sin: torch.Tensor     # fp32 [max_pos, 64]
+
+
+def make_rope_cache(max_pos: int, base: float = 10000.0) -> torch.Tensor:
+    """fp32 [max_pos, 64] cos|sin table of the 32 rotary frequencies."""
+    j = torch.arange(32, dtype=torch.float64)
+    inv_freq = base ** (-2.0 * j / 64.0)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv_freq[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32)
+
+
+def make_epilogue_inputs(rows: int, seed: int, max_pos: int = 131072,
+                         first_pos: int | None = None) -> EpilogueInputs:
+    """Positions drawn uniformly from [0, max_pos) (or first_pos + row, the
+    positions of consecutive prefill rows), and the cache."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    if first_pos is None:
+        pos = torch.randint(0, max_pos, (rows,), generator=gen, dtype=torch.int64)
+    else:
+        pos = (first_pos + torch.arange(rows, dtype=torch.int64)) % max_pos
+    return EpilogueInputs(pos.to(torch.int32), make_rope_cache(max_pos))
+
+
+def make_epilogue_rows(rows: int, heads: int, seed: int, std: float = 0.05) -> torch.Tensor:
+    """bf16 [R, H, 512] rows shaped like attention outputs, N(0, std^2), with
+    blocks that reach the MXFP8 edge cases: an all-zero 32-column block, a
+    block whose largest magnitude sits just under and one just at a power of
+    two, one block scaled up by 2^20 and one down by 2^-20 (e4m3 subnormals
+    and flushes), and negative values that round to zero."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(rows, heads, 512, generator=gen, dtype=torch.float32) * std
+    for r in range(rows):
+        h = r % heads
+        x[r, h, 0:32] = 0.0
+        x[r, h, 32:64] *= 1.0 / x[r, h, 32:64].abs().max()          # amax = 1 exactly
+        x[r, h, 64:96] *= (1.0 - 2.0 ** -8) / x[r, h, 64:96].abs().max()
+        x[r, h, 96:128] *= 2.0 ** 20
+        x[r, h, 128:160] *= 2.0 ** -20
+        x[r, h, 160] = -1e-9                                          # rounds to -0 in e4m3
+        x[r, h, 448:512] *= 4.0                                       # the rotated columns
+    return x.to(torch.bfloat16)
