@@ -48,7 +48,8 @@ typedef enum smla_dtype {
   SMLA_BF16 = 0,
   SMLA_FP8_E4M3FN = 1,
   SMLA_FP32 = 2,
-  SMLA_INT32 = 3
+  SMLA_INT32 = 3,
+  SMLA_E8M0 = 4 /* one byte, a power of two 2^(code - 127); MX block scales */
 } smla_dtype;
 
 typedef enum smla_status {
@@ -186,6 +187,66 @@ SMLA_API int sparse_mla_plan2(const smla_tensor* q, const smla_tensor* kv_pool,
                      const smla_tensor* extra_indices, const smla_options* opt,
                      int32_t num_cus, smla_plan* plan_main, smla_plan* plan_extra,
                      int64_t* workspace_bytes);
+
+/*
+ * Output epilogue, after "[Triton/Gluon] GFX950 sparse mla optimizations"
+ * (aiter PR 6159), the commit notes on the fused epilogue: before the output
+ * projection a serving stack rotates the last 64 columns of each attention
+ * output row back (inverse RoPE) and, for an MXFP8 projection, quantises the
+ * row to float8_e4m3fn with one E8M0 scale per 32 columns. The store that
+ * writes the output does both (the attention kernel's, or the split-combine
+ * kernel's when the plan splits).
+ *
+ * Arithmetic, for row r and head h: the output row is rounded to bf16 first;
+ * with positions, pair j = 0..31 of columns (448 + 2j, 449 + 2j) = (x, y) and
+ * c = cos_sin[pos[r], j], s = cos_sin[pos[r], 32 + j] becomes
+ * (x*c + y*s, y*c - x*s), every product and sum rounded to fp32 on its own.
+ * Then either a bf16 store (round to nearest even) or MXFP8: per 32-column
+ * block, scale code e = clamp(floor(log2(max |v|)) - 8 + 127, 0, 254) (code 0
+ * for an all-zero block), codes = e4m3fn(v / 2^(e - 127)) rounded to nearest
+ * even, saturated at +-448, sign kept. The fused result is bit-identical to
+ * running sparse_mla_out_epilogue on the bf16 output of the same call.
+ *
+ *  rope_positions  int32 [R] or NULL (no rotation). Positions outside
+ *                  [0, P) are a caller error: the kernels clamp them into
+ *                  range so no read leaves the cache.
+ *  rope_cos_sin    fp32 [P, 64], last dim contiguous, 4-byte aligned; given
+ *                  iff rope_positions is.
+ *  out_scale       E8M0 [R, H, 16] or NULL. Given: `out` holds the
+ *                  float8_e4m3fn codes [R, H, 512] (MXFP8); NULL: `out` is
+ *                  bf16 [R, H, 512]. Base, row and head strides of an MXFP8
+ *                  `out` must be multiples of 16 bytes.
+ * Every epilogue tensor is caller-owned device memory; none may alias out,
+ * out_scale or lse.
+ */
+typedef struct smla_epilogue {
+  const smla_tensor* rope_positions;
+  const smla_tensor* rope_cos_sin;
+  smla_tensor* out_scale;
+} smla_epilogue;
+
+/*
+ * sparse_mla_fwd_epi - the forward with its output epilogue: sparse_mla_fwd2
+ * (extra_* may be NULL for one segment) whose final store applies `epi`
+ * (NULL or an epilogue with nothing set: a plain bf16 store). Every other
+ * rule is sparse_mla_fwd2's.
+ */
+SMLA_API int sparse_mla_fwd_epi(const smla_tensor* q, const smla_tensor* kv_pool,
+                       const smla_tensor* kv_scale, const smla_tensor* indices,
+                       const smla_tensor* extra_pool, const smla_tensor* extra_kv_scale,
+                       const smla_tensor* extra_indices, float sm_scale,
+                       const smla_epilogue* epi, smla_tensor* out, smla_tensor* lse,
+                       void* stream, const smla_options* opt);
+
+/*
+ * sparse_mla_out_epilogue - the epilogue as a pass of its own over bf16 rows
+ * [R, H, 512] (e.g. a forward's output): the separate pass that the fused
+ * store replaces. rows: bf16, last dim contiguous, base and strides 16-byte
+ * aligned; epi must not be NULL; out as for sparse_mla_fwd_epi and must not
+ * alias rows. R * H == 0 is a no-op.
+ */
+SMLA_API int sparse_mla_out_epilogue(const smla_tensor* rows, const smla_epilogue* epi,
+                            smla_tensor* out, void* stream);
 
 /* 1 if the shapes/dtypes/strides are covered by the kernels, else 0 (the
  * reason is left in sparse_mla_last_error). Host-only; makes no HIP call. */

@@ -13,8 +13,10 @@ from ._lib import (  # noqa: F401
     load,
     sparse_mla_fwd,
     sparse_mla_fwd2,
+    sparse_mla_fwd_epi,
     sparse_mla_fwd_ex,
     sparse_mla_is_supported,
+    sparse_mla_out_epilogue,
     sparse_mla_plan,
     sparse_mla_plan2,
     sparse_mla_work_of,

@@ -15,15 +15,15 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsparse_mla.so")
 
-SMLA_BF16, SMLA_FP8_E4M3FN, SMLA_FP32, SMLA_INT32 = 0, 1, 2, 3
+SMLA_BF16, SMLA_FP8_E4M3FN, SMLA_FP32, SMLA_INT32, SMLA_E8M0 = 0, 1, 2, 3, 4
 SMLA_OK, SMLA_ERR_INVALID_ARG, SMLA_ERR_UNSUPPORTED, SMLA_ERR_HIP = 0, 1, 2, 3
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED", 3: "SMLA_ERR_HIP"}
 UNKNOWN_DTYPE = 1000  # any dtype the library does not know (e.g. float8_e4m3fnuz)
 
 EXPORTED = (
-    "sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_fwd2", "sparse_mla_is_supported",
-    "sparse_mla_plan", "sparse_mla_plan2", "sparse_mla_work_of", "sparse_mla_last_error",
-    "sparse_mla_version",
+    "sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_fwd2", "sparse_mla_fwd_epi",
+    "sparse_mla_out_epilogue", "sparse_mla_is_supported", "sparse_mla_plan", "sparse_mla_plan2",
+    "sparse_mla_work_of", "sparse_mla_last_error", "sparse_mla_version",
 )
 
 
@@ -45,6 +45,12 @@ class SmlaPlan(ctypes.Structure):
                 ("tile_slots", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("variant", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class SmlaEpilogue(ctypes.Structure):
+    _fields_ = [("rope_positions", ctypes.POINTER(SmlaTensor)),
+                ("rope_cos_sin", ctypes.POINTER(SmlaTensor)),
+                ("out_scale", ctypes.POINTER(SmlaTensor))]
 
 
 class SparseMLAError(RuntimeError):
@@ -74,6 +80,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_fwd2.argtypes = [T, T, T, T, T, T, T, ctypes.c_float, T, T, ctypes.c_void_p,
                                     ctypes.POINTER(SmlaOptions)]
     lib.sparse_mla_fwd2.restype = ctypes.c_int
+    E = ctypes.POINTER(SmlaEpilogue)
+    lib.sparse_mla_fwd_epi.argtypes = [T, T, T, T, T, T, T, ctypes.c_float, E, T, T,
+                                       ctypes.c_void_p, ctypes.POINTER(SmlaOptions)]
+    lib.sparse_mla_fwd_epi.restype = ctypes.c_int
+    lib.sparse_mla_out_epilogue.argtypes = [T, E, T, ctypes.c_void_p]
+    lib.sparse_mla_out_epilogue.restype = ctypes.c_int
     lib.sparse_mla_plan2.argtypes = [T, T, T, T, T, ctypes.POINTER(SmlaOptions), ctypes.c_int32,
                                      ctypes.POINTER(SmlaPlan), ctypes.POINTER(SmlaPlan),
                                      ctypes.POINTER(ctypes.c_int64)]
@@ -97,7 +109,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
 def dtype_code(dtype) -> int:
     import torch
     return {torch.bfloat16: SMLA_BF16, torch.float8_e4m3fn: SMLA_FP8_E4M3FN,
-            torch.float32: SMLA_FP32, torch.int32: SMLA_INT32}.get(dtype, UNKNOWN_DTYPE)
+            torch.float32: SMLA_FP32, torch.int32: SMLA_INT32,
+            torch.float8_e8m0fnu: SMLA_E8M0}.get(dtype, UNKNOWN_DTYPE)
 
 
 def describe(t) -> SmlaTensor | None:
@@ -265,3 +278,61 @@ def forward2(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_in
     sparse_mla_fwd2(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices,
                     sm_scale, out, lse, **options)
     return out, lse
+
+
+def _epilogue(rope_positions=None, rope_cos_sin=None, out_scale=None):
+    """smla_epilogue and the descriptors it points at (kept alive together)."""
+    ds = [describe(t) for t in (rope_positions, rope_cos_sin, out_scale)]
+    epi = SmlaEpilogue()
+    epi.rope_positions = ctypes.pointer(ds[0]) if ds[0] is not None else None
+    epi.rope_cos_sin = ctypes.pointer(ds[1]) if ds[1] is not None else None
+    epi.out_scale = ctypes.pointer(ds[2]) if ds[2] is not None else None
+    return epi, ds
+
+
+def sparse_mla_fwd_epi(q, kv_pool, kv_scale, indices, sm_scale, out, lse, rope_positions=None,
+                       rope_cos_sin=None, out_scale=None, extra_pool=None, extra_kv_scale=None,
+                       extra_indices=None, stream=None, head_block=0, splits=0, remap=0,
+                       workspace=None, workspace_bytes=None, variant=0) -> None:
+    """Forward whose final store applies the output epilogue: inverse RoPE of
+    columns 448..511 (rope_positions int32 [R], rope_cos_sin fp32 [P, 64]) and,
+    with out_scale (float8_e8m0fnu [R, H, 16]), an MXFP8 store of float8_e4m3fn
+    codes into out; else out is bf16."""
+    lib = load()
+    ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale,
+                                extra_indices, out, lse)]
+    epi, _keep = _epilogue(rope_positions, rope_cos_sin, out_scale)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant)
+    st = _stream_handle(stream, q, out)
+    _check(lib.sparse_mla_fwd_epi(*[_ptr(d) for d in ds[:7]], float(sm_scale), ctypes.byref(epi),
+                                  _ptr(ds[7]), _ptr(ds[8]), st, ctypes.byref(opt)))
+
+
+def sparse_mla_out_epilogue(rows, out, rope_positions=None, rope_cos_sin=None, out_scale=None,
+                            stream=None) -> None:
+    """The output epilogue as a pass of its own over bf16 rows [R, H, 512]."""
+    lib = load()
+    dr, do = describe(rows), describe(out)
+    epi, _keep = _epilogue(rope_positions, rope_cos_sin, out_scale)
+    st = _stream_handle(stream, rows, out)
+    _check(lib.sparse_mla_out_epilogue(_ptr(dr), ctypes.byref(epi), _ptr(do), st))
+
+
+def status_of_fwd_epi(q, kv_pool, kv_scale, indices, sm_scale, out, lse, rope_positions=None,
+                      rope_cos_sin=None, out_scale=None, stream=None) -> int:
+    """Raw status of sparse_mla_fwd_epi with one segment and no options (for
+    tests of the error paths)."""
+    lib = load()
+    ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, out, lse)]
+    epi, _keep = _epilogue(rope_positions, rope_cos_sin, out_scale)
+    return lib.sparse_mla_fwd_epi(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), _ptr(ds[3]), None, None,
+                                  None, float(sm_scale), ctypes.byref(epi), _ptr(ds[4]),
+                                  _ptr(ds[5]), stream, None)
+
+
+def status_of_out_epilogue(rows, out, rope_positions=None, rope_cos_sin=None, out_scale=None,
+                           stream=None) -> int:
+    lib = load()
+    dr, do = describe(rows), describe(out)
+    epi, _keep = _epilogue(rope_positions, rope_cos_sin, out_scale)
+    return lib.sparse_mla_out_epilogue(_ptr(dr), ctypes.byref(epi), _ptr(do), stream)

@@ -29,6 +29,7 @@ const char* dtype_name(int32_t d) {
     case SMLA_FP8_E4M3FN: return "fp8_e4m3fn";
     case SMLA_FP32: return "fp32";
     case SMLA_INT32: return "int32";
+    case SMLA_E8M0: return "e8m0";
     default: return "unknown";
   }
 }
@@ -39,6 +40,7 @@ int elem_size(int32_t d) {
     case SMLA_FP8_E4M3FN: return 1;
     case SMLA_FP32: return 4;
     case SMLA_INT32: return 4;
+    case SMLA_E8M0: return 1;
     default: return 0;
   }
 }
@@ -148,9 +150,10 @@ int validate_inputs(const smla_tensor* q, const smla_tensor* kv, const smla_tens
   return SMLA_OK;
 }
 
+// out is bf16, or float8_e4m3fn codes for an MXFP8 epilogue (out_dtype).
 int validate_all(const smla_tensor* q, const smla_tensor* kv, const smla_tensor* scale,
                  const smla_tensor* idx, float sm_scale, const smla_tensor* out,
-                 const smla_tensor* lse, Checked* c) {
+                 const smla_tensor* lse, Checked* c, int32_t out_dtype = SMLA_BF16) {
   int s;
   if ((s = validate_inputs(q, kv, idx, c))) return s;
   const int64_t R = c->pb.rows, H = c->pb.heads;
@@ -163,7 +166,7 @@ int validate_all(const smla_tensor* q, const smla_tensor* kv, const smla_tensor*
     return fail(SMLA_ERR_INVALID_ARG, "kv_scale: must be NULL for a bf16 pool");
   }
   if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_INVALID_ARG, "sm_scale: not finite");
-  if ((s = check_tensor(out, "out", 3, SMLA_BF16))) return s;
+  if ((s = check_tensor(out, "out", 3, out_dtype))) return s;
   if ((s = check_tensor(lse, "lse", 2, SMLA_FP32))) return s;
   if (out->shape[0] != R || out->shape[1] != H || out->shape[2] != kDv)
     return fail(SMLA_ERR_INVALID_ARG, "out: shape must be [R, H, 512]");
@@ -172,7 +175,8 @@ int validate_all(const smla_tensor* q, const smla_tensor* kv, const smla_tensor*
   if (R > 0) {
     if (!out->data) return fail(SMLA_ERR_INVALID_ARG, "out: null data");
     if (!lse->data) return fail(SMLA_ERR_INVALID_ARG, "lse: null data");
-    if (!aligned16(out->data) || (out->stride[0] * 2) % 16 != 0 || (out->stride[1] * 2) % 16 != 0)
+    const int ob = elem_size(out_dtype);
+    if (!aligned16(out->data) || (out->stride[0] * ob) % 16 != 0 || (out->stride[1] * ob) % 16 != 0)
       return fail(SMLA_ERR_UNSUPPORTED, "out: base, row and head strides must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(lse->data) & 3u) != 0)
       return fail(SMLA_ERR_INVALID_ARG, "lse: base must be 4-byte aligned");
@@ -234,6 +238,76 @@ int device_cus(int dev) {
     g_cu_count[dev] = n;
   }
   return g_cu_count[dev];
+}
+
+// dtype of `out` under an epilogue: e4m3fn codes with an MXFP8 scale tensor,
+// else bf16.
+int32_t epi_out_dtype(const smla_epilogue* epi) {
+  return (epi && epi->out_scale) ? SMLA_FP8_E4M3FN : SMLA_BF16;
+}
+
+// Checks the epilogue tensors of an R x H output (out already checked) and
+// fills the kernels' view of them; `ins` are the call's inputs, which the
+// epilogue's outputs must not alias.
+int validate_epilogue(const smla_epilogue* epi, int64_t R, int64_t H, smla_tensor* out,
+                      const smla_tensor* lse, const smla_tensor* const* ins, int n_ins,
+                      EpiOut* e) {
+  *e = EpiOut{};
+  e->out = static_cast<uint16_t*>(out->data);
+  e->out_rs = out->stride[0];
+  e->out_hs = out->stride[1];
+  if (!epi) return SMLA_OK;
+  int s;
+  const smla_tensor* pos = epi->rope_positions;
+  const smla_tensor* cs = epi->rope_cos_sin;
+  smla_tensor* sc = epi->out_scale;
+  if (pos) {
+    if ((s = check_tensor(pos, "rope_positions", 1, SMLA_INT32))) return s;
+    if (pos->shape[0] != R) return fail(SMLA_ERR_INVALID_ARG, "rope_positions: shape must be [R]");
+    if (!cs) return fail(SMLA_ERR_INVALID_ARG, "rope_cos_sin: required with rope_positions");
+    if ((s = check_tensor(cs, "rope_cos_sin", 2, SMLA_FP32))) return s;
+    if (cs->shape[1] != 64) return fail(SMLA_ERR_UNSUPPORTED, "rope_cos_sin: shape must be [P, 64]");
+    if (cs->shape[0] < 1 || cs->shape[0] > INT32_MAX)
+      return fail(SMLA_ERR_INVALID_ARG, "rope_cos_sin: P must be in [1, 2^31)");
+    if (cs->shape[0] > 1 && cs->stride[0] < 64)
+      return fail(SMLA_ERR_INVALID_ARG, "rope_cos_sin: row stride smaller than 64");
+    if (R > 0) {
+      if (!pos->data || !cs->data) return fail(SMLA_ERR_INVALID_ARG, "rope: null data");
+      if ((reinterpret_cast<uintptr_t>(pos->data) & 3u) || (reinterpret_cast<uintptr_t>(cs->data) & 3u))
+        return fail(SMLA_ERR_INVALID_ARG, "rope: base must be 4-byte aligned");
+    }
+    e->pos = static_cast<const int32_t*>(pos->data);
+    e->cs = static_cast<const float*>(cs->data);
+    e->cs_rs = cs->stride[0];
+    e->cs_rows = int32_t(cs->shape[0]);
+  } else if (cs) {
+    return fail(SMLA_ERR_INVALID_ARG, "rope_cos_sin: given without rope_positions");
+  }
+  if (sc) {
+    if ((s = check_tensor(sc, "out_scale", 3, SMLA_E8M0))) return s;
+    if (sc->shape[0] != R || sc->shape[1] != H || sc->shape[2] != kDv / 32)
+      return fail(SMLA_ERR_INVALID_ARG, "out_scale: shape must be [R, H, 16]");
+    if (R > 0 && !sc->data) return fail(SMLA_ERR_INVALID_ARG, "out_scale: null data");
+    e->out = nullptr;
+    e->q8 = static_cast<uint8_t*>(out->data);
+    e->sc = static_cast<uint8_t*>(sc->data);
+    e->sc_rs = sc->stride[0];
+    e->sc_hs = sc->stride[1];
+  }
+  if (R > 0 && H > 0) {
+    const smla_tensor* outs[3] = {out, sc, lse};
+    for (const smla_tensor* o : outs) {
+      if (!o) continue;
+      for (int i = 0; i < n_ins; ++i)
+        if (ins[i] && overlap(o, ins[i]))
+          return fail(SMLA_ERR_INVALID_ARG, "outputs must not alias an input");
+      if (o != out && overlap(o, out)) return fail(SMLA_ERR_INVALID_ARG, "out_scale/lse overlap out");
+      if (pos && (overlap(o, pos) || overlap(o, cs)))
+        return fail(SMLA_ERR_INVALID_ARG, "outputs must not alias the rope tensors");
+    }
+    if (sc && lse && overlap(sc, lse)) return fail(SMLA_ERR_INVALID_ARG, "out_scale and lse overlap");
+  }
+  return SMLA_OK;
 }
 
 // Kernel parameters of one segment: q/out/lse of the call, pool/scale/indices
@@ -357,20 +431,16 @@ int plan_two(const Checked& c1, const Checked& c2, const smla_options* opt, int 
   return SMLA_OK;
 }
 
-}  // namespace
-}  // namespace smla
-
-using namespace smla;
-
-extern "C" {
-
-int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
-                      const smla_tensor* kv_scale, const smla_tensor* indices, float sm_scale,
-                      smla_tensor* out, smla_tensor* lse, void* stream,
-                      const smla_options* opt) {
+// One-segment forward with an optional output epilogue.
+int fwd_one(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
+            const smla_tensor* indices, float sm_scale, const smla_epilogue* epi,
+            smla_tensor* out, smla_tensor* lse, void* stream, const smla_options* opt) {
   Checked c;
-  int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c);
+  int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c, epi_out_dtype(epi));
   if (s) return s;
+  EpiOut eo;
+  const smla_tensor* ins[4] = {q, kv_pool, indices, c.fp8 ? kv_scale : nullptr};
+  if ((s = validate_epilogue(epi, c.pb.rows, c.pb.heads, out, lse, ins, 4, &eo))) return s;
   if (c.pb.rows == 0) return SMLA_OK;
 
   int dev = 0;
@@ -382,6 +452,7 @@ int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
 
   FwdParams p = segment_params(q, kv_pool, c.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
                                indices, c, plan, sm_scale, out, lse);
+  p.epi = eo;
   if (plan.splits > 1) {
     void* ws = nullptr;
     int64_t lse_off = 0;
@@ -397,20 +468,26 @@ int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
   return SMLA_OK;
 }
 
-int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
-                    const smla_tensor* indices, const smla_tensor* extra_pool,
-                    const smla_tensor* extra_kv_scale, const smla_tensor* extra_indices,
-                    float sm_scale, smla_tensor* out, smla_tensor* lse, void* stream,
-                    const smla_options* opt) {
+// Two-segment forward (extra_indices NULL: one segment) with an optional
+// output epilogue.
+int fwd_two(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
+            const smla_tensor* indices, const smla_tensor* extra_pool,
+            const smla_tensor* extra_kv_scale, const smla_tensor* extra_indices, float sm_scale,
+            const smla_epilogue* epi, smla_tensor* out, smla_tensor* lse, void* stream,
+            const smla_options* opt) {
   if (!extra_indices)
-    return sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream, opt);
+    return fwd_one(q, kv_pool, kv_scale, indices, sm_scale, epi, out, lse, stream, opt);
   Checked c1, c2;
-  int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c1);
+  int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c1, epi_out_dtype(epi));
   if (s) return s;
   const float* scale2 = nullptr;
   if ((s = validate_extra(q, kv_pool, kv_scale, extra_pool, extra_kv_scale, extra_indices, out, lse,
                           &c2, &scale2)))
     return s;
+  EpiOut eo;
+  const smla_tensor* ins[7] = {q, kv_pool, indices, c1.fp8 ? kv_scale : nullptr, extra_pool,
+                               extra_indices, c1.fp8 ? extra_kv_scale : nullptr};
+  if ((s = validate_epilogue(epi, c1.pb.rows, c1.pb.heads, out, lse, ins, 7, &eo))) return s;
   if (c1.pb.rows == 0) return SMLA_OK;
 
   int dev = 0;
@@ -425,6 +502,7 @@ int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool, const smla
     FwdParams p = segment_params(q, kv_pool,
                                  c1.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
                                  indices, c1, plan1, sm_scale, out, lse);
+    p.epi = eo;
     p.pool2 = static_cast<const uint8_t*>(extra_pool->data);
     p.pool2_rs_bytes = extra_pool->stride[0] * elem_size(extra_pool->dtype);
     p.pool2_bytes = uint32_t(std::min<int64_t>(c2.pb.pool_bytes, kMaxBufferBytes));
@@ -467,9 +545,80 @@ int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool, const smla
   p2.part_lse = part_lse + int64_t(plan1.splits) * per_split;
   FwdParams pc = p1;
   pc.splits = int32_t(S);
+  pc.epi = eo;
   int le = launch_attention(p1, plan1, c1.pb.dqk, c1.fp8, stream);
   if (le == 0) le = launch_attention(p2, plan2, c2.pb.dqk, c2.fp8, stream);
   if (le == 0) le = launch_combine(pc, stream);
+  if (le != 0)
+    return fail(SMLA_ERR_HIP, std::string("kernel launch: ") +
+                                  hipGetErrorString(static_cast<hipError_t>(le)));
+  return SMLA_OK;
+}
+
+}  // namespace
+}  // namespace smla
+
+using namespace smla;
+
+extern "C" {
+
+int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
+                      const smla_tensor* kv_scale, const smla_tensor* indices, float sm_scale,
+                      smla_tensor* out, smla_tensor* lse, void* stream,
+                      const smla_options* opt) {
+  return fwd_one(q, kv_pool, kv_scale, indices, sm_scale, nullptr, out, lse, stream, opt);
+}
+
+int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
+                    const smla_tensor* indices, const smla_tensor* extra_pool,
+                    const smla_tensor* extra_kv_scale, const smla_tensor* extra_indices,
+                    float sm_scale, smla_tensor* out, smla_tensor* lse, void* stream,
+                    const smla_options* opt) {
+  return fwd_two(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices,
+                 sm_scale, nullptr, out, lse, stream, opt);
+}
+
+int sparse_mla_fwd_epi(const smla_tensor* q, const smla_tensor* kv_pool,
+                       const smla_tensor* kv_scale, const smla_tensor* indices,
+                       const smla_tensor* extra_pool, const smla_tensor* extra_kv_scale,
+                       const smla_tensor* extra_indices, float sm_scale,
+                       const smla_epilogue* epi, smla_tensor* out, smla_tensor* lse,
+                       void* stream, const smla_options* opt) {
+  return fwd_two(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices,
+                 sm_scale, epi, out, lse, stream, opt);
+}
+
+int sparse_mla_out_epilogue(const smla_tensor* rows, const smla_epilogue* epi, smla_tensor* out,
+                            void* stream) {
+  int s;
+  if (!epi) return fail(SMLA_ERR_INVALID_ARG, "epi: null");
+  if ((s = check_tensor(rows, "rows", 3, SMLA_BF16))) return s;
+  const int64_t R = rows->shape[0], H = rows->shape[1];
+  if (rows->shape[2] != kDv) return fail(SMLA_ERR_INVALID_ARG, "rows: shape must be [R, H, 512]");
+  const int32_t od = epi_out_dtype(epi);
+  if ((s = check_tensor(out, "out", 3, od))) return s;
+  if (out->shape[0] != R || out->shape[1] != H || out->shape[2] != kDv)
+    return fail(SMLA_ERR_INVALID_ARG, "out: shape must be [R, H, 512]");
+  if (R * H > (int64_t(1) << 31))
+    return fail(SMLA_ERR_UNSUPPORTED, "rows: more than 2^31 rows x heads");
+  if (R * H > 0) {
+    if (!rows->data || !out->data) return fail(SMLA_ERR_INVALID_ARG, "rows/out: null data");
+    if (!aligned16(rows->data) || (rows->stride[0] * 2) % 16 != 0 || (rows->stride[1] * 2) % 16 != 0)
+      return fail(SMLA_ERR_UNSUPPORTED, "rows: base, row and head strides must be 16-byte aligned");
+    const int ob = elem_size(od);
+    if (!aligned16(out->data) || (out->stride[0] * ob) % 16 != 0 || (out->stride[1] * ob) % 16 != 0)
+      return fail(SMLA_ERR_UNSUPPORTED, "out: base, row and head strides must be 16-byte aligned");
+  }
+  EpiPassParams p{};
+  const smla_tensor* ins[1] = {rows};
+  if ((s = validate_epilogue(epi, R, H, out, nullptr, ins, 1, &p.epi))) return s;
+  if (R * H == 0) return SMLA_OK;
+  p.in = static_cast<const uint16_t*>(rows->data);
+  p.in_rs = rows->stride[0];
+  p.in_hs = rows->stride[1];
+  p.rows = R;
+  p.heads = int32_t(H);
+  const int le = launch_out_epilogue(p, stream);
   if (le != 0)
     return fail(SMLA_ERR_HIP, std::string("kernel launch: ") +
                                   hipGetErrorString(static_cast<hipError_t>(le)));

@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "epilogue.h"
 #include "launch.h"
 #include "work_order.h"
 
@@ -60,7 +61,8 @@ constexpr float kLazyMax = 8.0f;    // log2-domain slack before the reference ma
 constexpr uint32_t kOutOfRange = 0xFFFFF000u;  // buffer offset of an invalid slot's row
 constexpr int kBufferWord3 = 0x00020000;       // raw buffer descriptor word 3 (gfx9 family)
 
-template <int DQK>
+// EPI: the final store goes through the output epilogue (epilogue.h).
+template <int DQK, bool EPI>
 __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdParams p) {
   constexpr int NCH = DQK / 16;  // 16-byte fp8 chunks per row
   constexpr int NI = NCH / 4;    // chunks per lane per step
@@ -314,8 +316,11 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
       s1 += *reinterpret_cast<const floatx4*>(src + 4);
     }
     const int h = h0 + head;
-    if (h < p.heads) {
-      if (!split_mode) {
+    if (h < p.heads) {  // uniform over the wave: one head per wave
+      if (EPI && !split_mode) {
+        float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        epi_store<8>(p.epi, r, h, col, v);
+      } else if (!split_mode) {
         *reinterpret_cast<u32x4*>(p.out + r * p.out_rs + int64_t(h) * p.out_hs + col) =
             u32x4{pack2_bf16(s0.x, s0.y), pack2_bf16(s0.z, s0.w), pack2_bf16(s1.x, s1.y),
                   pack2_bf16(s1.z, s1.w)};
@@ -360,10 +365,16 @@ KernelShape decode_shape(int dqk) {
 
 int launch_decode(const FwdParams& p, int dqk, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (dqk == 576)
-    hipLaunchKernelGGL(decode_kernel<576>, dim3(uint32_t(p.grid)), dim3(kDecWaves * 64), 0, st, p);
+  const dim3 grid(uint32_t(p.grid)), block(kDecWaves * 64);
+  const bool epi = epi_active(p.epi) && p.part_o == nullptr;
+  if (dqk == 576 && !epi)
+    hipLaunchKernelGGL((decode_kernel<576, false>), grid, block, 0, st, p);
+  else if (dqk == 576)
+    hipLaunchKernelGGL((decode_kernel<576, true>), grid, block, 0, st, p);
+  else if (dqk == 512 && !epi)
+    hipLaunchKernelGGL((decode_kernel<512, false>), grid, block, 0, st, p);
   else if (dqk == 512)
-    hipLaunchKernelGGL(decode_kernel<512>, dim3(uint32_t(p.grid)), dim3(kDecWaves * 64), 0, st, p);
+    hipLaunchKernelGGL((decode_kernel<512, true>), grid, block, 0, st, p);
   else
     return int(hipErrorInvalidValue);
   return int(hipGetLastError());

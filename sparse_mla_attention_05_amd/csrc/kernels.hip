@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "epilogue.h"
 #include "launch.h"
 #include "work_order.h"
 
@@ -75,7 +76,7 @@ struct Cfg {
 // One workgroup: (row, block of HB = 16*NHG heads, split). NW waves, TK-slot
 // tiles. DBUF keeps two tiles of gathers in flight (two register buffers,
 // the tile loop unrolled by two); otherwise one.
-template <int NHG, int NW, int TK_, bool DBUF, int DQK, bool FP8>
+template <int NHG, int NW, int TK_, bool DBUF, int DQK, bool FP8, bool EPI>
 __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   using C = Cfg<NHG, NW, TK_, DQK, FP8>;
   constexpr int HB = C::HB, TK = C::TK, PITCH = C::PITCH, PP = C::PP;
@@ -317,6 +318,8 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   __syncthreads();
 
   const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
+  const bool epi = EPI && !split_mode;
+  uint16_t* const eblk = kt;  // every wave is past its last tile read
 #pragma unroll
   for (int a = 0; a < NHG; ++a) {
 #pragma unroll
@@ -328,7 +331,11 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
       for (int k2 = 0; k2 < NKG; ++k2) lt += red[k2 * HB + head];
       const float inv = lt > 0.f ? out_scale / lt : 0.f;
       if (h < p.heads) {
-        if (!split_mode) {
+        if (epi) {  // bf16 row block in LDS, stored through the epilogue below
+          uint16_t* op = eblk + head * kEpiPitch + wave * C::DW + l16;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) op[b * 16] = uint16_t(bf16_rne(o[a][b][i] * inv));
+        } else if (!split_mode) {
           uint16_t* op = p.out + r * p.out_rs + int64_t(h) * p.out_hs + wave * C::DW + l16;
 #pragma unroll
           for (int b = 0; b < NB; ++b) op[b * 16] = uint16_t(bf16_rne(o[a][b][i] * inv));
@@ -340,6 +347,11 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
         }
       }
     }
+  }
+  if (epi) {
+    static_assert(HB * kEpiPitch <= TK * PITCH, "epilogue block fits the tile");
+    __syncthreads();
+    epi_store_lds_block(p.epi, eblk, eblk + 32 * kEpiPitch, 32, HB, r, h0, p.heads, tid, C::NT);
   }
   if (tid < HB) {
     const int h = h0 + tid;
@@ -359,6 +371,9 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
 // Split combine: one 128-thread workgroup per (row, head), 4 columns per
 // thread. lse = M + ln sum_s e^(lse_s - M), out = sum_s e^(lse_s - lse) O_s,
 // splits with lse_s = -inf weigh 0, all -inf gives out = 0 and lse = -inf.
+// EPI: the final store goes through the output epilogue (epilogue.h); each
+// thread holds 4 columns and 8 consecutive threads one 32-column block.
+template <bool EPI>
 __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
   const int64_t rh = blockIdx.x;
   const int64_t r = rh / p.heads;
@@ -370,7 +385,12 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
   for (int s = 0; s < p.splits; ++s) m = fmaxf(m, pl[s * stride_s]);
   uint16_t* op = p.out + r * p.out_rs + int64_t(h) * p.out_hs + 4 * tid;
   if (m == kNegInf) {
-    *reinterpret_cast<u32x2*>(op) = u32x2{0u, 0u};
+    if constexpr (EPI) {
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      epi_store<4>(p.epi, r, h, 4 * tid, v);
+    } else {
+      *reinterpret_cast<u32x2*>(op) = u32x2{0u, 0u};
+    }
     if (tid == 0) p.lse[r * p.lse_rs + int64_t(h) * p.lse_hs] = kNegInf;
     return;
   }
@@ -385,8 +405,13 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
     acc += w * *reinterpret_cast<const floatx4*>(po + s * stride_s * kDv);
   }
   const float inv = 1.0f / tot;
-  *reinterpret_cast<u32x2*>(op) =
-      u32x2{pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv)};
+  if constexpr (EPI) {
+    float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    epi_store<4>(p.epi, r, h, 4 * tid, v);
+  } else {
+    *reinterpret_cast<u32x2*>(op) =
+        u32x2{pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv)};
+  }
   if (tid == 0) p.lse[r * p.lse_rs + int64_t(h) * p.lse_hs] = m + __logf(tot);
 }
 
@@ -415,8 +440,13 @@ template <bool FP8, int V> struct InstFor<64, FP8, V> : Inst<4, 8, 64, false> {}
 template <int HB, int V, int DQK, bool FP8>
 hipError_t launch_inst(const FwdParams& p, hipStream_t st) {
   using I = InstFor<HB, FP8, V>;
-  hipLaunchKernelGGL((fwd_kernel<I::kNHG, I::kNW, I::kTK, I::kDBUF, DQK, FP8>),
-                     dim3(uint32_t(p.grid)), dim3(I::kNW * 64), 0, st, p);
+  const dim3 grid(uint32_t(p.grid)), block(I::kNW * 64);
+  if (epi_active(p.epi) && p.part_o == nullptr)
+    hipLaunchKernelGGL((fwd_kernel<I::kNHG, I::kNW, I::kTK, I::kDBUF, DQK, FP8, true>), grid,
+                       block, 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<I::kNHG, I::kNW, I::kTK, I::kDBUF, DQK, FP8, false>), grid,
+                       block, 0, st, p);
   return hipGetLastError();
 }
 
@@ -480,7 +510,11 @@ int launch_attention(const FwdParams& p, const smla_plan& plan, int dqk, bool fp
 
 int launch_combine(const FwdParams& p, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(combine_kernel, dim3(uint32_t(p.rows * p.heads)), dim3(128), 0, st, p);
+  const dim3 grid(uint32_t(p.rows * p.heads)), block(128);
+  if (epi_active(p.epi))
+    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, st, p);
   return int(hipGetLastError());
 }
 

@@ -12,6 +12,23 @@ constexpr int kMaxSplits = 64;
 constexpr int kMaxHeads = 1024;
 constexpr int64_t kMaxTopk = int64_t(1) << 20;
 
+// Where and how the output epilogue stores (epilogue.h): the inverse RoPE of
+// columns 448..511 when pos is set, and an MXFP8 store (codes in q8, E8M0
+// scales in sc) when q8 is set, else a bf16 store to out.
+struct EpiOut {
+  uint16_t* out;            // bf16 [R, H, 512] (q8 == nullptr)
+  uint8_t* q8;              // e4m3fn codes [R, H, 512], or nullptr
+  int64_t out_rs, out_hs;   // strides of out or q8
+  uint8_t* sc;              // E8M0 codes [R, H, 16]
+  int64_t sc_rs, sc_hs;
+  const int32_t* pos;       // int32 [R] position of each row, or nullptr
+  const float* cs;          // fp32 [cs_rows, 64]: cos of the 32 pair angles, then sin
+  int64_t cs_rs;
+  int32_t cs_rows;
+};
+
+inline bool epi_active(const EpiOut& e) { return e.pos != nullptr || e.q8 != nullptr; }
+
 // Everything the attention kernel reads, with strides in elements except
 // where named "_bytes".
 struct FwdParams {
@@ -49,7 +66,20 @@ struct FwdParams {
   const int32_t* idx2;
   int64_t idx2_rs;
   int32_t topk2;
+  // Output epilogue of the final store (the attention kernel's without
+  // splits, the combine kernel's with them); inactive: plain bf16 to out.
+  EpiOut epi;
 };
+
+// The output epilogue as a pass of its own over bf16 rows [rows, heads, 512].
+struct EpiPassParams {
+  const uint16_t* in;
+  int64_t in_rs, in_hs;
+  int64_t rows;
+  int32_t heads;
+  EpiOut epi;
+};
+int launch_out_epilogue(const EpiPassParams& p, void* stream);
 
 struct Problem {
   int64_t rows;

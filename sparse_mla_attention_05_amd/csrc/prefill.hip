@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "epilogue.h"
 #include "launch.h"
 #include "work_order.h"
 
@@ -66,7 +67,8 @@ struct PreCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-template <int DQK, bool FP8>
+// EPI: the final store goes through the output epilogue (epilogue.h).
+template <int DQK, bool FP8, bool EPI>
 __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdParams p) {
   using C = PreCfg<DQK, FP8>;
   constexpr int HB = C::HB, NHG = C::NHG, NKG = C::NKG, BPW = C::BPW, TK = C::TK;
@@ -329,6 +331,8 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   if (kg == 0 && g == 0) mfin_s[hg * 16 + l16] = m_ref;
   __syncthreads();
   const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
+  const bool epi = EPI && !split_mode;
+  uint16_t* const eblk = &kt[0][0];  // every wave is past its last tile read
 #pragma unroll
   for (int a = 0; a < NHG; ++a) {
 #pragma unroll
@@ -340,7 +344,11 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
       for (int k2 = 0; k2 < NKG; ++k2) lt += red[k2 * HB + head];
       const float inv = lt > 0.f ? out_scale / lt : 0.f;
       if (h < p.heads) {
-        if (!split_mode) {
+        if (epi) {  // bf16 row block in LDS, stored through the epilogue below
+          uint16_t* op = eblk + head * kEpiPitch + wave * C::DW + l16;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) op[b * 16] = uint16_t(bf16_rne(o[a][b][i] * inv));
+        } else if (!split_mode) {
           uint16_t* op = p.out + r * p.out_rs + int64_t(h) * p.out_hs + wave * C::DW + l16;
 #pragma unroll
           for (int b = 0; b < NB; ++b) op[b * 16] = uint16_t(bf16_rne(o[a][b][i] * inv));
@@ -352,6 +360,11 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
         }
       }
     }
+  }
+  if (epi) {
+    static_assert(HB * kEpiPitch <= TK * PITCH, "epilogue block fits the tile");
+    __syncthreads();
+    epi_store_lds_block(p.epi, eblk, eblk + 32 * kEpiPitch, 32, HB, r, h0, p.heads, tid, C::NT);
   }
   if (tid < HB) {
     const int h = h0 + tid;
@@ -383,19 +396,25 @@ KernelShape prefill_shape(int dqk, bool fp8) {
   return k;
 }
 
-int launch_prefill(const FwdParams& p, int dqk, bool fp8, void* stream) {
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+template <bool EPI>
+static int launch_prefill_inst(const FwdParams& p, int dqk, bool fp8, hipStream_t st) {
   const dim3 grid(uint32_t(p.grid)), block(kPreWaves * 64);
   if (dqk == 576) {
-    if (fp8) hipLaunchKernelGGL((prefill_kernel<576, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((prefill_kernel<576, false>), grid, block, 0, st, p);
+    if (fp8) hipLaunchKernelGGL((prefill_kernel<576, true, EPI>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_kernel<576, false, EPI>), grid, block, 0, st, p);
   } else if (dqk == 512) {
-    if (fp8) hipLaunchKernelGGL((prefill_kernel<512, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((prefill_kernel<512, false>), grid, block, 0, st, p);
+    if (fp8) hipLaunchKernelGGL((prefill_kernel<512, true, EPI>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((prefill_kernel<512, false, EPI>), grid, block, 0, st, p);
   } else {
     return int(hipErrorInvalidValue);
   }
   return int(hipGetLastError());
+}
+
+int launch_prefill(const FwdParams& p, int dqk, bool fp8, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (epi_active(p.epi) && p.part_o == nullptr) return launch_prefill_inst<true>(p, dqk, fp8, st);
+  return launch_prefill_inst<false>(p, dqk, fp8, st);
 }
 
 }  // namespace smla

@@ -46,6 +46,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "epilogue.h"
 #include "launch.h"
 #include "work_order.h"
 
@@ -90,7 +91,8 @@ __device__ __forceinline__ int tile_perm(int r) {
   return ((r & 1) * 3) | (((r ^ (r >> 1)) & 1) << 2) | (((r >> 2) & 1) << 3);
 }
 
-template <int DQK>
+// EPI: the final store goes through the output epilogue (epilogue.h).
+template <int DQK, bool EPI>
 __global__ void __launch_bounds__(kXWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 prefill_fp8_kernel(const FwdParams p) {
   using C = XCfg<DQK>;
@@ -481,16 +483,26 @@ prefill_fp8_kernel(const FwdParams p) {
     const int h = h0 + 16 * hb + l16;
     if (h >= p.heads) continue;
     const float inv = lt[hb] > 0.f ? kv_scale / lt[hb] : 0.f;
+    if (EPI && !split_mode) {
+      // 32-column blocks: d = 2m and 2m + 1 of the four lanes g of a head
 #pragma unroll
-    for (int d = 0; d < NDW; ++d) {
-      const floatx4 res = o[d][hb] * inv;
-      const int col = 256 * kh + 16 * d + 4 * g;
-      if (!split_mode) {
-        *reinterpret_cast<u32x2*>(p.out + r * p.out_rs + int64_t(h) * p.out_hs + col) =
-            u32x2{pack_bf16(res[0], res[1]), pack_bf16(res[2], res[3])};
-      } else {
-        *reinterpret_cast<floatx4*>(
-            p.part_o + ((int64_t(split) * p.rows + r) * p.heads + h) * kDv + col) = res;
+      for (int m = 0; m < NDW / 2; ++m) {
+        const floatx4 ra = o[2 * m][hb] * inv, rb = o[2 * m + 1][hb] * inv;
+        float va[4] = {ra[0], ra[1], ra[2], ra[3]}, vb[4] = {rb[0], rb[1], rb[2], rb[3]};
+        epi_store_c16x2(p.epi, r, h, 256 * kh + 32 * m + 4 * g, va, vb);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < NDW; ++d) {
+        const floatx4 res = o[d][hb] * inv;
+        const int col = 256 * kh + 16 * d + 4 * g;
+        if (!split_mode) {
+          *reinterpret_cast<u32x2*>(p.out + r * p.out_rs + int64_t(h) * p.out_hs + col) =
+              u32x2{pack_bf16(res[0], res[1]), pack_bf16(res[2], res[3])};
+        } else {
+          *reinterpret_cast<floatx4*>(
+              p.part_o + ((int64_t(split) * p.rows + r) * p.heads + h) * kDv + col) = res;
+        }
       }
     }
     if (kh == 0 && g == 0) {
@@ -520,11 +532,16 @@ KernelShape prefill_fp8_shape(int dqk) {
 
 int launch_prefill_fp8(const FwdParams& p, int dqk, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool epi = epi_active(p.epi) && p.part_o == nullptr;
   const dim3 grid(uint32_t(p.grid)), block(kXWaves * 64);
-  if (dqk == 576)
-    hipLaunchKernelGGL((prefill_fp8_kernel<576>), grid, block, 0, st, p);
+  if (dqk == 576 && epi)
+    hipLaunchKernelGGL((prefill_fp8_kernel<576, true>), grid, block, 0, st, p);
+  else if (dqk == 576)
+    hipLaunchKernelGGL((prefill_fp8_kernel<576, false>), grid, block, 0, st, p);
+  else if (dqk == 512 && epi)
+    hipLaunchKernelGGL((prefill_fp8_kernel<512, true>), grid, block, 0, st, p);
   else if (dqk == 512)
-    hipLaunchKernelGGL((prefill_fp8_kernel<512>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((prefill_fp8_kernel<512, false>), grid, block, 0, st, p);
   else
     return int(hipErrorInvalidValue);
   return int(hipGetLastError());

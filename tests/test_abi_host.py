@@ -235,3 +235,82 @@ def test_plan2_workspace_covers_both_segments(H, K1, K2, dtype):
         S = p1["splits"] + p2["splits"]
     o_bytes = S * R * H * 512 * 4
     assert ws == ((o_bytes + 255) // 256 * 256 + S * R * H * 4 if S else 0)
+
+
+# ------------------------------------------------------------ output epilogue
+
+def _epi_args(R=4, H=16, mx=True, rope=True):
+    a = _args(R=R, H=H)
+    if mx:
+        a["out"] = torch.zeros(R, H, 512, dtype=torch.float8_e4m3fn)
+        a["out_scale"] = torch.zeros(R, H, 16, dtype=torch.uint8).view(torch.float8_e8m0fnu)
+    else:
+        a["out_scale"] = None
+    a["rope_positions"] = torch.zeros(R, dtype=torch.int32) if rope else None
+    a["rope_cos_sin"] = torch.zeros(64, 64, dtype=torch.float32) if rope else None
+    return a
+
+
+def _status_epi(a):
+    return _lib.status_of_fwd_epi(a["q"], a["kv_pool"], a["kv_scale"], a["indices"], a["sm_scale"],
+                                  a["out"], a["lse"], a["rope_positions"], a["rope_cos_sin"],
+                                  a["out_scale"])
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: a.update(out=torch.zeros(4, 16, 512, dtype=torch.bfloat16)), UNSUP),   # MXFP8 needs fp8 codes
+    (lambda a: a.update(out_scale=torch.zeros(4, 16, 8, dtype=torch.uint8).view(torch.float8_e8m0fnu)), INVALID),
+    (lambda a: a.update(out_scale=torch.zeros(4, 16, 16, dtype=torch.uint8)), UNSUP),  # not E8M0
+    (lambda a: a.update(rope_positions=torch.zeros(5, dtype=torch.int32)), INVALID),
+    (lambda a: a.update(rope_positions=torch.zeros(4, dtype=torch.int64)), UNSUP),
+    (lambda a: a.update(rope_cos_sin=None), INVALID),                                 # positions alone
+    (lambda a: a.update(rope_positions=None), INVALID),                               # cache alone
+    (lambda a: a.update(rope_cos_sin=torch.zeros(64, 32, dtype=torch.float32)), UNSUP),
+    (lambda a: a.update(rope_cos_sin=torch.zeros(0, 64, dtype=torch.float32)), INVALID),
+    (lambda a: a.update(rope_cos_sin=torch.zeros(64, 64, dtype=torch.bfloat16)), UNSUP),
+    (lambda a: a.update(out_scale=torch.zeros(4, 16, 32, dtype=torch.uint8).view(torch.float8_e8m0fnu)[:, :, ::2]), UNSUP),
+    (lambda a: a.update(out=torch.zeros(4, 16, 520, dtype=torch.float8_e4m3fn)[:, :, :512]), UNSUP),  # 520-B row
+])
+def test_epilogue_validation(mutate, expected):
+    a = _epi_args()
+    mutate(a)
+    assert _status_epi(a) == expected, _lib.last_error()
+    assert _lib.last_error()
+
+
+def test_epilogue_outputs_must_not_alias():
+    a = _epi_args()
+    buf = torch.zeros(4 * 16 * 512 + 4 * 16 * 16, dtype=torch.uint8)
+    a["out"] = buf[:4 * 16 * 512].view(4, 16, 512).view(torch.float8_e4m3fn)
+    a["out_scale"] = buf[:4 * 16 * 16].view(4, 16, 16).view(torch.float8_e8m0fnu)  # overlaps out
+    assert _status_epi(a) == INVALID
+    a = _epi_args()
+    a["rope_cos_sin"] = a["lse"].view(-1)[:64].view(1, 64)                             # lse aliases cache
+    assert _status_epi(a) == INVALID
+
+
+def test_epilogue_zero_rows_is_a_noop():
+    for mx in (True, False):
+        a = _epi_args(R=0, mx=mx)
+        assert _status_epi(a) == _lib.SMLA_OK, _lib.last_error()
+    rows = torch.zeros(0, 16, 512, dtype=torch.bfloat16)
+    out = torch.zeros(0, 16, 512, dtype=torch.float8_e4m3fn)
+    sc = torch.zeros(0, 16, 16, dtype=torch.uint8).view(torch.float8_e8m0fnu)
+    assert _lib.status_of_out_epilogue(rows, out, out_scale=sc) == _lib.SMLA_OK
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda r, o, k: k.update(out_scale=None), UNSUP),                              # fp8 out without scales
+    (lambda r, o, k: k.update(rope_positions=torch.zeros(3, dtype=torch.int32)), INVALID),
+    (lambda r, o, k: r.__setitem__(0, torch.zeros(4, 16, 256, dtype=torch.bfloat16)), INVALID),
+    (lambda r, o, k: r.__setitem__(0, torch.zeros(4, 16, 512, dtype=torch.float32)), UNSUP),
+    (lambda r, o, k: o.__setitem__(0, torch.zeros(4, 8, 512, dtype=torch.float8_e4m3fn)), INVALID),
+])
+def test_out_epilogue_pass_validation(mutate, expected):
+    rows = [torch.zeros(4, 16, 512, dtype=torch.bfloat16)]
+    out = [torch.zeros(4, 16, 512, dtype=torch.float8_e4m3fn)]
+    kw = dict(rope_positions=torch.zeros(4, dtype=torch.int32),
+              rope_cos_sin=torch.zeros(8, 64, dtype=torch.float32),
+              out_scale=torch.zeros(4, 16, 16, dtype=torch.uint8).view(torch.float8_e8m0fnu))
+    mutate(rows, out, kw)
+    assert _lib.status_of_out_epilogue(rows[0], out[0], **kw) == expected, _lib.last_error()
