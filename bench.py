@@ -17,7 +17,10 @@ decode shape the HBM-roofline target is set on). The two 64-head prefill
 workloads are timed too and reported under "prefill" with their MFMA fraction,
 and the two decode workloads again as two-segment calls (a seeded 128-slot
 sliding window over a second pool with its own scale, next to the same
-workload's one-segment time) under "two_segment".
+workload's one-segment time) under "two_segment", and with the output
+epilogue (inverse RoPE of the last 64 columns and an MXFP8 store) fused into
+the forward's store, next to the plain forward followed by the separate
+epilogue pass, under "epilogue".
 """
 
 from __future__ import annotations
@@ -63,6 +66,8 @@ def parse():
                     help="comma list of workloads also timed with a sliding-window second "
                          "segment ('' for none)")
     ap.add_argument("--window", type=int, default=128, help="slots of that second segment")
+    ap.add_argument("--epilogue", default="decode_bf16,decode_fp8",
+                    help="workloads also timed with the fused inverse-RoPE + MXFP8 store")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
@@ -123,12 +128,16 @@ def traffic_from_profiles(kernel_src, workload):
         return None
 
 
-def time_workload(name, steps, warmup, cold, window=0):
+def time_workload(name, steps, warmup, cold, window=0, epi=None):
     """Time one workload; with `window` > 0 as a two-segment call whose second
-    segment is a seeded sliding window of that many slots over its own pool."""
+    segment is a seeded sliding window of that many slots over its own pool;
+    with epi = "fused" the forward's store applies the inverse RoPE and the
+    MXFP8 store, with epi = "unfused" the plain forward is followed by the
+    separate epilogue pass."""
     import torch
     from sparse_mla_attention_05_amd import _lib
-    from sparse_mla_attention_05_amd.inputs import make_extra_segment, make_inputs
+    from sparse_mla_attention_05_amd.inputs import (make_epilogue_inputs, make_extra_segment,
+                                                    make_inputs)
 
     inp = make_inputs(name)
     dev = torch.device("cuda:0")
@@ -150,6 +159,22 @@ def time_workload(name, steps, warmup, cold, window=0):
         def call():
             _lib.sparse_mla_fwd2(q, pool, scale, idx, xpool, xscale, xidx, inp.sm_scale, out, lse,
                                  stream=stream)
+    elif epi is not None:
+        plan = _lib.sparse_mla_plan(q, pool, idx)
+        e = make_epilogue_inputs(R, seed=inp.workload.seed)
+        pos, cs = e.positions.to(dev), e.cos_sin.to(dev)
+        codes = torch.empty((R, H, 512), dtype=torch.float8_e4m3fn, device=dev)
+        scales = torch.empty((R, H, 16), dtype=torch.float8_e8m0fnu, device=dev)
+        if epi == "fused":
+            def call():
+                _lib.sparse_mla_fwd_epi(q, pool, scale, idx, inp.sm_scale, codes, lse,
+                                        rope_positions=pos, rope_cos_sin=cs, out_scale=scales,
+                                        stream=stream)
+        else:
+            def call():
+                _lib.sparse_mla_fwd(q, pool, scale, idx, inp.sm_scale, out, lse, stream=stream)
+                _lib.sparse_mla_out_epilogue(out, codes, rope_positions=pos, rope_cos_sin=cs,
+                                             out_scale=scales, stream=stream)
     else:
         plan = _lib.sparse_mla_plan(q, pool, idx)
 
@@ -314,6 +339,20 @@ def main():
         del r, one
     if two:
         line["two_segment"] = two
+    epis = []
+    for name in [s for s in args.epilogue.split(",") if s]:
+        res = {m: time_workload(name, args.steps, 3, cold, epi=m)
+               for m in ("fused", "unfused", None)}
+        us_ = {m: statistics.median(r["times"]) for m, r in res.items()}
+        epis.append({"workload": name, "epilogue": "inverse RoPE (64 columns) + MXFP8 store",
+                     "us_fused": round(us_["fused"], 1), "us_unfused": round(us_["unfused"], 1),
+                     "us_plain_bf16": round(us_[None], 1),
+                     "fused_vs_unfused": round(us_["fused"] / us_["unfused"] - 1.0, 4),
+                     "warm_us_fused": round(res["fused"]["warm_us"], 1),
+                     "warm_us_unfused": round(res["unfused"]["warm_us"], 1)})
+        del res
+    if epis:
+        line["epilogue"] = epis
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head["inp"], args.cpu_seconds)
     print(json.dumps(line), flush=True)

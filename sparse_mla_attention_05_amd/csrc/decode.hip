@@ -84,6 +84,15 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
   work /= p.head_blocks;
   const int split = int(work % p.splits);
   const int64_t r = work / p.splits;
+  // Output epilogue: this row's cos/sin row, read now so that the two
+  // dependent reads (position, then cache) overlap the walk; one wave keeps
+  // it in a register until the epilogue copies it to LDS.
+  __shared__ float epi_cs[64];
+  float cs_pre = 0.f;
+  if constexpr (EPI) {
+    if (p.epi.pos != nullptr && tid < 64) cs_pre = epi_cs_row(p.epi, r)[tid];
+  }
+
   const int h0 = hb * 16;
 
   // Q^T fragments in the gather's column order.
@@ -277,6 +286,9 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
     red_m[wave * 16 + l16] = m_ref;
     red_l[wave * 16 + l16] = l_head;
   }
+  if constexpr (EPI) {
+    if (tid < 64) epi_cs[tid] = cs_pre;
+  }
   __syncthreads();  // also: every wave is done with its V staging area
 
   float* part = reinterpret_cast<float*>(smem) + wave * (kOWave / 4);
@@ -319,7 +331,7 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
     if (h < p.heads) {  // uniform over the wave: one head per wave
       if (EPI && !split_mode) {
         float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        epi_store<8>(p.epi, r, h, col, v);
+        epi_store<8>(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, r, h, col, v);
       } else if (!split_mode) {
         *reinterpret_cast<u32x4*>(p.out + r * p.out_rs + int64_t(h) * p.out_hs + col) =
             u32x4{pack2_bf16(s0.x, s0.y), pack2_bf16(s0.z, s0.w), pack2_bf16(s1.x, s1.y),

@@ -10,7 +10,8 @@
 // row of a position holds cos of the 32 pair angles, then their sines. The
 // scale of a 32-column block is 2^(floor(log2 amax) - 8) (the OCP MX v1.0
 // conversion for e4m3), clamped to 2^-127 for tiny or zero blocks; elements
-// are rounded to nearest even and saturated at 448.
+// are divided by it exactly (a power of two), rounded to nearest even and
+// saturated at 448.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,21 +24,17 @@ namespace smla {
 constexpr int kRopeStart = kDv - 64;  // first rotated column
 constexpr int kEpiPitch = kDv + 8;    // bf16 per row of an LDS output block (1040 B)
 
-// float8_e4m3fn code of x: nearest even, magnitudes from 448 up saturate to
-// 448 (0x7E), the sign bit of x kept (so a negative value that rounds to zero
-// gives 0x80). Normal range: the fp32 exponent field and top three mantissa
-// bits, rounded at bit 20, rebased from bias 127 to bias 7; below 2^-6 the
-// e4m3 values are the multiples of 2^-9 and x * 2^9 is exact.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t ua = u & 0x7FFFFFFFu;
-  const float a = __uint_as_float(ua);
-  const uint32_t rnd = ua + 0x7FFFFu + ((ua >> 20) & 1u);
-  uint32_t code = (rnd >> 20) - (120u << 3);
-  if (a < 0x1p-6f) code = uint32_t(__builtin_rintf(a * 512.f));
-  if (a >= 448.f) code = 0x7Eu;
-  return sign | code;
+// Four values, already divided by their block scale, to four float8_e4m3fn
+// codes in one dword (the first value in the low byte). The gfx950
+// conversion (scale operand 1) rounds to nearest even and keeps the sign of
+// a value that rounds to zero; the clamp to +-448 first makes the
+// saturation explicit.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const auto sat = [](float x) { return __builtin_amdgcn_fmed3f(x, -448.f, 448.f); };
+  const s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, sat(a), sat(b), 1.0f, false);
+  const s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(c), sat(d), 1.0f, true);
+  return __builtin_bit_cast(uint32_t, w);
 }
 
 // Inverse rotation of the pairs among N consecutive columns starting at an
@@ -54,18 +51,31 @@ __device__ __forceinline__ void inverse_rope_pairs(float (&v)[N], const float* c
   }
 }
 
+// Row of the cos/sin cache at row r's position (clamped into the cache), or
+// nullptr when the epilogue does not rotate. Kernels load it early (the
+// position read and the cache read are two dependent round trips) and hand
+// the epilogue a copy in LDS.
+__device__ __forceinline__ const float* epi_cs_row(const EpiOut& e, int64_t r) {
+  if (e.pos == nullptr) return nullptr;
+  int pos = e.pos[r];
+  pos = pos < 0 ? 0 : (pos >= e.cs_rows ? e.cs_rows - 1 : pos);
+  return e.cs + int64_t(pos) * e.cs_rs;
+}
+
 // First half of a store through the epilogue: the bf16 rounding of N
-// consecutive columns [col0, col0 + N) of row r (col0 even), then the
-// inverse rotation where they fall in the rotated range.
+// consecutive columns [col0, col0 + N) (col0 even), then the inverse
+// rotation where they fall in the rotated range; cs_row is the row's
+// cos/sin (global or LDS), nullptr for no rotation.
 template <int N>
-__device__ __forceinline__ void epi_prepare(const EpiOut& e, int64_t r, int col0, float (&v)[N]) {
+__device__ __forceinline__ void epi_prepare(const float* cs_row, int col0, float (&v)[N]) {
 #pragma unroll
-  for (int k = 0; k < N; ++k) v[k] = __uint_as_float(bf16_rne(v[k]) << 16);
-  if (e.pos != nullptr && col0 >= kRopeStart) {
-    int pos = e.pos[r];
-    pos = pos < 0 ? 0 : (pos >= e.cs_rows ? e.cs_rows - 1 : pos);
-    inverse_rope_pairs<N>(v, e.cs + int64_t(pos) * e.cs_rs + ((col0 - kRopeStart) >> 1));
+  for (int k = 0; k < N; k += 2) {
+    const uint32_t w = pack2_bf16(v[k], v[k + 1]);  // round to nearest even, two at once
+    v[k] = __uint_as_float(w << 16);
+    v[k + 1] = __uint_as_float(w & 0xFFFF0000u);
   }
+  if (cs_row != nullptr && col0 >= kRopeStart)
+    inverse_rope_pairs<N>(v, cs_row + ((col0 - kRopeStart) >> 1));
 }
 
 template <int N>
@@ -95,7 +105,7 @@ __device__ __forceinline__ void epi_emit(const EpiOut& e, int64_t r, int h, int 
   if (e.q8 == nullptr) {
     uint32_t w[N / 2];
 #pragma unroll
-    for (int k = 0; k < N / 2; ++k) w[k] = bf16_rne(v[2 * k]) | (bf16_rne(v[2 * k + 1]) << 16);
+    for (int k = 0; k < N / 2; ++k) w[k] = pack2_bf16(v[2 * k], v[2 * k + 1]);
     if constexpr (N == 4) {
       *reinterpret_cast<u32x2*>(e.out + off) = u32x2{w[0], w[1]};
     } else {
@@ -109,8 +119,7 @@ __device__ __forceinline__ void epi_emit(const EpiOut& e, int64_t r, int h, int 
   uint32_t w[N / 4];
 #pragma unroll
   for (int k = 0; k < N / 4; ++k)
-    w[k] = e4m3_rne_sat(v[4 * k] * inv) | (e4m3_rne_sat(v[4 * k + 1] * inv) << 8) |
-           (e4m3_rne_sat(v[4 * k + 2] * inv) << 16) | (e4m3_rne_sat(v[4 * k + 3] * inv) << 24);
+    w[k] = e4m3x4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
   if constexpr (N == 4) {
     *reinterpret_cast<uint32_t*>(e.q8 + off) = w[0];
   } else if constexpr (N == 8) {
@@ -125,14 +134,14 @@ __device__ __forceinline__ void epi_emit(const EpiOut& e, int64_t r, int h, int 
 }
 
 // Stores N consecutive output columns [col0, col0 + N) of row r, head h
-// through the epilogue. The 32-column scale group of an MXFP8 store spans
+// through the epilogue (cs_row as for epi_prepare). The 32-column scale group of an MXFP8 store spans
 // 32 / N consecutive lanes, which must all make this call together (N = 32:
 // one lane). v holds the values before the bf16 rounding.
 template <int N>
-__device__ __forceinline__ void epi_store(const EpiOut& e, int64_t r, int h, int col0,
-                                          float (&v)[N]) {
+__device__ __forceinline__ void epi_store(const EpiOut& e, const float* cs_row, int64_t r, int h,
+                                          int col0, float (&v)[N]) {
   static_assert(N == 4 || N == 8 || N == 32, "columns per lane");
-  epi_prepare<N>(e, r, col0, v);
+  epi_prepare<N>(cs_row, col0, v);
   uint32_t sc = 0u;
   float inv = 1.f;
   if (e.q8 != nullptr) {
@@ -148,10 +157,10 @@ __device__ __forceinline__ void epi_store(const EpiOut& e, int64_t r, int h, int
 // consecutive columns at col_a = 32m + 4g and 4 more at col_a + 16 (g = lane
 // bits 4..5): the 32-column block [32m, 32m + 32) is spread over the four
 // lanes with equal bits 0..3, which must all make this call together.
-__device__ __forceinline__ void epi_store_c16x2(const EpiOut& e, int64_t r, int h, int col_a,
-                                                float (&va)[4], float (&vb)[4]) {
-  epi_prepare<4>(e, r, col_a, va);
-  epi_prepare<4>(e, r, col_a + 16, vb);
+__device__ __forceinline__ void epi_store_c16x2(const EpiOut& e, const float* cs_row, int64_t r,
+                                                int h, int col_a, float (&va)[4], float (&vb)[4]) {
+  epi_prepare<4>(cs_row, col_a, va);
+  epi_prepare<4>(cs_row, col_a + 16, vb);
   uint32_t sc = 0u;
   float inv = 1.f;
   if (e.q8 != nullptr) {
@@ -169,7 +178,8 @@ __device__ __forceinline__ void epi_store_c16x2(const EpiOut& e, int64_t r, int 
 // at hi + (i - split) * kEpiPitch. Thread tid of nt stores 32-column pieces
 // through the epilogue, heads h0 .. h0 + nh - 1 below `heads` only. The
 // caller has made the block visible (barrier).
-__device__ __forceinline__ void epi_store_lds_block(const EpiOut& e, const uint16_t* lo,
+__device__ __forceinline__ void epi_store_lds_block(const EpiOut& e, const float* cs_row,
+                                                    const uint16_t* lo,
                                                     const uint16_t* hi, int split, int nh,
                                                     int64_t r, int h0, int heads, int tid,
                                                     int nt) {
@@ -188,7 +198,7 @@ __device__ __forceinline__ void epi_store_lds_block(const EpiOut& e, const uint1
         v[8 * k + 2 * j + 1] = __uint_as_float(q[j] & 0xFFFF0000u);
       }
     }
-    epi_store<32>(e, r, h0 + head, 32 * c, v);
+    epi_store<32>(e, cs_row, r, h0 + head, 32 * c, v);
   }
 }
 

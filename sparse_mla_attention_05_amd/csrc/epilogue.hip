@@ -22,6 +22,7 @@ __global__ void __launch_bounds__(kEpiPassThreads) out_epilogue_kernel(const Epi
   const int64_t r = item / p.heads;
   const int h = int(item % p.heads);
   const int col = 8 * (threadIdx.x & 63);
+  const float* cs_row = epi_cs_row(p.epi, r);
   const u32x4 q = *reinterpret_cast<const u32x4*>(p.in + r * p.in_rs + int64_t(h) * p.in_hs + col);
   float v[8];
 #pragma unroll
@@ -29,7 +30,7 @@ __global__ void __launch_bounds__(kEpiPassThreads) out_epilogue_kernel(const Epi
     v[2 * j] = __uint_as_float(q[j] << 16);
     v[2 * j + 1] = __uint_as_float(q[j] & 0xFFFF0000u);
   }
-  epi_store<8>(p.epi, r, h, col, v);
+  epi_store<8>(p.epi, cs_row, r, h, col, v);
 }
 
 }  // namespace

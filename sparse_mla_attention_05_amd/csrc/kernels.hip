@@ -99,6 +99,15 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   work /= p.head_blocks;
   const int split = int(work % p.splits);
   const int64_t r = work / p.splits;
+  // Output epilogue: this row's cos/sin row, read now so that the two
+  // dependent reads (position, then cache) overlap the walk; one wave keeps
+  // it in a register until the epilogue copies it to LDS.
+  __shared__ float epi_cs[64];
+  float cs_pre = 0.f;
+  if constexpr (EPI) {
+    if (p.epi.pos != nullptr && tid < 64) cs_pre = epi_cs_row(p.epi, r)[tid];
+  }
+
   const int h0 = hb * HB;
 
   const int ntiles = (p.topk + TK - 1) / TK;
@@ -315,6 +324,9 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   // ---- epilogue: combine the per-wave row sums, normalise, store
   if (g == 0) red[kg * HB + hg * 16 + l16] = l_run;
   if (kg == 0 && g == 0) mfin_s[hg * 16 + l16] = m_run;
+  if constexpr (EPI) {
+    if (tid < 64) epi_cs[tid] = cs_pre;
+  }
   __syncthreads();
 
   const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
@@ -351,7 +363,8 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   if (epi) {
     static_assert(HB * kEpiPitch <= TK * PITCH, "epilogue block fits the tile");
     __syncthreads();
-    epi_store_lds_block(p.epi, eblk, eblk + 32 * kEpiPitch, 32, HB, r, h0, p.heads, tid, C::NT);
+    epi_store_lds_block(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, eblk,
+                        eblk + 32 * kEpiPitch, 32, HB, r, h0, p.heads, tid, C::NT);
   }
   if (tid < HB) {
     const int h = h0 + tid;
@@ -384,10 +397,11 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
   float m = kNegInf;
   for (int s = 0; s < p.splits; ++s) m = fmaxf(m, pl[s * stride_s]);
   uint16_t* op = p.out + r * p.out_rs + int64_t(h) * p.out_hs + 4 * tid;
+  const float* cs_row = EPI ? epi_cs_row(p.epi, r) : nullptr;
   if (m == kNegInf) {
     if constexpr (EPI) {
       float v[4] = {0.f, 0.f, 0.f, 0.f};
-      epi_store<4>(p.epi, r, h, 4 * tid, v);
+      epi_store<4>(p.epi, cs_row, r, h, 4 * tid, v);
     } else {
       *reinterpret_cast<u32x2*>(op) = u32x2{0u, 0u};
     }
@@ -407,7 +421,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
   const float inv = 1.0f / tot;
   if constexpr (EPI) {
     float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-    epi_store<4>(p.epi, r, h, 4 * tid, v);
+    epi_store<4>(p.epi, cs_row, r, h, 4 * tid, v);
   } else {
     *reinterpret_cast<u32x2*>(op) =
         u32x2{pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv)};

@@ -92,6 +92,15 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   work /= p.head_blocks;
   const int split = int(work % p.splits);
   const int64_t r = work / p.splits;
+  // Output epilogue: this row's cos/sin row, read now so that the two
+  // dependent reads (position, then cache) overlap the walk; one wave keeps
+  // it in a register until the epilogue copies it to LDS.
+  __shared__ float epi_cs[64];
+  float cs_pre = 0.f;
+  if constexpr (EPI) {
+    if (p.epi.pos != nullptr && tid < 64) cs_pre = epi_cs_row(p.epi, r)[tid];
+  }
+
   const int h0 = hb * HB;
 
   // Tiles [0, T1) hold the main top-k, tiles [T1, ntiles) a second segment
@@ -329,6 +338,9 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   l_head += __shfl_xor(l_head, 32);
   if (g == 0) red[kg * HB + hg * 16 + l16] = l_head;
   if (kg == 0 && g == 0) mfin_s[hg * 16 + l16] = m_ref;
+  if constexpr (EPI) {
+    if (tid < 64) epi_cs[tid] = cs_pre;
+  }
   __syncthreads();
   const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
   const bool epi = EPI && !split_mode;
@@ -364,7 +376,8 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   if (epi) {
     static_assert(HB * kEpiPitch <= TK * PITCH, "epilogue block fits the tile");
     __syncthreads();
-    epi_store_lds_block(p.epi, eblk, eblk + 32 * kEpiPitch, 32, HB, r, h0, p.heads, tid, C::NT);
+    epi_store_lds_block(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, eblk,
+                        eblk + 32 * kEpiPitch, 32, HB, r, h0, p.heads, tid, C::NT);
   }
   if (tid < HB) {
     const int h = h0 + tid;

@@ -121,6 +121,15 @@ prefill_fp8_kernel(const FwdParams p) {
   work /= p.head_blocks;
   const int split = int(work % p.splits);
   const int64_t r = work / p.splits;
+  // Output epilogue: this row's cos/sin row, read now so that the two
+  // dependent reads (position, then cache) overlap the walk; one wave keeps
+  // it in a register until the epilogue copies it to LDS.
+  __shared__ float epi_cs[64];
+  float cs_pre = 0.f;
+  if constexpr (EPI) {
+    if (p.epi.pos != nullptr && tid < 64) cs_pre = epi_cs_row(p.epi, r)[tid];
+  }
+
   const int h0 = hblk * C::HB + 32 * hp;  // heads h0 + 16hb + l16 of this lane
 
   const int ntiles = (p.topk + TK - 1) / TK;
@@ -474,6 +483,9 @@ prefill_fp8_kernel(const FwdParams p) {
     xf[(wave * 2 + hb) * 64 + lane] = t;
     lt[hb] = t;
   }
+  if constexpr (EPI) {
+    if (tid < 64) epi_cs[tid] = cs_pre;
+  }
   __syncthreads();
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) lt[hb] += xf[(partner * 2 + hb) * 64 + lane];
@@ -489,7 +501,8 @@ prefill_fp8_kernel(const FwdParams p) {
       for (int m = 0; m < NDW / 2; ++m) {
         const floatx4 ra = o[2 * m][hb] * inv, rb = o[2 * m + 1][hb] * inv;
         float va[4] = {ra[0], ra[1], ra[2], ra[3]}, vb[4] = {rb[0], rb[1], rb[2], rb[3]};
-        epi_store_c16x2(p.epi, r, h, 256 * kh + 32 * m + 4 * g, va, vb);
+        epi_store_c16x2(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, r, h,
+                        256 * kh + 32 * m + 4 * g, va, vb);
       }
     } else {
 #pragma unroll

@@ -113,6 +113,15 @@ prefill_pp_kernel(const FwdParams p) {
   work /= p.head_blocks;
   const int split = int(work % p.splits);
   const int64_t r = work / p.splits;
+  // Output epilogue: this row's cos/sin row, read now so that the two
+  // dependent reads (position, then cache) overlap the walk; one wave keeps
+  // it in a register until the epilogue copies it to LDS.
+  __shared__ float epi_cs[64];
+  float cs_pre = 0.f;
+  if constexpr (EPI) {
+    if (p.epi.pos != nullptr && wave == 4) cs_pre = epi_cs_row(p.epi, r)[lane];
+  }
+
   const int h0 = hblk * 64 + 32 * hp;  // heads h0 + 16hb + l16 of this lane
 
   const int ntiles = (p.topk + TK - 1) / TK;
@@ -435,6 +444,9 @@ prefill_pp_kernel(const FwdParams p) {
       __syncthreads();
       if (!again) break;
     }
+    if constexpr (EPI) {
+      if (wave == 4) epi_cs[lane] = cs_pre;
+    }
     __syncthreads();  // row sums of the QK waves in xq
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -448,7 +460,8 @@ prefill_pp_kernel(const FwdParams p) {
         for (int m = 0; m < NDW / 2; ++m) {
           const floatx4 ra = o[2 * m][hb] * inv, rb = o[2 * m + 1][hb] * inv;
           float va[4] = {ra[0], ra[1], ra[2], ra[3]}, vb[4] = {rb[0], rb[1], rb[2], rb[3]};
-          epi_store_c16x2(p.epi, r, h, 256 * kh + 32 * m + 4 * g, va, vb);
+          epi_store_c16x2(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, r, h,
+                          256 * kh + 32 * m + 4 * g, va, vb);
         }
       } else {
 #pragma unroll
