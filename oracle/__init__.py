@@ -16,3 +16,4 @@ from .sparse_mla_oracle import (  # noqa: F401
     sparse_mla_fwd_torch,
 )
 from . import out_epilogue  # noqa: F401,E402  (inverse RoPE + MXFP8 output epilogue)
+from . import indexer  # noqa: F401,E402  (fp8 MQA logits + top-k of the indexer)

@@ -345,3 +345,116 @@ def make_epilogue_rows(rows: int, heads: int, seed: int, std: float = 0.05) -> t
         x[r, h, 160] = -1e-9                                          # rounds to -0 in e4m3
         x[r, h, 448:512] *= 4.0                                       # the rotated columns
     return x.to(torch.bfloat16)
+
+
+# ------------------------------------------------------------- indexer ---
+
+@dataclass(frozen=True)
+class IndexerWorkload:
+    """One synthetic indexer call: `rows` query rows of `requests` requests,
+    each request's rows the last positions of its own `keys / requests`-key
+    context (causal windows), 32 heads of 128 dims, top-k `topk`."""
+    name: str
+    rows: int
+    keys: int
+    requests: int = 1
+    heads: int = 32
+    dim: int = 128
+    topk: int = 2048
+    seed: int = 0
+    description: str = ""
+
+
+# The indexer shapes of "[HIP] [JIT] fp8_mqa_logits: v35w gfx950 prefill
+# indexer logits kernel" (aiter PR 7183), its kernel-time table: causal
+# chunks of one request, and of four requests per chunk.
+INDEXER_WORKLOADS = {
+    w.name: w for w in [
+        IndexerWorkload("ix_tiny", rows=70, keys=600, requests=2, topk=64, seed=21,
+                        description="small ragged case: 2 requests, 35 rows, 300 keys each"),
+        IndexerWorkload("ix_causal_8k_8k", 8192, 8192, 1, seed=22,
+                        description="causal, one request: s_q 8192, s_k 8192"),
+        IndexerWorkload("ix_causal_4k_32k", 4096, 32768, 1, seed=23,
+                        description="causal, one request: s_q 4096, s_k 32768"),
+        IndexerWorkload("ix_causal_2k_64k", 2048, 65536, 1, seed=24,
+                        description="causal, one request: s_q 2048, s_k 65536"),
+        IndexerWorkload("ix_causal_1k_128k", 1024, 131072, 1, seed=25,
+                        description="causal, one request: s_q 1024, s_k 131072"),
+        IndexerWorkload("ix_multi_4k_32k", 4096, 32768, 4, seed=26,
+                        description="causal, four requests per chunk: s_q 4096, s_k 32768"),
+    ]
+}
+
+
+@dataclass
+class IndexerInputs:
+    workload: IndexerWorkload
+    q: torch.Tensor         # float8_e4m3fn [M, H, D]
+    k: torch.Tensor         # float8_e4m3fn [N, D]
+    kv_scale: torch.Tensor  # fp32 [N]
+    w: torch.Tensor         # fp32 [M, H]
+    ks: torch.Tensor        # int32 [M]
+    ke: torch.Tensor        # int32 [M]
+
+
+def indexer_windows(w: IndexerWorkload) -> tuple[torch.Tensor, torch.Tensor]:
+    """Request b owns rows [b M/B, (b+1) M/B) and keys [b N/B, (b+1) N/B); its
+    local row i sits at key position N/B - M/B + i and sees the keys of its
+    request up to and including that position."""
+    B = w.requests
+    mb, nb = w.rows // B, w.keys // B
+    m = torch.arange(w.rows, dtype=torch.int64)
+    b = torch.clamp(m // mb, max=B - 1)
+    i = m - b * mb
+    ks = b * nb
+    ke = ks + (nb - mb) + i + 1
+    return ks.to(torch.int32), ke.to(torch.int32)
+
+
+def make_indexer_inputs(w: IndexerWorkload | str) -> IndexerInputs:
+    """Draw order: q (N(0,1) to e4m3), k (N(0,1) per key, quantised with the
+    key's own scale max|k|/448), w (N(0, 1/32))."""
+    if isinstance(w, str):
+        w = INDEXER_WORKLOADS[w]
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    q = torch.randn(w.rows, w.heads, w.dim, generator=gen).clamp(-FP8_MAX, FP8_MAX)
+    q = q.to(torch.float8_e4m3fn)
+    kx = torch.randn(w.keys, w.dim, generator=gen)
+    scale = kx.abs().amax(dim=1) / FP8_MAX
+    k = (kx / scale[:, None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    wt = torch.randn(w.rows, w.heads, generator=gen) * w.heads ** -0.5
+    ks, ke = indexer_windows(w)
+    return IndexerInputs(w, q, k, scale.to(torch.float32), wt.to(torch.float32), ks, ke)
+
+
+def make_topk_logits(rows: int, keys: int, seed: int, k: int) -> tuple[torch.Tensor, torch.Tensor,
+                                                                       torch.Tensor]:
+    """fp32 logits [rows, keys] with windows [ks, ke) of every kind a top-k
+    meets: empty, shorter than k, exactly k, longer; rows of continuous
+    values, rows drawn from a handful of values (many ties at the k-th
+    value), rows with negative zeros and huge magnitudes. Outside the window
+    the values are NaN (a top-k must not read them)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(rows, keys, generator=gen)
+    ks = torch.randint(0, max(1, keys // 4), (rows,), generator=gen)
+    span = torch.randint(0, keys, (rows,), generator=gen)
+    for r in range(rows):
+        kind = r % 6
+        if kind == 1:
+            x[r] = torch.randint(-3, 4, (keys,), generator=gen).float()   # ties
+        elif kind == 2:
+            x[r] = torch.where(torch.rand(keys, generator=gen) < 0.5, -0.0, 0.0)
+            x[r, ::7] = 1.0
+        elif kind == 3:
+            x[r] *= 1e30
+        if r % 5 == 0:
+            span[r] = 0                     # empty window
+        elif r % 5 == 1:
+            span[r] = k // 2                # shorter than k
+        elif r % 5 == 2:
+            span[r] = k                     # exactly k
+    ke = torch.clamp(ks + span, max=keys)
+    for r in range(rows):
+        x[r, :ks[r]] = float("nan")
+        x[r, ke[r]:] = float("nan")
+    return x.to(torch.float32), ks.to(torch.int32), ke.to(torch.int32)
