@@ -248,6 +248,48 @@ SMLA_API int sparse_mla_fwd_epi(const smla_tensor* q, const smla_tensor* kv_pool
 SMLA_API int sparse_mla_out_epilogue(const smla_tensor* rows, const smla_epilogue* epi,
                             smla_tensor* out, void* stream);
 
+/*
+ * Indexer (the stage that produces the index rows the forward consumes),
+ * after "[HIP] [JIT] fp8_mqa_logits: v35w gfx950 prefill indexer logits
+ * kernel" (aiter PR 7183), Motivation:
+ *
+ *   logits[m, n] = sum_h relu(q[m,h,:] . k[n,:]) * w[m,h] * kv_scale[n]
+ *                  for n in [ks[m], ke[m]) (clipped to [0, N)), -inf elsewhere
+ *
+ * sparse_mla_indexer_logits
+ *  q        float8_e4m3fn [M, 32, 128] (the indexer's 32 heads x 128 dims);
+ *           last dim contiguous, base and strides multiples of 16 bytes.
+ *  k        float8_e4m3fn [N, 128], N <= 2^27; base and row stride multiples
+ *           of 16 bytes.
+ *  kv_scale fp32 [N], contiguous: each key's dequantisation scale.
+ *  w        fp32 [M, 32], last dim contiguous, base 16-byte aligned, row
+ *           stride a multiple of 4: the per-(row, head) weights.
+ *  ks, ke   int32 [M], contiguous: each row's window [ks, ke).
+ *  clean    1: positions outside a row's window are written -inf; 0: only
+ *           the window is written (the rest of the row is left as it was).
+ *  logits   fp32 [M, N], last dim contiguous; must not alias an input.
+ * Products and dots are formed by fp8 MFMA with fp32 accumulation; relu, the
+ * head weights and the head sum in fp32, then the key scale.
+ *
+ * sparse_mla_indexer_topk - per row, the indices of the k largest logits
+ * inside [ks, ke) (clipped to [0, N)), ascending, ties at the k-th value to
+ * the lower index, -1 after the window's keys when it holds fewer than k
+ * (the pages describe no selection; this is the plainest reading). Only the
+ * window is read, so the rest of a row may hold anything.
+ *  logits   fp32 [R, N], N < 2^31, last dim contiguous.
+ *  ks, ke   int32 [R].
+ *  k        1 .. 65536.
+ *  indices  int32 [R, k], last dim contiguous; must not alias an input. An
+ *           index row the forward can take directly (negative = invalid).
+ */
+SMLA_API int sparse_mla_indexer_logits(const smla_tensor* q, const smla_tensor* k,
+                              const smla_tensor* kv_scale, const smla_tensor* w,
+                              const smla_tensor* ks, const smla_tensor* ke, int32_t clean,
+                              smla_tensor* logits, void* stream);
+SMLA_API int sparse_mla_indexer_topk(const smla_tensor* logits, const smla_tensor* ks,
+                            const smla_tensor* ke, int32_t k, smla_tensor* indices,
+                            void* stream);
+
 /* 1 if the shapes/dtypes/strides are covered by the kernels, else 0 (the
  * reason is left in sparse_mla_last_error). Host-only; makes no HIP call. */
 SMLA_API int sparse_mla_is_supported(const smla_tensor* q, const smla_tensor* kv_pool,

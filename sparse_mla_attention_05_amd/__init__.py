@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     sparse_mla_fwd2,
     sparse_mla_fwd_epi,
     sparse_mla_fwd_ex,
+    sparse_mla_indexer_logits,
+    sparse_mla_indexer_topk,
     sparse_mla_is_supported,
     sparse_mla_out_epilogue,
     sparse_mla_plan,

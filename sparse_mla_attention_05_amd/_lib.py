@@ -24,6 +24,7 @@ EXPORTED = (
     "sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_fwd2", "sparse_mla_fwd_epi",
     "sparse_mla_out_epilogue", "sparse_mla_is_supported", "sparse_mla_plan", "sparse_mla_plan2",
     "sparse_mla_work_of", "sparse_mla_last_error", "sparse_mla_version",
+    "sparse_mla_indexer_logits", "sparse_mla_indexer_topk",
 )
 
 
@@ -86,6 +87,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_fwd_epi.restype = ctypes.c_int
     lib.sparse_mla_out_epilogue.argtypes = [T, E, T, ctypes.c_void_p]
     lib.sparse_mla_out_epilogue.restype = ctypes.c_int
+    lib.sparse_mla_indexer_logits.argtypes = [T, T, T, T, T, T, ctypes.c_int32, T, ctypes.c_void_p]
+    lib.sparse_mla_indexer_logits.restype = ctypes.c_int
+    lib.sparse_mla_indexer_topk.argtypes = [T, T, T, ctypes.c_int32, T, ctypes.c_void_p]
+    lib.sparse_mla_indexer_topk.restype = ctypes.c_int
     lib.sparse_mla_plan2.argtypes = [T, T, T, T, T, ctypes.POINTER(SmlaOptions), ctypes.c_int32,
                                      ctypes.POINTER(SmlaPlan), ctypes.POINTER(SmlaPlan),
                                      ctypes.POINTER(ctypes.c_int64)]
@@ -336,3 +341,30 @@ def status_of_out_epilogue(rows, out, rope_positions=None, rope_cos_sin=None, ou
     dr, do = describe(rows), describe(out)
     epi, _keep = _epilogue(rope_positions, rope_cos_sin, out_scale)
     return lib.sparse_mla_out_epilogue(_ptr(dr), ctypes.byref(epi), _ptr(do), stream)
+
+
+def status_of_indexer_logits(q, k, kv_scale, w, ks, ke, logits, clean=True, stream=None) -> int:
+    """Raw status of sparse_mla_indexer_logits."""
+    lib = load()
+    ds = [describe(t) for t in (q, k, kv_scale, w, ks, ke, logits)]
+    st = _stream_handle(stream, q, logits) if stream is None and q is not None and q.is_cuda else stream
+    return lib.sparse_mla_indexer_logits(*[_ptr(d) for d in ds[:6]], int(bool(clean)), _ptr(ds[6]), st)
+
+
+def sparse_mla_indexer_logits(q, k, kv_scale, w, ks, ke, logits, clean=True, stream=None) -> None:
+    """Indexer logits: per key the sum over 32 heads of relu(q . k) * w, times
+    the key's scale, inside [ks, ke) (-inf outside when clean)."""
+    _check(status_of_indexer_logits(q, k, kv_scale, w, ks, ke, logits, clean, stream))
+
+
+def status_of_indexer_topk(logits, ks, ke, k, indices, stream=None) -> int:
+    lib = load()
+    ds = [describe(t) for t in (logits, ks, ke, indices)]
+    st = _stream_handle(stream, logits) if stream is None and logits is not None and logits.is_cuda else stream
+    return lib.sparse_mla_indexer_topk(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), int(k), _ptr(ds[3]), st)
+
+
+def sparse_mla_indexer_topk(logits, ks, ke, k, indices, stream=None) -> None:
+    """Per row the indices of the k largest logits inside [ks, ke), ascending,
+    -1 padded."""
+    _check(status_of_indexer_topk(logits, ks, ke, k, indices, stream))

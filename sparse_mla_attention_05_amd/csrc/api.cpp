@@ -625,6 +625,114 @@ int sparse_mla_out_epilogue(const smla_tensor* rows, const smla_epilogue* epi, s
   return SMLA_OK;
 }
 
+int sparse_mla_indexer_logits(const smla_tensor* q, const smla_tensor* k,
+                              const smla_tensor* kv_scale, const smla_tensor* w,
+                              const smla_tensor* ks, const smla_tensor* ke, int32_t clean,
+                              smla_tensor* logits, void* stream) {
+  int s;
+  if ((s = check_tensor(q, "q", 3, SMLA_FP8_E4M3FN))) return s;
+  if ((s = check_tensor(k, "k", 2, SMLA_FP8_E4M3FN))) return s;
+  if ((s = check_tensor(kv_scale, "kv_scale", 1, SMLA_FP32))) return s;
+  if ((s = check_tensor(w, "w", 2, SMLA_FP32))) return s;
+  if ((s = check_tensor(ks, "ks", 1, SMLA_INT32))) return s;
+  if ((s = check_tensor(ke, "ke", 1, SMLA_INT32))) return s;
+  if ((s = check_tensor(logits, "logits", 2, SMLA_FP32))) return s;
+  const int64_t M = q->shape[0], N = k->shape[0];
+  if (q->shape[1] != kIxHeads || q->shape[2] != kIxDim)
+    return fail(SMLA_ERR_UNSUPPORTED, "q: the indexer takes 32 heads of 128 dims");
+  if (k->shape[1] != kIxDim) return fail(SMLA_ERR_UNSUPPORTED, "k: rows must be 128 wide");
+  if (kv_scale->shape[0] != N) return fail(SMLA_ERR_INVALID_ARG, "kv_scale: shape must be [N]");
+  if (w->shape[0] != M || w->shape[1] != kIxHeads)
+    return fail(SMLA_ERR_INVALID_ARG, "w: shape must be [M, 32]");
+  if (ks->shape[0] != M || ke->shape[0] != M)
+    return fail(SMLA_ERR_INVALID_ARG, "ks/ke: shape must be [M]");
+  if (logits->shape[0] != M || logits->shape[1] != N)
+    return fail(SMLA_ERR_INVALID_ARG, "logits: shape must be [M, N]");
+  if (N > (int64_t(1) << 27)) return fail(SMLA_ERR_UNSUPPORTED, "k: more than 2^27 keys");
+  if (clean != 0 && clean != 1) return fail(SMLA_ERR_INVALID_ARG, "clean must be 0 or 1");
+  if (M == 0 || N == 0) return SMLA_OK;
+  const smla_tensor* all[7] = {q, k, kv_scale, w, ks, ke, logits};
+  for (const smla_tensor* t : all)
+    if (!t->data) return fail(SMLA_ERR_INVALID_ARG, "null data");
+  if (!aligned16(q->data) || q->stride[0] % 16 != 0 || q->stride[1] % 16 != 0)
+    return fail(SMLA_ERR_UNSUPPORTED, "q: base, row and head strides must be 16-byte aligned");
+  if (!aligned16(k->data) || (N > 1 && k->stride[0] % 16 != 0))
+    return fail(SMLA_ERR_UNSUPPORTED, "k: base and row stride must be 16-byte aligned");
+  if (!aligned16(w->data) || (M > 1 && w->stride[0] % 4 != 0))
+    return fail(SMLA_ERR_UNSUPPORTED, "w: base 16-byte aligned, row stride a multiple of 4");
+  const smla_tensor* vecs[3] = {kv_scale, ks, ke};
+  for (const smla_tensor* t : vecs)
+    if ((reinterpret_cast<uintptr_t>(t->data) & 3u) != 0)
+      return fail(SMLA_ERR_INVALID_ARG, "kv_scale/ks/ke: base must be 4-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(logits->data) & 3u) != 0)
+    return fail(SMLA_ERR_INVALID_ARG, "logits: base must be 4-byte aligned");
+  for (int i = 0; i < 6; ++i)
+    if (overlap(logits, all[i])) return fail(SMLA_ERR_INVALID_ARG, "logits must not alias an input");
+  IxParams p{};
+  p.q = static_cast<const uint8_t*>(q->data);
+  p.q_rs = q->stride[0];
+  p.q_hs = q->stride[1];
+  p.k = static_cast<const uint8_t*>(k->data);
+  p.k_rs = k->stride[0];
+  p.kv_scale = static_cast<const float*>(kv_scale->data);
+  p.w = static_cast<const float*>(w->data);
+  p.w_rs = w->stride[0];
+  p.ks = static_cast<const int32_t*>(ks->data);
+  p.ke = static_cast<const int32_t*>(ke->data);
+  p.logits = static_cast<float*>(logits->data);
+  p.l_rs = logits->stride[0];
+  p.m = M;
+  p.n = int32_t(N);
+  p.clean = clean;
+  const int le = launch_ix_logits(p, stream);
+  if (le != 0)
+    return fail(SMLA_ERR_HIP, std::string("kernel launch: ") +
+                                  hipGetErrorString(static_cast<hipError_t>(le)));
+  return SMLA_OK;
+}
+
+int sparse_mla_indexer_topk(const smla_tensor* logits, const smla_tensor* ks,
+                            const smla_tensor* ke, int32_t k, smla_tensor* indices,
+                            void* stream) {
+  int s;
+  if ((s = check_tensor(logits, "logits", 2, SMLA_FP32))) return s;
+  if ((s = check_tensor(ks, "ks", 1, SMLA_INT32))) return s;
+  if ((s = check_tensor(ke, "ke", 1, SMLA_INT32))) return s;
+  if ((s = check_tensor(indices, "indices", 2, SMLA_INT32))) return s;
+  const int64_t R = logits->shape[0], N = logits->shape[1];
+  if (k < 1 || k > 65536) return fail(SMLA_ERR_UNSUPPORTED, "k must be in [1, 65536]");
+  if (ks->shape[0] != R || ke->shape[0] != R)
+    return fail(SMLA_ERR_INVALID_ARG, "ks/ke: shape must be [R]");
+  if (indices->shape[0] != R || indices->shape[1] != k)
+    return fail(SMLA_ERR_INVALID_ARG, "indices: shape must be [R, k]");
+  if (N >= (int64_t(1) << 31)) return fail(SMLA_ERR_UNSUPPORTED, "logits: 2^31 or more keys");
+  if (R > (int64_t(1) << 31)) return fail(SMLA_ERR_UNSUPPORTED, "logits: more than 2^31 rows");
+  if (R == 0) return SMLA_OK;
+  const smla_tensor* all[4] = {logits, ks, ke, indices};
+  for (const smla_tensor* t : all) {
+    if (!t->data) return fail(SMLA_ERR_INVALID_ARG, "null data");
+    if ((reinterpret_cast<uintptr_t>(t->data) & 3u) != 0)
+      return fail(SMLA_ERR_INVALID_ARG, "base must be 4-byte aligned");
+  }
+  for (int i = 0; i < 3; ++i)
+    if (overlap(indices, all[i])) return fail(SMLA_ERR_INVALID_ARG, "indices must not alias an input");
+  TopkParams p{};
+  p.logits = static_cast<const float*>(logits->data);
+  p.l_rs = logits->stride[0];
+  p.ks = static_cast<const int32_t*>(ks->data);
+  p.ke = static_cast<const int32_t*>(ke->data);
+  p.out = static_cast<int32_t*>(indices->data);
+  p.o_rs = indices->stride[0];
+  p.rows = R;
+  p.n = int32_t(N);
+  p.k = k;
+  const int le = launch_topk(p, stream);
+  if (le != 0)
+    return fail(SMLA_ERR_HIP, std::string("kernel launch: ") +
+                                  hipGetErrorString(static_cast<hipError_t>(le)));
+  return SMLA_OK;
+}
+
 int sparse_mla_plan2(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* indices,
                      const smla_tensor* extra_pool, const smla_tensor* extra_indices,
                      const smla_options* opt, int32_t num_cus, smla_plan* plan_main,

@@ -1,0 +1,328 @@
+// The indexer that produces the sparse attention's index rows: fp8 MQA
+// logits and a per-row top-k, after "[HIP] [JIT] fp8_mqa_logits: v35w gfx950
+// prefill indexer logits kernel" (aiter PR 7183), Motivation and Design:
+//
+//   logits[m, n] = sum_h relu(Q[m,h,:] . K[n,:]) * w[m,h] * kv_scale[n]
+//                  for n in [ks[m], ke[m]), -inf elsewhere
+//
+// Logits kernel. A workgroup takes 32 query rows (8 waves x 4 rows) and one
+// 4096-key column of the output; Q (4 rows x 32 heads x 128 fp8 = 64 VGPRs)
+// and w stay in registers, and all waves walk the same K sequence through
+// LDS (64-key stages, double-buffered, chunk-XOR swizzled rows), so K is read
+// once per 32 rows. One v_mfma_f32_16x16x128_f8f6f4 computes 16 heads x 16
+// keys over all 128 dims (A = Q rows, B = K rows, the same lane->k mapping on
+// both sides). A lane's accumulator holds heads 4g..4g+3 of one key; relu
+// and the head weight are applied there, the four lanes g of a key are summed
+// by two xor shuffles arranged as a butterfly over the wave's four rows
+// (afterwards lane g owns row g), and the key's scale is applied after the
+// head sum. Tiles outside every row's window are not computed; with `clean`
+// the kernel writes -inf there itself.
+//
+// Top-k kernel. One workgroup per row: a three-level radix select (11, 11
+// and 10 bits) on the order-preserving integer image of the fp32 logits
+// finds the k-th largest value T; a last pass writes, in ascending index
+// order, every key above T and the lowest-index keys equal to T (block-wide
+// prefix sums of two ballots per 1024 keys). Only the window is read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace smla {
+namespace {
+
+constexpr int kIxWaves = 8;
+constexpr int kIxRowsPerWave = 4;
+constexpr int kIxRows = kIxWaves * kIxRowsPerWave;
+constexpr int kIxTile = 64;                    // keys per LDS stage
+constexpr int kIxTileBytes = kIxTile * kIxDim;  // 8 KB
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i cat(u32x4 a, u32x4 b) {
+  return v8i{int(a.x), int(a.y), int(a.z), int(a.w), int(b.x), int(b.y), int(b.z), int(b.w)};
+}
+
+__global__ void __launch_bounds__(kIxWaves * 64, 2) ix_logits_kernel(const IxParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][kIxTileBytes];
+  __shared__ float ksc[2][kIxTile];
+  __shared__ int wlo[kIxWaves], whi[kIxWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t m0 = int64_t(blockIdx.x) * kIxRows + kIxRowsPerWave * wave;
+  const int n_begin = int(blockIdx.y) * kIxChunk;
+  const int n_end = min(p.n, n_begin + kIxChunk);
+
+  // ---- this wave's rows: windows, Q and w in registers.
+  int lo[kIxRowsPerWave], hi[kIxRowsPerWave];
+  v8i qa[kIxRowsPerWave][2];
+  floatx4 wv[kIxRowsPerWave][2];
+  int my_lo = 0, my_hi = 0;  // the window of row g (the row this lane stores)
+#pragma unroll
+  for (int j = 0; j < kIxRowsPerWave; ++j) {
+    const int64_t m = m0 + j;
+    const int64_t mc = m < p.m ? m : p.m - 1;
+    int a = m < p.m ? p.ks[m] : 0, b = m < p.m ? p.ke[m] : 0;
+    a = a < 0 ? 0 : (a > p.n ? p.n : a);
+    b = b < a ? a : (b > p.n ? p.n : b);
+    lo[j] = a;
+    hi[j] = b;
+    if (g == j) {
+      my_lo = a;
+      my_hi = b;
+    }
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(p.q + mc * p.q_rs +
+                                                        int64_t(16 * ht + l16) * p.q_hs + 32 * g);
+      qa[j][ht] = cat(src[0], src[1]);
+      wv[j][ht] = *reinterpret_cast<const floatx4*>(p.w + mc * p.w_rs + 16 * ht + 4 * g);
+    }
+  }
+
+  // ---- keys any of the 32 rows sees inside this column: whole tiles only.
+  int ulo = p.n, uhi = 0;
+#pragma unroll
+  for (int j = 0; j < kIxRowsPerWave; ++j)
+    if (hi[j] > lo[j]) {
+      ulo = min(ulo, lo[j]);
+      uhi = max(uhi, hi[j]);
+    }
+  if (lane == 0) {
+    wlo[wave] = ulo;
+    whi[wave] = uhi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kIxWaves; ++w) {
+    ulo = min(ulo, wlo[w]);
+    uhi = max(uhi, whi[w]);
+  }
+  ulo = max(ulo, n_begin);
+  uhi = min(uhi, n_end);
+  const int t_first = ulo < uhi ? (ulo / kIxTile) * kIxTile : n_begin;
+  const int ntiles = ulo < uhi ? (uhi - t_first + kIxTile - 1) / kIxTile : 0;
+  const int t_stop = min(n_end, t_first + ntiles * kIxTile);
+
+  // ---- -inf outside the computed tiles (clean mode): rows of this wave.
+  if (p.clean) {
+#pragma unroll
+    for (int j = 0; j < kIxRowsPerWave; ++j) {
+      const int64_t m = m0 + j;
+      if (m >= p.m) continue;
+      float* row = p.logits + m * p.l_rs;
+      for (int n = n_begin + lane; n < t_first; n += 64) row[n] = kNegInf;
+      for (int n = t_stop + lane; n < n_end; n += 64) row[n] = kNegInf;
+    }
+  }
+  if (ntiles == 0) return;
+
+  // ---- K staging: thread t moves 16 bytes (key t/8, chunk t%8) of a tile;
+  // physical chunk = chunk ^ (key & 7).
+  const int skey = tid >> 3, schunk = tid & 7;
+  const int sdst = skey * kIxDim + 16 * (schunk ^ (skey & 7));
+  auto load_tile = [&](int n0, u32x4& v, float& sc) {
+    const int n = n0 + skey;
+    v = n < p.n ? *reinterpret_cast<const u32x4*>(p.k + int64_t(n) * p.k_rs + 16 * schunk)
+                : u32x4{0u, 0u, 0u, 0u};
+    sc = (tid < kIxTile && n0 + tid < p.n) ? p.kv_scale[n0 + tid] : 0.f;
+  };
+  u32x4 pre;
+  float psc;
+  load_tile(t_first, pre, psc);
+  *reinterpret_cast<u32x4*>(&kt[0][sdst]) = pre;
+  if (tid < kIxTile) ksc[0][tid] = psc;
+  __syncthreads();
+
+  const int64_t my_m = m0 + g;
+  float* const my_row = p.logits + (my_m < p.m ? my_m : 0) * p.l_rs;
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int n0 = t_first + it * kIxTile;
+    const bool more = it + 1 < ntiles;
+    if (more) load_tile(n0 + kIxTile, pre, psc);
+    const uint8_t* tile = kt[buf];
+#pragma unroll
+    for (int kb = 0; kb < kIxTile / 16; ++kb) {
+      const int key = 16 * kb + l16;
+      const uint8_t* krow = tile + key * kIxDim;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * g) ^ (key & 7)));
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * g + 1) ^ (key & 7)));
+      const v8i kb8 = cat(b0, b1);
+      float part[kIxRowsPerWave];
+#pragma unroll
+      for (int j = 0; j < kIxRowsPerWave; ++j) {
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+        const floatx4 s0 =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[j][0], kb8, zero, 0, 0, 0, 0, 0, 0);
+        const floatx4 s1 =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[j][1], kb8, zero, 0, 0, 0, 0, 0, 0);
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a = __builtin_fmaf(fmaxf(s0[i], 0.f), wv[j][0][i], a);
+          b = __builtin_fmaf(fmaxf(s1[i], 0.f), wv[j][1][i], b);
+        }
+        part[j] = a + b;
+      }
+      // Butterfly over the lane groups g (bits 4, 5): afterwards lane g holds
+      // row g's sum over all 32 heads for key `key`.
+      const bool b0s = (g & 1) != 0, b1s = (g & 2) != 0;
+      const float qa0 = (b0s ? part[1] : part[0]) + __shfl_xor(b0s ? part[0] : part[1], 16);
+      const float qb0 = (b0s ? part[3] : part[2]) + __shfl_xor(b0s ? part[2] : part[3], 16);
+      const float tot = (b1s ? qb0 : qa0) + __shfl_xor(b1s ? qa0 : qb0, 32);
+      const int n = n0 + key;
+      if (my_m < p.m && n < t_stop) {
+        if (n >= my_lo && n < my_hi)
+          my_row[n] = tot * ksc[buf][key];
+        else if (p.clean)
+          my_row[n] = kNegInf;
+      }
+    }
+    if (more) {
+      *reinterpret_cast<u32x4*>(&kt[buf ^ 1][sdst]) = pre;
+      if (tid < kIxTile) ksc[buf ^ 1][tid] = psc;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ top-k
+
+constexpr int kTkThreads = 1024;
+constexpr int kTkWaves = kTkThreads / 64;
+
+// Order-preserving integer image of an fp32 value (-0 taken as +0, so the two
+// zeros tie as they do as numbers).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive count of the items after this thread's in thread order (a
+// suffix sum), over the whole block; sh holds kTkWaves words.
+__device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, uint32_t* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;  // inclusive suffix within the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_down(x, d);
+    if (lane + d < 64) x += y;
+  }
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  uint32_t above = 0;
+  for (int w = wave + 1; w < kTkWaves; ++w) above += sh[w];
+  __syncthreads();
+  return x - v + above;
+}
+
+__global__ void __launch_bounds__(kTkThreads) topk_kernel(const TopkParams p) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scan[kTkWaves];
+  __shared__ uint32_t pick[2];  // bin, count above it
+  __shared__ uint32_t cnt[2][2][kTkWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const float* row = p.logits + r * p.l_rs;
+  int32_t* out = p.out + r * p.o_rs;
+  int lo = p.ks[r], hi = p.ke[r];
+  lo = lo < 0 ? 0 : (lo > p.n ? p.n : lo);
+  hi = hi < lo ? lo : (hi > p.n ? p.n : hi);
+  const int len = hi - lo;
+  if (len <= p.k) {
+    for (int i = tid; i < p.k; i += kTkThreads) out[i] = i < len ? lo + i : -1;
+    return;
+  }
+
+  // ---- radix select: three levels of 11, 11 and 10 bits.
+  uint32_t prefix = 0;     // selected high bits so far
+  uint32_t need = p.k;     // how many of the candidates still to take
+  constexpr int kShift[3] = {21, 10, 0};
+  constexpr int kBins[3] = {2048, 2048, 1024};
+#pragma unroll
+  for (int lv = 0; lv < 3; ++lv) {
+    const int sh = kShift[lv];
+    const int bins = kBins[lv];
+    for (int i = tid; i < 2048; i += kTkThreads) hist[i] = 0u;
+    __syncthreads();
+    const int hs = lv == 0 ? 32 : kShift[lv - 1];  // candidates match `prefix` above bit hs
+    for (int n = lo + tid; n < hi; n += kTkThreads) {
+      const uint32_t u = order_key(row[n]);
+      if (lv == 0 || (u >> hs) == prefix) atomicAdd(&hist[(u >> sh) & uint32_t(bins - 1)], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins 2t (lower) and 2t + 1
+    const uint32_t h0 = 2 * tid < bins ? hist[2 * tid] : 0u;
+    const uint32_t h1 = 2 * tid + 1 < bins ? hist[2 * tid + 1] : 0u;
+    const uint32_t above1 = block_suffix_excl(h0 + h1, scan);  // count in bins > 2t + 1
+    if (above1 < need && above1 + h1 >= need) {
+      pick[0] = 2 * tid + 1;
+      pick[1] = above1;
+    } else if (above1 + h1 < need && above1 + h1 + h0 >= need) {
+      pick[0] = 2 * tid;
+      pick[1] = above1 + h1;
+    }
+    __syncthreads();
+    prefix = (prefix << (lv == 0 ? 11 : (lv == 1 ? 11 : 10))) | pick[0];
+    need -= pick[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;  // the k-th largest key; `need` keys equal to it are taken
+
+  // ---- output in ascending index order: 1024 keys per round.
+  uint32_t eq_base = 0, sel_base = 0;
+  for (int base = lo, round = 0; base < hi; base += kTkThreads, ++round) {
+    const int n = base + tid;
+    const uint32_t u = n < hi ? order_key(row[n]) : 0u;
+    const bool eq = n < hi && u == T;
+    const uint64_t eqm = __ballot(eq);
+    const uint32_t eq_in_wave = __popcll(eqm & ((uint64_t(1) << lane) - 1));
+    uint32_t (*c)[kTkWaves] = cnt[round & 1];
+    if (lane == 0) c[0][wave] = __popcll(eqm);
+    __syncthreads();
+    uint32_t eq_before = eq_base, eq_round = 0;
+    for (int w = 0; w < kTkWaves; ++w) {
+      const uint32_t x = c[0][w];
+      if (w < wave) eq_before += x;
+      eq_round += x;
+    }
+    const bool sel = n < hi && (u > T || (eq && eq_before + eq_in_wave < need));
+    const uint64_t selm = __ballot(sel);
+    if (lane == 0) c[1][wave] = __popcll(selm);
+    __syncthreads();
+    uint32_t sel_before = sel_base, sel_round = 0;
+    for (int w = 0; w < kTkWaves; ++w) {
+      const uint32_t x = c[1][w];
+      if (w < wave) sel_before += x;
+      sel_round += x;
+    }
+    if (sel) out[sel_before + __popcll(selm & ((uint64_t(1) << lane) - 1))] = n;
+    eq_base += eq_round;
+    sel_base += sel_round;
+  }
+}
+
+}  // namespace
+
+int launch_ix_logits(const IxParams& p, void* stream) {
+  if (p.m == 0 || p.n == 0) return 0;
+  const dim3 grid(uint32_t((p.m + kIxRows - 1) / kIxRows), uint32_t((p.n + kIxChunk - 1) / kIxChunk));
+  hipLaunchKernelGGL(ix_logits_kernel, grid, dim3(kIxWaves * 64), 0,
+                     reinterpret_cast<hipStream_t>(stream), p);
+  return int(hipGetLastError());
+}
+
+int launch_topk(const TopkParams& p, void* stream) {
+  if (p.rows == 0) return 0;
+  hipLaunchKernelGGL(topk_kernel, dim3(uint32_t(p.rows)), dim3(kTkThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), p);
+  return int(hipGetLastError());
+}
+
+}  // namespace smla

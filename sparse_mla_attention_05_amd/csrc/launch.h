@@ -81,6 +81,43 @@ struct EpiPassParams {
 };
 int launch_out_epilogue(const EpiPassParams& p, void* stream);
 
+// Indexer logits (indexer.hip): 32 heads x 128 dims of fp8, strides in bytes
+// for the fp8 tensors and in elements otherwise.
+constexpr int kIxHeads = 32;
+constexpr int kIxDim = 128;
+constexpr int kIxChunk = 4096;  // keys per workgroup column
+struct IxParams {
+  const uint8_t* q;          // e4m3fn [M, 32, 128]
+  int64_t q_rs, q_hs;
+  const uint8_t* k;          // e4m3fn [N, 128]
+  int64_t k_rs;
+  const float* kv_scale;     // fp32 [N]
+  const float* w;            // fp32 [M, 32]
+  int64_t w_rs;
+  const int32_t* ks;         // int32 [M]
+  const int32_t* ke;
+  float* logits;             // fp32 [M, N]
+  int64_t l_rs;
+  int64_t m;
+  int32_t n;
+  int32_t clean;             // 1: write -inf outside each row's window too
+};
+int launch_ix_logits(const IxParams& p, void* stream);
+
+// Per-row top-k of logits inside each row's window (indexer.hip).
+struct TopkParams {
+  const float* logits;       // fp32 [R, N]
+  int64_t l_rs;
+  const int32_t* ks;         // int32 [R]
+  const int32_t* ke;
+  int32_t* out;              // int32 [R, k]
+  int64_t o_rs;
+  int64_t rows;
+  int32_t n;
+  int32_t k;
+};
+int launch_topk(const TopkParams& p, void* stream);
+
 struct Problem {
   int64_t rows;
   int32_t heads;

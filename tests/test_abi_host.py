@@ -314,3 +314,60 @@ def test_out_epilogue_pass_validation(mutate, expected):
               out_scale=torch.zeros(4, 16, 16, dtype=torch.uint8).view(torch.float8_e8m0fnu))
     mutate(rows, out, kw)
     assert _lib.status_of_out_epilogue(rows[0], out[0], **kw) == expected, _lib.last_error()
+
+
+# ------------------------------------------------------------------ indexer
+
+def _ix_args(M=40, N=300):
+    return dict(q=torch.zeros(M, 32, 128, dtype=torch.float8_e4m3fn),
+                k=torch.zeros(N, 128, dtype=torch.float8_e4m3fn),
+                kv_scale=torch.ones(N), w=torch.zeros(M, 32), ks=torch.zeros(M, dtype=torch.int32),
+                ke=torch.zeros(M, dtype=torch.int32), logits=torch.zeros(M, N))
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: a.update(q=torch.zeros(40, 16, 128, dtype=torch.float8_e4m3fn)), UNSUP),
+    (lambda a: a.update(q=torch.zeros(40, 32, 64, dtype=torch.float8_e4m3fn)), UNSUP),
+    (lambda a: a.update(q=torch.zeros(40, 32, 128, dtype=torch.bfloat16)), UNSUP),
+    (lambda a: a.update(k=torch.zeros(300, 64, dtype=torch.float8_e4m3fn)), UNSUP),
+    (lambda a: a.update(kv_scale=torch.ones(299)), INVALID),
+    (lambda a: a.update(w=torch.zeros(40, 16)), INVALID),
+    (lambda a: a.update(w=torch.zeros(40, 34)[:, :32]), UNSUP),          # row stride 34
+    (lambda a: a.update(ks=torch.zeros(39, dtype=torch.int32)), INVALID),
+    (lambda a: a.update(ke=torch.zeros(40, dtype=torch.int64)), UNSUP),
+    (lambda a: a.update(logits=torch.zeros(40, 299)), INVALID),
+    (lambda a: a.update(logits=torch.zeros(40, 300, dtype=torch.float64)), UNSUP),
+    (lambda a: a.update(k=torch.zeros(300, 136, dtype=torch.float8_e4m3fn)[:, :128]), UNSUP),  # 136-B rows
+])
+def test_indexer_logits_validation(mutate, expected):
+    a = _ix_args()
+    mutate(a)
+    assert _lib.status_of_indexer_logits(**a) == expected, _lib.last_error()
+
+
+def test_indexer_logits_alias_and_noop():
+    a = _ix_args()
+    buf = torch.zeros(40 * 300 + 40 * 32)
+    a["w"] = buf[:40 * 32].view(40, 32)
+    a["logits"] = buf[:40 * 300].view(40, 300)                       # overlaps w
+    assert _lib.status_of_indexer_logits(**a) == INVALID
+    assert _lib.status_of_indexer_logits(**_ix_args(M=0)) == _lib.SMLA_OK
+    assert _lib.status_of_indexer_logits(**_ix_args(N=0)) == _lib.SMLA_OK
+    assert _lib.status_of_indexer_topk(torch.zeros(0, 10), torch.zeros(0, dtype=torch.int32),
+                                       torch.zeros(0, dtype=torch.int32), 4,
+                                       torch.zeros(0, 4, dtype=torch.int32)) == _lib.SMLA_OK
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: a.update(k=0), UNSUP),
+    (lambda a: a.update(k=70000), UNSUP),
+    (lambda a: a.update(indices=torch.zeros(8, 32, dtype=torch.int32)), INVALID),
+    (lambda a: a.update(indices=torch.zeros(8, 16, dtype=torch.int64)), UNSUP),
+    (lambda a: a.update(ks=torch.zeros(7, dtype=torch.int32)), INVALID),
+    (lambda a: a.update(logits=torch.zeros(8, 100, dtype=torch.bfloat16)), UNSUP),
+])
+def test_indexer_topk_validation(mutate, expected):
+    a = dict(logits=torch.zeros(8, 100), ks=torch.zeros(8, dtype=torch.int32),
+             ke=torch.zeros(8, dtype=torch.int32), k=16, indices=torch.zeros(8, 16, dtype=torch.int32))
+    mutate(a)
+    assert _lib.status_of_indexer_topk(**a) == expected, _lib.last_error()

@@ -1,0 +1,144 @@
+"""GPU checks of the indexer through the C ABI: fp8 MQA logits against the
+fp64 oracle, and the per-row top-k against the oracle's selection.
+
+Logits bar, per element: |gpu - ref| <= 2^-14 * A + 1e-30, with A =
+kv_scale[n] * sum_h |w[m,h]| * sum_d |q[m,h,d] k[n,d]| the magnitude the
+fp32 arithmetic works at (the MFMA's fp32 accumulation of 128 exact
+products, the 32-term head sum and two scalings: about 160 roundings of
+2^-24 relative to A, bounded here by 2^-14). Positions outside a row's window
+are exactly -inf with clean logits and untouched (the NaN poison stays)
+without. The top-k on seeded logits is integer work: bit-exact against the
+oracle (ascending indices, ties to the lower index, -1 padding). Outputs
+start NaN- or sentinel-poisoned.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import indexer as ix
+from sparse_mla_attention_05_amd import _lib
+from sparse_mla_attention_05_amd.inputs import (INDEXER_WORKLOADS, IndexerWorkload,
+                                                make_indexer_inputs, make_topk_logits)
+
+pytestmark = pytest.mark.gpu
+
+
+def _codes(t):
+    return t.view(torch.uint8).numpy()
+
+
+def run_logits(inp, clean=True):
+    M, N = inp.q.shape[0], inp.k.shape[0]
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    _lib.sparse_mla_indexer_logits(inp.q.cuda(), inp.k.cuda(), inp.kv_scale.cuda(), inp.w.cuda(),
+                                   inp.ks.cuda(), inp.ke.cuda(), out, clean=clean)
+    torch.cuda.synchronize()
+    return out
+
+
+def magnitude(inp, rows):
+    """A[m, n] = kv_scale[n] * sum_h |w| * sum_d |q k| for the sampled rows."""
+    q = np.abs(ix.decode_e4m3(_codes(inp.q)[rows]))          # [r, H, D]
+    k = np.abs(ix.decode_e4m3(_codes(inp.k)))                # [N, D]
+    w = np.abs(inp.w.numpy()[rows].astype(np.float64))       # [r, H]
+    wq = np.einsum("rh,rhd->rd", w, q)
+    return (wq @ k.T) * inp.kv_scale.numpy().astype(np.float64)[None, :]
+
+
+def assert_logits(got, inp, rows, clean=True):
+    ref = ix.mqa_logits(_codes(inp.q), _codes(inp.k), inp.kv_scale.numpy(), inp.w.numpy(),
+                        inp.ks.numpy(), inp.ke.numpy(), rows=rows)
+    g = got.cpu().numpy()[rows].astype(np.float64)
+    fin = np.isfinite(ref)
+    if clean:
+        assert np.all(g[~fin] == -np.inf), "outside the window: must be -inf"
+    else:
+        assert np.all(np.isnan(g[~fin])), "outside the window: must be left untouched"
+    a = magnitude(inp, rows)
+    err = np.abs(g[fin] - ref[fin])
+    bound = 2.0 ** -14 * a[fin] + 1e-30
+    assert np.all(err <= bound), f"worst err/bound {np.max(err / bound)}"
+    return dict(max_rel_to_A=float(np.max(err / np.maximum(a[fin], 1e-30))) if err.size else 0.0,
+                window_frac=float(fin.mean()))
+
+
+@pytest.mark.parametrize("clean", [True, False])
+def test_logits_tiny_all_rows(clean):
+    print(f"\n[indexer logits] ix_tiny clean={clean}", flush=True)
+    inp = make_indexer_inputs("ix_tiny")
+    inp.ks[3], inp.ke[3] = 50, 50              # an empty window
+    inp.ks[4], inp.ke[4] = -20, 700             # clipped at both ends
+    got = run_logits(inp, clean)
+    stats = assert_logits(got, inp, np.arange(inp.q.shape[0]), clean)
+    print(f"[indexer logits] {stats}", flush=True)
+
+
+@pytest.mark.parametrize("M,N", [(33, 4097), (1, 64), (64, 8200)])
+def test_logits_ragged_shapes(M, N):
+    """Row blocks and key columns with ragged tails, windows anywhere."""
+    print(f"\n[indexer logits] M={M} N={N}", flush=True)
+    inp = make_indexer_inputs(IndexerWorkload("r", rows=M, keys=N, requests=1, seed=M + N))
+    gen = torch.Generator().manual_seed(M * N)
+    a = torch.randint(-100, N, (M,), generator=gen)
+    b = a + torch.randint(0, N, (M,), generator=gen)
+    inp.ks, inp.ke = a.to(torch.int32), b.to(torch.int32)
+    got = run_logits(inp)
+    print(f"[indexer logits] {assert_logits(got, inp, np.arange(M))}", flush=True)
+
+
+@pytest.mark.parametrize("name", [n for n in INDEXER_WORKLOADS if n != "ix_tiny"])
+def test_logits_workloads_sampled_rows(name):
+    """The full workload in one call; the oracle checks 6 rows spread over it
+    (first, last, and rows at request boundaries)."""
+    print(f"\n[indexer logits] workload={name}", flush=True)
+    inp = make_indexer_inputs(name)
+    got = run_logits(inp)
+    M = inp.q.shape[0]
+    rows = np.unique(np.array([0, 31, 32, M // 4, M // 2 + 7, M - 1]))
+    print(f"[indexer logits] {name}: {assert_logits(got, inp, rows)}", flush=True)
+
+
+@pytest.mark.parametrize("R,N,k", [(30, 500, 64), (12, 5000, 2048), (6, 70000, 2048),
+                                   (18, 3000, 512)])
+def test_topk_equals_oracle(R, N, k):
+    print(f"\n[indexer topk] R={R} N={N} k={k}", flush=True)
+    x, ks, ke = make_topk_logits(R, N, seed=R + N, k=k)
+    out = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    _lib.sparse_mla_indexer_topk(x.cuda(), ks.cuda(), ke.cuda(), k, out)
+    torch.cuda.synchronize()
+    want = ix.topk_indices(x.numpy(), ks.numpy(), ke.numpy(), k)
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_topk_on_workload_logits():
+    """Top-2048 of a workload's logits, through the library end to end: the
+    selection against the oracle's logits allows a tie-break by the logits
+    bar. Every selected key's oracle logit is at least the oracle's k-th
+    value minus the bar; every unselected window key's at most that plus it."""
+    inp = make_indexer_inputs("ix_causal_8k_8k")
+    M = inp.q.shape[0]
+    k = inp.workload.topk
+    got = run_logits(inp)
+    out = torch.full((M, k), -7, dtype=torch.int32, device="cuda")
+    _lib.sparse_mla_indexer_topk(got, inp.ks.cuda(), inp.ke.cuda(), k, out)
+    torch.cuda.synchronize()
+    idx = out.cpu().numpy()
+    rows = np.array([0, 1000, 2047, 2048, 5000, M - 1])
+    ref = ix.mqa_logits(_codes(inp.q), _codes(inp.k), inp.kv_scale.numpy(), inp.w.numpy(),
+                        inp.ks.numpy(), inp.ke.numpy(), rows=rows)
+    a = magnitude(inp, rows)
+    for i, r in enumerate(rows):
+        lo, hi = int(inp.ks[r]), int(inp.ke[r])
+        sel = idx[r][idx[r] >= 0]
+        assert len(sel) == min(k, hi - lo) and len(np.unique(sel)) == len(sel)
+        assert np.all((sel >= lo) & (sel < hi)) and np.all(np.diff(sel) > 0)
+        assert np.all(idx[r][len(sel):] == -1)
+        if hi - lo <= k:
+            continue
+        v = ref[i, lo:hi]
+        thr = np.sort(v)[::-1][k - 1]
+        tol = 2.0 ** -13 * a[i, lo:hi].max()
+        chosen = np.zeros(hi - lo, bool)
+        chosen[sel - lo] = True
+        assert np.all(v[chosen] >= thr - tol) and np.all(v[~chosen] <= thr + tol)
