@@ -20,7 +20,9 @@ sliding window over a second pool with its own scale, next to the same
 workload's one-segment time) under "two_segment", and with the output
 epilogue (inverse RoPE of the last 64 columns and an MXFP8 store) fused into
 the forward's store, next to the plain forward followed by the separate
-epilogue pass, under "epilogue".
+epilogue pass, under "epilogue". The indexer that produces index rows (fp8
+MQA logits over [ks, ke) windows, then a per-row top-k) is timed on the
+shapes of its own kernel-time table under "indexer".
 """
 
 from __future__ import annotations
@@ -66,6 +68,9 @@ def parse():
                     help="comma list of workloads also timed with a sliding-window second "
                          "segment ('' for none)")
     ap.add_argument("--window", type=int, default=128, help="slots of that second segment")
+    ap.add_argument("--indexer", default="ix_causal_8k_8k,ix_causal_4k_32k,ix_causal_2k_64k,"
+                    "ix_causal_1k_128k,ix_multi_4k_32k",
+                    help="indexer workloads timed (fp8 MQA logits, then the top-k)")
     ap.add_argument("--epilogue", default="decode_bf16,decode_fp8",
                     help="workloads also timed with the fused inverse-RoPE + MXFP8 store")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -218,6 +223,57 @@ def time_workload(name, steps, warmup, cold, window=0, epi=None):
     return dict(inp=inp, plan=plan, times=times, wall=wall, warm_us=warm_us, alg=alg)
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, TFLOP/s
+
+
+def time_indexer(name, steps, warmup):
+    """Cold device time of the indexer logits (clean) and of the top-k over
+    them, for one workload."""
+    import torch
+    from sparse_mla_attention_05_amd import _lib
+    from sparse_mla_attention_05_amd.inputs import make_indexer_inputs
+
+    inp = make_indexer_inputs(name)
+    dev = torch.device("cuda:0")
+    q, k, sc, w = inp.q.to(dev), inp.k.to(dev), inp.kv_scale.to(dev), inp.w.to(dev)
+    ks, ke = inp.ks.to(dev), inp.ke.to(dev)
+    M, N = q.shape[0], k.shape[0]
+    logits = torch.empty((M, N), dtype=torch.float32, device=dev)
+    topk = inp.workload.topk
+    idx = torch.empty((M, topk), dtype=torch.int32, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    calls = {
+        "logits": lambda: _lib.sparse_mla_indexer_logits(q, k, sc, w, ks, ke, logits, True, stream=stream),
+        "topk": lambda: _lib.sparse_mla_indexer_topk(logits, ks, ke, topk, idx, stream=stream),
+    }
+    res = {}
+    for key, call in calls.items():
+        for _ in range(warmup):
+            call()
+        times = []
+        for _ in range(steps):
+            flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        res[key] = statistics.median(times)
+    lo = inp.ks.clamp(0, N).long()
+    hi = torch.maximum(inp.ke.clamp(0, N).long(), lo)
+    pairs = int((hi - lo).sum())
+    flops = 2 * pairs * inp.workload.heads * inp.workload.dim
+    tf = flops / (res["logits"] * 1e-6) / 1e12
+    return {"workload": name, "rows": M, "keys": N, "requests": inp.workload.requests,
+            "logits_us": round(res["logits"], 1), "topk_us": round(res["topk"], 1), "topk": topk,
+            "window_pairs": pairs, "tflops": round(tf, 1),
+            "mfma_fp8_frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4),
+            "logits_write_tbs": round(M * N * 4 / (res["logits"] * 1e-6) / 1e12, 2)}
+
+
 def cpu_baseline(inp, target_s):
     """Time the fp64 oracle as it stands on a bounded sample of rows (random
     order, cycling through the rows again if one pass takes less than
@@ -353,6 +409,10 @@ def main():
         del res
     if epis:
         line["epilogue"] = epis
+    ixs = [time_indexer(name, max(5, args.steps // 2), 2)
+           for name in [s for s in args.indexer.split(",") if s]]
+    if ixs:
+        line["indexer"] = ixs
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head["inp"], args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -5,13 +5,14 @@
 //   logits[m, n] = sum_h relu(Q[m,h,:] . K[n,:]) * w[m,h] * kv_scale[n]
 //                  for n in [ks[m], ke[m]), -inf elsewhere
 //
-// Logits kernel. A workgroup takes 32 query rows (8 waves x 4 rows) and one
+// Logits kernel. A workgroup takes 16 query rows (4 waves x 4 rows) and one
 // 4096-key column of the output; Q (4 rows x 32 heads x 128 fp8 = 64 VGPRs)
 // and w stay in registers, and all waves walk the same K sequence through
 // LDS (64-key stages, double-buffered, chunk-XOR swizzled rows), so K is read
-// once per 32 rows. One v_mfma_f32_16x16x128_f8f6f4 computes 16 heads x 16
-// keys over all 128 dims (A = Q rows, B = K rows, the same lane->k mapping on
-// both sides). A lane's accumulator holds heads 4g..4g+3 of one key; relu
+// once per 16 rows; two workgroups share a CU, so one wave's relu and head
+// sums run under the other's MFMAs. One v_mfma_f32_16x16x128_f8f6f4 computes
+// 16 heads x 16 keys over all 128 dims (A = Q rows, B = K rows, the same
+// lane->k mapping on both sides). A lane's accumulator holds heads 4g..4g+3 of one key; relu
 // and the head weight are applied there, the four lanes g of a key are summed
 // by two xor shuffles arranged as a butterfly over the wave's four rows
 // (afterwards lane g owns row g), and the key's scale is applied after the
@@ -32,25 +33,35 @@
 namespace smla {
 namespace {
 
-constexpr int kIxWaves = 8;
+constexpr int kIxWaves = 4;
 constexpr int kIxRowsPerWave = 4;
 constexpr int kIxRows = kIxWaves * kIxRowsPerWave;
 constexpr int kIxTile = 64;                    // keys per LDS stage
 constexpr int kIxTileBytes = kIxTile * kIxDim;  // 8 KB
+constexpr uint32_t kIxOutOfRange = 0xFFFFF000u;  // buffer offset past every range
+constexpr int kIxBufferWord3 = 0x00020000;      // raw buffer descriptor word 3 (gfx9 family)
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+
+// max(x, 0) as one integer max: a negative float is a negative int32 and
+// -0.0 becomes +0.0 (fmaxf would first quiet NaNs, a second instruction).
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
 
 __device__ __forceinline__ v8i cat(u32x4 a, u32x4 b) {
   return v8i{int(a.x), int(a.y), int(a.z), int(a.w), int(b.x), int(b.y), int(b.z), int(b.w)};
 }
 
-__global__ void __launch_bounds__(kIxWaves * 64, 2) ix_logits_kernel(const IxParams p) {
+__global__ void __launch_bounds__(kIxWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+ix_logits_kernel(const IxParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][kIxTileBytes];
   __shared__ float ksc[2][kIxTile];
   __shared__ int wlo[kIxWaves], whi[kIxWaves];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar row base
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t m0 = int64_t(blockIdx.x) * kIxRows + kIxRowsPerWave * wave;
   const int n_begin = int(blockIdx.y) * kIxChunk;
@@ -83,7 +94,7 @@ __global__ void __launch_bounds__(kIxWaves * 64, 2) ix_logits_kernel(const IxPar
     }
   }
 
-  // ---- keys any of the 32 rows sees inside this column: whole tiles only.
+  // ---- keys any of the workgroup's rows sees inside this column: whole tiles.
   int ulo = p.n, uhi = 0;
 #pragma unroll
   for (int j = 0; j < kIxRowsPerWave; ++j)
@@ -120,30 +131,48 @@ __global__ void __launch_bounds__(kIxWaves * 64, 2) ix_logits_kernel(const IxPar
   }
   if (ntiles == 0) return;
 
-  // ---- K staging: thread t moves 16 bytes (key t/8, chunk t%8) of a tile;
-  // physical chunk = chunk ^ (key & 7).
+  // ---- K staging: thread t moves 16-byte pieces (key, chunk) = (t/8 + 32i,
+  // t%8) of a tile; physical chunk = chunk ^ (key & 7). K and the key scales
+  // are read through buffer resources whose ranges end at key N, so a piece
+  // past the last key reads 0 without a branch; two tiles are in flight.
+  constexpr int NT = kIxWaves * 64;
+  constexpr int SPT = kIxTileBytes / 16 / NT;  // pieces per thread
   const int skey = tid >> 3, schunk = tid & 7;
-  const int sdst = skey * kIxDim + 16 * (schunk ^ (skey & 7));
-  auto load_tile = [&](int n0, u32x4& v, float& sc) {
-    const int n = n0 + skey;
-    v = n < p.n ? *reinterpret_cast<const u32x4*>(p.k + int64_t(n) * p.k_rs + 16 * schunk)
-                : u32x4{0u, 0u, 0u, 0u};
-    sc = (tid < kIxTile && n0 + tid < p.n) ? p.kv_scale[n0 + tid] : 0.f;
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.k), 0, uint32_t(int64_t(p.n) * p.k_rs), kIxBufferWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.kv_scale), 0, uint32_t(4 * p.n), kIxBufferWord3);
+  // Offsets go in the per-lane operand (the range check covers it; the
+  // scalar offset is not checked).
+  auto load_tile = [&](int n0, u32x4 (&v)[SPT], float& sc) {
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const uint32_t key = uint32_t(n0 + skey + (NT / 8) * i);
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           k_rsrc, key * uint32_t(p.k_rs) + 16u * uint32_t(schunk), 0, 0));
+    }
+    sc = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, tid < kIxTile ? 4u * uint32_t(n0 + tid) : 0u, 0, 0));
   };
-  u32x4 pre;
-  float psc;
-  load_tile(t_first, pre, psc);
-  *reinterpret_cast<u32x4*>(&kt[0][sdst]) = pre;
-  if (tid < kIxTile) ksc[0][tid] = psc;
-  __syncthreads();
+  auto store_tile = [&](int b, const u32x4 (&v)[SPT], float sc) {
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int key = skey + (NT / 8) * i;
+      *reinterpret_cast<u32x4*>(&kt[b][key * kIxDim + 16 * (schunk ^ (key & 7))]) = v[i];
+    }
+    if (tid < kIxTile) ksc[b][tid] = sc;
+  };
 
-  const int64_t my_m = m0 + g;
-  float* const my_row = p.logits + (my_m < p.m ? my_m : 0) * p.l_rs;
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int n0 = t_first + it * kIxTile;
-    const bool more = it + 1 < ntiles;
-    if (more) load_tile(n0 + kIxTile, pre, psc);
+  // ---- logits: this wave's 4 rows through one buffer resource (rows past M
+  // and dropped positions get an offset past its range, so stores need no
+  // branch); lane group g stores row g.
+  const int rv = int(min<int64_t>(kIxRowsPerWave, p.m - m0));  // valid rows of the wave (>= 0)
+  const __amdgpu_buffer_rsrc_t l_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      p.logits + (m0 < p.m ? m0 : 0) * p.l_rs, 0,
+      rv > 0 ? uint32_t(4 * (int64_t(rv - 1) * p.l_rs + p.n)) : 0u, kIxBufferWord3);
+  const uint32_t row_off = 4u * uint32_t(g) * uint32_t(p.l_rs);
+
+  auto compute = [&](int buf, int n0) {
     const uint8_t* tile = kt[buf];
 #pragma unroll
     for (int kb = 0; kb < kIxTile / 16; ++kb) {
@@ -152,6 +181,8 @@ __global__ void __launch_bounds__(kIxWaves * 64, 2) ix_logits_kernel(const IxPar
       const u32x4 b0 = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * g) ^ (key & 7)));
       const u32x4 b1 = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * g + 1) ^ (key & 7)));
       const v8i kb8 = cat(b0, b1);
+      float sc = ksc[buf][key];
+      asm volatile("" : "+v"(sc));  // read unconditionally: no branch around the LDS read
       float part[kIxRowsPerWave];
 #pragma unroll
       for (int j = 0; j < kIxRowsPerWave; ++j) {
@@ -163,8 +194,8 @@ __global__ void __launch_bounds__(kIxWaves * 64, 2) ix_logits_kernel(const IxPar
         float a = 0.f, b = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          a = __builtin_fmaf(fmaxf(s0[i], 0.f), wv[j][0][i], a);
-          b = __builtin_fmaf(fmaxf(s1[i], 0.f), wv[j][1][i], b);
+          a = __builtin_fmaf(relu(s0[i]), wv[j][0][i], a);
+          b = __builtin_fmaf(relu(s1[i]), wv[j][1][i], b);
         }
         part[j] = a + b;
       }
@@ -175,17 +206,33 @@ __global__ void __launch_bounds__(kIxWaves * 64, 2) ix_logits_kernel(const IxPar
       const float qb0 = (b0s ? part[3] : part[2]) + __shfl_xor(b0s ? part[2] : part[3], 16);
       const float tot = (b1s ? qb0 : qa0) + __shfl_xor(b1s ? qa0 : qb0, 32);
       const int n = n0 + key;
-      if (my_m < p.m && n < t_stop) {
-        if (n >= my_lo && n < my_hi)
-          my_row[n] = tot * ksc[buf][key];
-        else if (p.clean)
-          my_row[n] = kNegInf;
-      }
+      const bool inside = n >= my_lo && n < my_hi;
+      const bool write = n < t_stop && (inside || p.clean != 0);
+      const float val = inside ? tot * sc : kNegInf;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), l_rsrc,
+                                            write ? row_off + 4u * uint32_t(n) : kIxOutOfRange, 0, 0);
     }
-    if (more) {
-      *reinterpret_cast<u32x4*>(&kt[buf ^ 1][sdst]) = pre;
-      if (tid < kIxTile) ksc[buf ^ 1][tid] = psc;
-    }
+  };
+
+  u32x4 pa[SPT], pb[SPT];
+  float sa, sb;
+  load_tile(t_first, pa, sa);
+  if (ntiles > 1) load_tile(t_first + kIxTile, pb, sb);
+  store_tile(0, pa, sa);
+  __syncthreads();
+  // Tile t's staging registers: pa for even t, pb for odd t. Iteration t
+  // loads tile t + 2 into the set tile t left, computes tile t, then moves
+  // tile t + 1 into the other LDS buffer.
+  for (int it = 0; it < ntiles; it += 2) {
+    const int n0 = t_first + it * kIxTile;
+    if (it + 2 < ntiles) load_tile(n0 + 2 * kIxTile, pa, sa);
+    compute(0, n0);
+    if (it + 1 < ntiles) store_tile(1, pb, sb);
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    if (it + 3 < ntiles) load_tile(n0 + 3 * kIxTile, pb, sb);
+    compute(1, n0 + kIxTile);
+    if (it + 2 < ntiles) store_tile(0, pa, sa);
     __syncthreads();
   }
 }
