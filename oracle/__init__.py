@@ -6,6 +6,7 @@ from .sparse_mla_oracle import (  # noqa: F401
     D_V,
     attend_row,
     bf16_bits_to_f64,
+    decode_q,
     decode_rows,
     e4m3fn_table,
     lse_combine,

@@ -137,18 +137,32 @@ def attend_row(q_row: np.ndarray, gathered: np.ndarray, sm: float) -> tuple[np.n
     return out, lse
 
 
+def decode_q(q_raw: np.ndarray, q_scale: float | None) -> np.ndarray:
+    """fp64 values of q: bf16 bit patterns (uint16), or float8_e4m3fn codes
+    (uint8) times the per-tensor q scale ("an fp8 q is widened in the
+    kernel", commit notes on the two-loop route of "[Triton/Gluon] GFX950
+    sparse mla optimizations"; value = code * q_scale, as for the cache)."""
+    q_raw = np.asarray(q_raw)
+    if q_raw.dtype == np.uint8:
+        return e4m3fn_table()[q_raw] * (1.0 if q_scale is None else float(np.float32(q_scale)))
+    return bf16_bits_to_f64(q_raw)
+
+
 def sparse_mla_fwd(q_bits: np.ndarray, pool_raw: np.ndarray, kv_dtype: str,
                    kv_scale: float | None, indices: np.ndarray, sm_scale: float,
-                   rows: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+                   rows: np.ndarray | None = None,
+                   q_scale: float | None = None) -> tuple[np.ndarray, np.ndarray]:
     """Sparse MLA forward in fp64.
 
-    q_bits   : uint16 [R, H, D_qk] bf16 bit patterns of q
+    q_bits   : uint16 [R, H, D_qk] bf16 bit patterns of q, or uint8 e4m3fn
+               codes of an fp8 q (value = code * q_scale)
     pool_raw : uint16 [N, >=D_qk] bf16 bits, or uint8 [N, >=D_qk] e4m3fn codes
     kv_dtype : "bf16" or "fp8"
     kv_scale : fp32 per-tensor scale for fp8 pools (None for bf16)
     indices  : int32 [R, K]; negative = invalid slot
     sm_scale : softmax scale (used as its fp32 value)
     rows     : optional subset of query rows to compute (for big workloads)
+    q_scale  : fp32 per-tensor scale of an fp8 q (None: 1)
 
     Returns (out fp64 [len(rows), H, 512], lse fp64 [len(rows), H]).
     """
@@ -170,18 +184,27 @@ def sparse_mla_fwd(q_bits: np.ndarray, pool_raw: np.ndarray, kv_dtype: str,
         if valid.max() >= n_pool:
             raise IndexError(f"row {r}: index {int(valid.max())} >= pool rows {n_pool}")
         gathered = decode_rows(pool_raw, valid, d_qk, kv_dtype, kv_scale)
-        out[i], lse[i] = attend_row(bf16_bits_to_f64(q_bits[r]), gathered, sm)
+        out[i], lse[i] = attend_row(decode_q(q_bits[r], q_scale), gathered, sm)
     return out, lse
 
 
-def sparse_mla_fwd_torch(q, pool, kv_scale, indices, sm_scale, rows=None):
-    """Convenience wrapper taking CPU torch tensors (bf16 q; bf16 or e4m3fn pool).
+def _q_raw(q):
+    import torch  # local: the oracle itself is numpy-only
+    if q.dtype == torch.float8_e4m3fn:
+        return q.contiguous().view(torch.uint8).numpy()
+    return q.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def sparse_mla_fwd_torch(q, pool, kv_scale, indices, sm_scale, rows=None, q_scale=None):
+    """Convenience wrapper taking CPU torch tensors (bf16 or e4m3fn q with
+    q_scale; bf16 or e4m3fn pool).
 
     Only views raw bytes; all arithmetic is in ``sparse_mla_fwd``.
     """
     import torch  # local: the oracle itself is numpy-only
 
-    q_bits = q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    q_bits = _q_raw(q)
+    qs = None if q_scale is None else float(q_scale.reshape(-1)[0])
     if pool.dtype == torch.bfloat16:
         kv_dtype, raw, s = "bf16", pool.view(torch.int16).numpy().view(np.uint16), None
     elif pool.dtype == torch.float8_e4m3fn:
@@ -189,7 +212,8 @@ def sparse_mla_fwd_torch(q, pool, kv_scale, indices, sm_scale, rows=None):
         s = float(kv_scale.reshape(-1)[0])
     else:
         raise ValueError(f"unsupported pool dtype {pool.dtype}")
-    return sparse_mla_fwd(q_bits, raw, kv_dtype, s, indices.numpy(), sm_scale, rows=rows)
+    return sparse_mla_fwd(q_bits, raw, kv_dtype, s, indices.numpy(), sm_scale, rows=rows,
+                          q_scale=qs)
 
 
 # ------------------------------------------------------------ two segments ---
@@ -198,8 +222,9 @@ def sparse_mla_fwd_2seg(q_bits: np.ndarray, pool_raw: np.ndarray, kv_dtype: str,
                         kv_scale: float | None, indices: np.ndarray,
                         extra_raw: np.ndarray, extra_scale: float | None,
                         extra_indices: np.ndarray, sm_scale: float,
-                        rows: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
-    """Two-segment sparse MLA forward in fp64.
+                        rows: np.ndarray | None = None,
+                        q_scale: float | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Two-segment sparse MLA forward in fp64 (q as for sparse_mla_fwd).
 
     After "[Triton/Gluon] GFX950 sparse mla optimizations" (aiter PR 6159),
     commit notes on the per-tensor fp8 two-loop route: a row attends under
@@ -235,17 +260,18 @@ def sparse_mla_fwd_2seg(q_bits: np.ndarray, pool_raw: np.ndarray, kv_dtype: str,
             parts.append(decode_rows(raw, valid, d_qk, kv_dtype, scale))
         if not parts:
             continue
-        out[i], lse[i] = attend_row(bf16_bits_to_f64(q_bits[r]), np.concatenate(parts), sm)
+        out[i], lse[i] = attend_row(decode_q(q_bits[r], q_scale), np.concatenate(parts), sm)
     return out, lse
 
 
 def sparse_mla_fwd_2seg_torch(q, pool, kv_scale, indices, extra_pool, extra_scale,
-                              extra_indices, sm_scale, rows=None):
+                              extra_indices, sm_scale, rows=None, q_scale=None):
     """Wrapper of ``sparse_mla_fwd_2seg`` taking CPU torch tensors. Only views
     raw bytes; all arithmetic is in ``sparse_mla_fwd_2seg``."""
     import torch  # local: the oracle itself is numpy-only
 
-    q_bits = q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    q_bits = _q_raw(q)
+    qs = None if q_scale is None else float(q_scale.reshape(-1)[0])
     if pool.dtype == torch.bfloat16:
         kv_dtype = "bf16"
         raw = pool.view(torch.int16).numpy().view(np.uint16)
@@ -259,7 +285,7 @@ def sparse_mla_fwd_2seg_torch(q, pool, kv_scale, indices, extra_pool, extra_scal
     else:
         raise ValueError(f"unsupported pool dtype {pool.dtype}")
     return sparse_mla_fwd_2seg(q_bits, raw, kv_dtype, s1, indices.numpy(), xraw, s2,
-                               extra_indices.numpy(), sm_scale, rows=rows)
+                               extra_indices.numpy(), sm_scale, rows=rows, q_scale=qs)
 
 
 # ----------------------------------------------------- split combination ---

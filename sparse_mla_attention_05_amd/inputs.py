@@ -458,3 +458,9 @@ def make_topk_logits(rows: int, keys: int, seed: int, k: int) -> tuple[torch.Ten
         x[r, :ks[r]] = float("nan")
         x[r, ke[r]:] = float("nan")
     return x.to(torch.float32), ks.to(torch.int32), ke.to(torch.int32)
+
+
+def make_fp8_q(inp: Inputs) -> tuple[torch.Tensor, torch.Tensor]:
+    """An fp8 q for the same call: the workload's q quantised to e4m3fn with
+    one per-tensor scale (max|q| / 448), the way the cache is."""
+    return quantize_fp8(inp.q.to(torch.float32))

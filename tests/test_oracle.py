@@ -473,11 +473,49 @@ def test_planted_mask_mistake_is_caught(monkeypatch):
     inp.indices = idx
     real = orc.sparse_mla_fwd
 
-    def mutant(q_bits, pool_raw, kv_dtype, kv_scale, indices, sm_scale, rows=None):
+    def mutant(q_bits, pool_raw, kv_dtype, kv_scale, indices, sm_scale, rows=None, q_scale=None):
         ind = np.where(indices == 0, -1, indices)
-        return real(q_bits, pool_raw, kv_dtype, kv_scale, ind, sm_scale, rows=rows)
+        return real(q_bits, pool_raw, kv_dtype, kv_scale, ind, sm_scale, rows=rows, q_scale=q_scale)
 
     monkeypatch.setattr(orc, "sparse_mla_fwd", mutant)
     out, _ = orc.sparse_mla_fwd_torch(inp.q, inp.pool, inp.kv_scale, inp.indices, inp.sm_scale)
     bo, _ = _brute_force(inp)
     assert _rel(out, bo) > 1e-6
+
+
+# ------------------------------------------------------------------ fp8 q
+
+def test_fp8_q_is_scale_folding_of_a_bf16_q():
+    """An fp8 q with scale s attends like a bf16 q holding the codes' values
+    (every e4m3fn value is a bf16 value) with sm_scale * s."""
+    from sparse_mla_attention_05_amd.inputs import make_fp8_q
+    inp = make_inputs(custom_workload(rows=5, heads=16, d_qk=576, pool_rows=2000, topk=100,
+                                      kv_dtype="fp8", seed=8, invalid_per_row=3))
+    q8, _ = make_fp8_q(inp)
+    qs = torch.tensor([2.0 ** -5])   # a power of two: sm_scale * s stays exact in fp32
+    a_out, a_lse = oracle.sparse_mla_fwd_torch(q8, inp.pool, inp.kv_scale, inp.indices,
+                                               inp.sm_scale, q_scale=qs)
+    q_as_bf16 = q8.to(torch.float32).to(torch.bfloat16)          # exact
+    assert torch.equal(q_as_bf16.to(torch.float32), q8.to(torch.float32))
+    sm = float(np.float32(inp.sm_scale)) * float(qs[0])
+    b_out, b_lse = oracle.sparse_mla_fwd_torch(q_as_bf16, inp.pool, inp.kv_scale, inp.indices, sm)
+    assert np.allclose(a_out, b_out, rtol=1e-12, atol=1e-14)
+    assert np.allclose(a_lse, b_lse, rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_q_brute_force():
+    from sparse_mla_attention_05_amd.inputs import make_fp8_q
+    inp = make_inputs(custom_workload(rows=4, heads=16, d_qk=512, pool_rows=1500, topk=80,
+                                      kv_dtype="bf16", seed=9, invalid_per_row=2))
+    q8, qs = make_fp8_q(inp)
+    got, got_lse = oracle.sparse_mla_fwd_torch(q8, inp.pool, None, inp.indices, inp.sm_scale,
+                                               q_scale=qs)
+    q = q8.to(torch.float64) * float(qs[0])
+    sm = float(np.float32(inp.sm_scale))
+    for r in range(4):
+        idx = inp.indices[r][inp.indices[r] >= 0].long()
+        kv = inp.pool[idx, :512].to(torch.float64)
+        s = sm * (q[r] @ kv.T)
+        w = torch.softmax(s, dim=-1)
+        assert np.allclose(got[r], (w @ kv).numpy(), rtol=1e-10, atol=1e-12)
+        assert np.allclose(got_lse[r], torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12)
