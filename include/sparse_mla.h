@@ -69,7 +69,8 @@ typedef struct smla_tensor {
   int64_t stride[3];
 } smla_tensor;
 
-/* Overrides for tests and benchmarks; zero-initialise for the defaults. */
+/* Optional call parameters (planner overrides for tests and benchmarks, a
+ * caller workspace, the scale of an fp8 q); zero-initialise for the defaults. */
 typedef struct smla_options {
   int32_t head_block;      /* 0 = planner's choice, else 16, 32 or 64 heads per workgroup */
   int32_t splits;          /* 0 = planner's choice, else 1..64 splits of each row's slots */
@@ -83,6 +84,8 @@ typedef struct smla_options {
                               with the QK and PV work on separate wavefronts */
   void* workspace;         /* optional caller device buffer for split partials */
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
+  const void* q_scale;     /* fp32 [1] device pointer: per-tensor scale of a float8_e4m3fn q
+                              (value = code * q_scale; NULL = 1). Must be NULL for a bf16 q */
 } smla_options;
 
 /* What the planner picked for a call (sparse_mla_plan). */
@@ -104,11 +107,20 @@ typedef struct smla_plan {
 /*
  * sparse_mla_fwd - the forward pass.
  *
- *  q        bf16 [R, H, D_qk]; last dim contiguous; row and head strides free.
+ *  q        bf16 [R, H, D_qk], or float8_e4m3fn codes with a per-tensor scale
+ *           (smla_options.q_scale, through the _ex/2/_epi entry points), widened
+ *           exactly to bf16 in the kernels with the scale applied to the scores
+ *           (commit notes on the two-loop route: an fp8 q is widened in the
+ *           kernel); last dim contiguous; base and strides 16-byte aligned.
  *  kv_pool  bf16 or fp8 e4m3fn [N, W], W >= D_qk (only the first D_qk columns
  *           are read, so a padded row pitch needs no copy); last dim
  *           contiguous; the row stride in bytes must be a multiple of 16 and
- *           the base 16-byte aligned.
+ *           the base 16-byte aligned. Or paged, [P, B, W] with B a power of
+ *           two: slot index i is row i % B of page i / B, with the page pitch
+ *           stride[0] (>= one page, a multiple of 16 bytes) free, so a pool
+ *           whose pages are padded needs no copy either (commit notes on the
+ *           two-loop route: the launcher keeps a padded [nb, block, R] pool
+ *           paged). N = P * B.
  *  kv_scale fp32 [1] device pointer, given iff kv_pool is fp8 (NULL for bf16).
  *  indices  int32 [R, K]; last dim contiguous; any negative value is an
  *           invalid slot. Values >= N are a caller error: not checked on the
@@ -152,7 +164,7 @@ SMLA_API int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
  *   = i >= 0 }, out = softmax(sm_scale * q . k) V, lse = ln sum exp(...).
  *
  *  extra_pool      same dtype as kv_pool, [N2, W2] with W2 >= D_qk, same
- *                  alignment rules; its own rows and row stride.
+ *                  alignment rules; its own rows and row stride (2-D only).
  *  extra_kv_scale  fp32 [1] device pointer for an fp8 pool; NULL means the
  *                  extra segment uses kv_scale. Must be NULL for bf16 pools.
  *  extra_indices   int32 [R, K2], K2 in [1, 2^20]; negative = invalid slot.

@@ -36,7 +36,8 @@ class SmlaTensor(ctypes.Structure):
 class SmlaOptions(ctypes.Structure):
     _fields_ = [("head_block", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("remap", ctypes.c_int32), ("variant", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+                ("q_scale", ctypes.c_void_p)]
 
 
 class SmlaPlan(ctypes.Structure):
@@ -160,9 +161,12 @@ def _check(status: int):
         raise SparseMLAError(status, last_error())
 
 
-def _options(head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None, variant=0):
+def _options(head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None, variant=0,
+             q_scale=None):
     o = SmlaOptions()
     o.head_block, o.splits, o.remap, o.variant = head_block, splits, remap, variant
+    if q_scale is not None:
+        o.q_scale = q_scale.data_ptr()
     if workspace is not None:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size() \
@@ -181,13 +185,13 @@ def sparse_mla_fwd(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=Non
 
 def sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None,
                       head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None,
-                      variant=0) -> None:
+                      variant=0, q_scale=None) -> None:
     """sparse_mla_fwd with planner overrides (head_block 16/32/64, splits,
     remap 1 = XCD-aware / 2 = grid order, kernel variant) and an optional
     caller workspace."""
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, out, lse)]
-    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale)
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd_ex(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), _ptr(ds[3]),
                                  float(sm_scale), _ptr(ds[4]), _ptr(ds[5]), st, ctypes.byref(opt)))
@@ -230,14 +234,14 @@ def sparse_mla_plan(q, kv_pool, indices, head_block=0, splits=0, remap=0, num_cu
 
 def sparse_mla_fwd2(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices,
                     sm_scale, out, lse, stream=None, head_block=0, splits=0, remap=0,
-                    workspace=None, workspace_bytes=None, variant=0) -> None:
+                    workspace=None, workspace_bytes=None, variant=0, q_scale=None) -> None:
     """Two-segment forward: one softmax over the valid slots of `indices` into
     kv_pool (scale kv_scale) and of `extra_indices` into extra_pool (scale
     extra_kv_scale, or kv_scale when None for fp8 pools)."""
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale,
                                 extra_indices, out, lse)]
-    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale)
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd2(*[_ptr(d) for d in ds[:7]], float(sm_scale), _ptr(ds[7]),
                                _ptr(ds[8]), st, ctypes.byref(opt)))
@@ -298,7 +302,7 @@ def _epilogue(rope_positions=None, rope_cos_sin=None, out_scale=None):
 def sparse_mla_fwd_epi(q, kv_pool, kv_scale, indices, sm_scale, out, lse, rope_positions=None,
                        rope_cos_sin=None, out_scale=None, extra_pool=None, extra_kv_scale=None,
                        extra_indices=None, stream=None, head_block=0, splits=0, remap=0,
-                       workspace=None, workspace_bytes=None, variant=0) -> None:
+                       workspace=None, workspace_bytes=None, variant=0, q_scale=None) -> None:
     """Forward whose final store applies the output epilogue: inverse RoPE of
     columns 448..511 (rope_positions int32 [R], rope_cos_sin fp32 [P, 64]) and,
     with out_scale (float8_e8m0fnu [R, H, 16]), an MXFP8 store of float8_e4m3fn
@@ -307,7 +311,7 @@ def sparse_mla_fwd_epi(q, kv_pool, kv_scale, indices, sm_scale, out, lse, rope_p
     ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale,
                                 extra_indices, out, lse)]
     epi, _keep = _epilogue(rope_positions, rope_cos_sin, out_scale)
-    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale)
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd_epi(*[_ptr(d) for d in ds[:7]], float(sm_scale), ctypes.byref(epi),
                                   _ptr(ds[7]), _ptr(ds[8]), st, ctypes.byref(opt)))

@@ -93,20 +93,32 @@ bool overlap(const smla_tensor* a, const smla_tensor* b) {
 struct Checked {
   Problem pb;
   bool fp8;
+  bool q_fp8;
 };
 
 // q / kv_pool / indices: shapes, dtypes, strides, alignment.
 int validate_inputs(const smla_tensor* q, const smla_tensor* kv, const smla_tensor* idx,
                     Checked* c) {
   int s;
-  if ((s = check_tensor(q, "q", 3, SMLA_BF16))) return s;
+  if (!q) return fail(SMLA_ERR_INVALID_ARG, "q: null descriptor");
+  if (q->dtype != SMLA_BF16 && q->dtype != SMLA_FP8_E4M3FN)
+    return fail(SMLA_ERR_UNSUPPORTED, std::string("q: dtype ") + dtype_name(q->dtype) +
+                                          " (code " + std::to_string(q->dtype) +
+                                          ") not supported, expected bf16 or fp8_e4m3fn");
+  if ((s = check_tensor(q, "q", 3, q->dtype))) return s;
   if (!kv) return fail(SMLA_ERR_INVALID_ARG, "kv_pool: null descriptor");
   if (kv->dtype != SMLA_BF16 && kv->dtype != SMLA_FP8_E4M3FN)
     return fail(SMLA_ERR_UNSUPPORTED, std::string("kv_pool: dtype ") + dtype_name(kv->dtype) +
                                           " (code " + std::to_string(kv->dtype) +
                                           ") not supported, expected bf16 or fp8_e4m3fn");
-  if ((s = check_tensor(kv, "kv_pool", 2, kv->dtype))) return s;
+  // [N, W], or paged [pages, page rows, W] with its own page pitch
+  const bool paged = kv->ndim == 3;
+  if ((s = check_tensor(kv, "kv_pool", paged ? 3 : 2, kv->dtype))) return s;
   if ((s = check_tensor(idx, "indices", 2, SMLA_INT32))) return s;
+  const int64_t page_rows = paged ? kv->shape[1] : 1;
+  const int64_t N = paged ? kv->shape[0] * kv->shape[1] : kv->shape[0];
+  const int64_t W = paged ? kv->shape[2] : kv->shape[1];
+  const int64_t rs = paged ? kv->stride[1] : kv->stride[0];  // row stride (elements)
 
   const int64_t R = q->shape[0], H = q->shape[1], D = q->shape[2];
   if (D != 576 && D != 512)
@@ -120,33 +132,52 @@ int validate_inputs(const smla_tensor* q, const smla_tensor* kv, const smla_tens
   if (K < 1 || K > kMaxTopk)
     return fail(SMLA_ERR_UNSUPPORTED, "indices: top-k must be in [1, 2^20], got " +
                                           std::to_string(K));
-  if (kv->shape[1] < D)
-    return fail(SMLA_ERR_INVALID_ARG, "kv_pool: row width " + std::to_string(kv->shape[1]) +
+  if (W < D)
+    return fail(SMLA_ERR_INVALID_ARG, "kv_pool: row width " + std::to_string(W) +
                                           " < D_qk " + std::to_string(D));
-  if (R > 0 && kv->shape[0] < 1) return fail(SMLA_ERR_INVALID_ARG, "kv_pool: no rows");
+  if (R > 0 && N < 1) return fail(SMLA_ERR_INVALID_ARG, "kv_pool: no rows");
+  if (paged && (page_rows < 1 || (page_rows & (page_rows - 1)) != 0))
+    return fail(SMLA_ERR_UNSUPPORTED, "kv_pool: rows per page must be a power of two");
   if (R > 0) {
     if (!q->data) return fail(SMLA_ERR_INVALID_ARG, "q: null data");
     if (!kv->data) return fail(SMLA_ERR_INVALID_ARG, "kv_pool: null data");
     if (!idx->data) return fail(SMLA_ERR_INVALID_ARG, "indices: null data");
   }
   const int eb = elem_size(kv->dtype);
-  if (kv->shape[0] > 1 && kv->stride[0] < kv->shape[1])
-    return fail(SMLA_ERR_INVALID_ARG, "kv_pool: row stride smaller than row width");
-  if (!aligned16(kv->data) || (kv->stride[0] * eb) % 16 != 0)
+  if (page_rows > 1 || !paged) {
+    if ((paged ? page_rows : N) > 1 && rs < W)
+      return fail(SMLA_ERR_INVALID_ARG, "kv_pool: row stride smaller than row width");
+    if ((rs * eb) % 16 != 0)
+      return fail(SMLA_ERR_UNSUPPORTED, "kv_pool: base and row stride must be 16-byte aligned");
+  }
+  if (paged && kv->shape[0] > 1) {
+    if (kv->stride[0] < page_rows * (page_rows > 1 ? rs : W))
+      return fail(SMLA_ERR_INVALID_ARG, "kv_pool: page pitch smaller than a page");
+    if ((kv->stride[0] * eb) % 16 != 0)
+      return fail(SMLA_ERR_UNSUPPORTED, "kv_pool: page pitch must be 16-byte aligned");
+  }
+  if (!aligned16(kv->data))
     return fail(SMLA_ERR_UNSUPPORTED, "kv_pool: base and row stride must be 16-byte aligned");
-  if (!aligned16(q->data) || (q->stride[0] * 2) % 16 != 0 || (q->stride[1] * 2) % 16 != 0)
+  const int qb = elem_size(q->dtype);
+  if (!aligned16(q->data) || (q->stride[0] * qb) % 16 != 0 || (q->stride[1] * qb) % 16 != 0)
     return fail(SMLA_ERR_UNSUPPORTED, "q: base, row and head strides must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(idx->data) & 3u) != 0)
     return fail(SMLA_ERR_INVALID_ARG, "indices: base must be 4-byte aligned");
-  if (kv->shape[0] > (int64_t(1) << 31))
-    return fail(SMLA_ERR_UNSUPPORTED, "kv_pool: more than 2^31 rows");
+  if (N > (int64_t(1) << 31)) return fail(SMLA_ERR_UNSUPPORTED, "kv_pool: more than 2^31 rows");
   c->pb.rows = R;
   c->pb.heads = int32_t(H);
   c->pb.dqk = int32_t(D);
   c->pb.topk = int32_t(K);
   c->pb.kv_fp8 = kv->dtype == SMLA_FP8_E4M3FN;
   c->fp8 = c->pb.kv_fp8 != 0;
-  c->pb.pool_bytes = kv->shape[0] > 0 ? (kv->shape[0] - 1) * kv->stride[0] * eb + D * eb : 0;
+  c->q_fp8 = q->dtype == SMLA_FP8_E4M3FN;
+  // bytes from the base to the end of the last row read
+  if (N == 0)
+    c->pb.pool_bytes = 0;
+  else if (paged)
+    c->pb.pool_bytes = ((kv->shape[0] - 1) * kv->stride[0] + (page_rows - 1) * rs + D) * eb;
+  else
+    c->pb.pool_bytes = ((N - 1) * rs + D) * eb;
   return SMLA_OK;
 }
 
@@ -240,6 +271,16 @@ int device_cus(int dev) {
   return g_cu_count[dev];
 }
 
+// The per-tensor scale of an fp8 q (options): NULL means 1; a bf16 q takes
+// none.
+int check_q_scale(const Checked& c, const smla_options* opt) {
+  const void* qs = opt ? opt->q_scale : nullptr;
+  if (qs && !c.q_fp8) return fail(SMLA_ERR_INVALID_ARG, "q_scale: must be NULL for a bf16 q");
+  if (qs && (reinterpret_cast<uintptr_t>(qs) & 3u))
+    return fail(SMLA_ERR_INVALID_ARG, "q_scale: must be 4-byte aligned");
+  return SMLA_OK;
+}
+
 // dtype of `out` under an epilogue: e4m3fn codes with an MXFP8 scale tensor,
 // else bf16.
 int32_t epi_out_dtype(const smla_epilogue* epi) {
@@ -320,7 +361,20 @@ FwdParams segment_params(const smla_tensor* q, const smla_tensor* pool, const fl
   p.q_rs = q->stride[0];
   p.q_hs = q->stride[1];
   p.pool = static_cast<const uint8_t*>(pool->data);
-  p.pool_rs_bytes = pool->stride[0] * elem_size(pool->dtype);
+  const int eb = elem_size(pool->dtype);
+  if (pool->ndim == 3) {  // paged: slot i is row i % page_rows of page i / page_rows
+    int shift = 0;
+    while ((int64_t(1) << shift) < pool->shape[1]) ++shift;
+    p.pool_rs_bytes = pool->stride[1] * eb;
+    p.page_shift = shift;
+    p.page_mask = uint32_t(pool->shape[1] - 1);
+    p.page_bytes = pool->stride[0] * eb;
+  } else {
+    p.pool_rs_bytes = pool->stride[0] * eb;
+    p.page_shift = 31;
+    p.page_mask = 0x7fffffffu;
+    p.page_bytes = 0;
+  }
   p.pool_bytes = uint32_t(std::min<int64_t>(c.pb.pool_bytes, kMaxBufferBytes));
   p.kv_scale = c.fp8 ? scale : nullptr;
   p.idx = static_cast<const int32_t*>(idx->data);
@@ -340,6 +394,7 @@ FwdParams segment_params(const smla_tensor* q, const smla_tensor* pool, const fl
   p.remap = plan.remap;
   p.grid = plan.grid;
   p.sm_log2 = sm_scale * 1.4426950408889634f;
+  p.q_fp8 = c.q_fp8 ? 1 : 0;
   return p;
 }
 
@@ -376,6 +431,8 @@ int validate_extra(const smla_tensor* q, const smla_tensor* kv_pool, const smla_
     return fail(s, "extra segment: " + g_last_error);
   if (extra_pool->dtype != kv_pool->dtype)
     return fail(SMLA_ERR_UNSUPPORTED, "extra_pool: dtype must match kv_pool");
+  if (extra_pool->ndim != 2)
+    return fail(SMLA_ERR_UNSUPPORTED, "extra_pool: must be 2-D (only the main pool may be paged)");
   *scale2 = nullptr;
   if (c2->fp8) {
     if (extra_scale && extra_scale->data) {
@@ -438,6 +495,7 @@ int fwd_one(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
   Checked c;
   int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c, epi_out_dtype(epi));
   if (s) return s;
+  if ((s = check_q_scale(c, opt))) return s;
   EpiOut eo;
   const smla_tensor* ins[4] = {q, kv_pool, indices, c.fp8 ? kv_scale : nullptr};
   if ((s = validate_epilogue(epi, c.pb.rows, c.pb.heads, out, lse, ins, 4, &eo))) return s;
@@ -453,6 +511,7 @@ int fwd_one(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
   FwdParams p = segment_params(q, kv_pool, c.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
                                indices, c, plan, sm_scale, out, lse);
   p.epi = eo;
+  p.q_scale = opt ? static_cast<const float*>(opt->q_scale) : nullptr;
   if (plan.splits > 1) {
     void* ws = nullptr;
     int64_t lse_off = 0;
@@ -480,6 +539,7 @@ int fwd_two(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
   Checked c1, c2;
   int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c1, epi_out_dtype(epi));
   if (s) return s;
+  if ((s = check_q_scale(c1, opt))) return s;
   const float* scale2 = nullptr;
   if ((s = validate_extra(q, kv_pool, kv_scale, extra_pool, extra_kv_scale, extra_indices, out, lse,
                           &c2, &scale2)))
@@ -503,6 +563,7 @@ int fwd_two(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
                                  c1.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
                                  indices, c1, plan1, sm_scale, out, lse);
     p.epi = eo;
+    p.q_scale = opt ? static_cast<const float*>(opt->q_scale) : nullptr;
     p.pool2 = static_cast<const uint8_t*>(extra_pool->data);
     p.pool2_rs_bytes = extra_pool->stride[0] * elem_size(extra_pool->dtype);
     p.pool2_bytes = uint32_t(std::min<int64_t>(c2.pb.pool_bytes, kMaxBufferBytes));
@@ -541,6 +602,7 @@ int fwd_two(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
   p1.part_o = part_o;
   p1.part_lse = part_lse;
   FwdParams p2 = segment_params(q, extra_pool, scale2, extra_indices, c2, plan2, sm_scale, out, lse);
+  p1.q_scale = p2.q_scale = opt ? static_cast<const float*>(opt->q_scale) : nullptr;
   p2.part_o = part_o + int64_t(plan1.splits) * per_split * kDv;
   p2.part_lse = part_lse + int64_t(plan1.splits) * per_split;
   FwdParams pc = p1;
@@ -745,6 +807,8 @@ int sparse_mla_plan2(const smla_tensor* q, const smla_tensor* kv_pool, const sml
   if ((s = validate_inputs(q, extra_pool, extra_indices, &c2))) return s;
   if (extra_pool->dtype != kv_pool->dtype)
     return fail(SMLA_ERR_UNSUPPORTED, "extra_pool: dtype must match kv_pool");
+  if (extra_pool->ndim != 2)
+    return fail(SMLA_ERR_UNSUPPORTED, "extra_pool: must be 2-D (only the main pool may be paged)");
   return plan_two(c1, c2, opt, num_cus, plan_main, plan_extra, workspace_bytes);
 }
 

@@ -100,18 +100,18 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
   {
     const int h = h0 + l16;
     if (h < p.heads) {
-      const uint16_t* qp = p.q + r * p.q_rs + int64_t(h) * p.q_hs + 16 * g;
+      const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 16 * g;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        qf[s] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(qp + 64 * (s >> 1) + 8 * (s & 1)));
+        qf[s] = load_q8(p.q, p.q_fp8, qp + 64 * (s >> 1) + 8 * (s & 1));
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
   const float kv_scale = *p.kv_scale;
-  float c = p.sm_log2 * kv_scale;  // raw dot -> log2-domain score (per segment)
+  const float qs = q_scale_of(p.q_scale);
+  float c = p.sm_log2 * qs * kv_scale;  // raw dot -> log2-domain score (per segment)
   float vs = kv_scale;             // scale of the V codes O is accumulated in
 
   // This split's slots of the virtual list [main top-k | second segment],
@@ -126,8 +126,8 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
   // copied between iterations, make the compiler wait for all outstanding
   // loads. An invalid slot's row is read at an offset past the end of the
   // pool's buffer range, which returns zeros without touching memory.
-  auto gather = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t rs_bytes, u32x4 (&kr)[NI], int id) {
-    const uint32_t off = id >= 0 ? uint32_t(id) * rs_bytes + 16u * g : kOutOfRange;
+  auto gather = [&](const __amdgpu_buffer_rsrc_t& rsrc, const PoolMap& pm, u32x4 (&kr)[NI], int id) {
+    const uint32_t off = id >= 0 ? slot_offset(pm, id) + 16u * g : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 64u * i, 0, 0));
@@ -210,9 +210,9 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
   };
 
   // Slots [lo, hi) of the virtual list, all in the segment that starts at
-  // virtual slot sb, whose rows come from `rsrc` (row stride rs_bytes) and
+  // virtual slot sb, whose rows come from `rsrc` (slot offsets from pm) and
   // whose indices are idx_seg[0..).
-  auto walk_range = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t rs_bytes,
+  auto walk_range = [&](const __amdgpu_buffer_rsrc_t& rsrc, const PoolMap& pm,
                         const int32_t* idx_seg, int lo, int hi, int sb) {
     for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
       const int c1 = min(hi, c0 + kIdxChunk);
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
 #pragma unroll
         for (int u = 0; u < kDecBufs; ++u) {
           idb[u] = slot_idx(u);
-          gather(rsrc, rs_bytes, kr[u], idb[u]);
+          gather(rsrc, pm, kr[u], idb[u]);
         }
         const int nj_pad = (nj + kDecBufs - 1) / kDecBufs * kDecBufs;
         for (int j = 0; j < nj_pad; j += kDecBufs) {
@@ -244,7 +244,7 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
           for (int u = 0; u < kDecBufs; ++u) {
             step(kr[u], idb[u]);
             idb[u] = slot_idx(j + u + kDecBufs);
-            gather(rsrc, rs_bytes, kr[u], idb[u]);
+            gather(rsrc, pm, kr[u], idb[u]);
           }
         }
       }
@@ -265,16 +265,18 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
 #pragma unroll
       for (int nb = 0; nb < 32; ++nb) o[nb] *= rebase;
       vs = s2;
-      c = p.sm_log2 * s2;
+      c = p.sm_log2 * qs * s2;
     }
     const int sb = second ? p.topk : 0;
     const int lo = max(kbeg, sb), hi = min(kend, second ? ktot : p.topk);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(second ? p.pool2 : p.pool), 0, second ? p.pool2_bytes : p.pool_bytes,
         kBufferWord3);
-    const uint32_t rs_bytes = uint32_t(second ? p.pool2_rs_bytes : p.pool_rs_bytes);
+    const PoolMap pm = second ? PoolMap{uint32_t(p.pool2_rs_bytes), 0u, 31u, 0x7fffffffu}
+                              : PoolMap{uint32_t(p.pool_rs_bytes), uint32_t(p.page_bytes),
+                                        uint32_t(p.page_shift), p.page_mask};
     const int32_t* idx_seg = second ? p.idx2 + r * p.idx2_rs : p.idx + r * p.idx_rs;
-    walk_range(rsrc, rs_bytes, idx_seg, lo, hi, sb);
+    walk_range(rsrc, pm, idx_seg, lo, hi, sb);
   }
 
   // ---- merge the four waves: M = max_w m_w, L = sum_w 2^(m_w - M) l_w,

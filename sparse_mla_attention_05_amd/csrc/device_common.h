@@ -69,4 +69,31 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Eight query elements starting at element offset `off` as an MFMA bf16
+// operand: a bf16 q as it is (16 bytes), a float8_e4m3fn q (q8 != 0) widened
+// exactly from 8 codes; its per-tensor scale is applied to the scores.
+__device__ __forceinline__ bf16x8 load_q8(const uint16_t* q, int32_t q8, int64_t off) {
+  if (q8) {
+    const u32x2 c = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(q) + off);
+    return widen_fp8x8(c.x, c.y);
+  }
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + off));
+}
+
+// Byte offset of pool slot `id` in a paged pool: row id & mask of page
+// id >> shift, pages `page_bytes` apart. A 2-D pool has shift 31, mask
+// 0x7fffffff and page_bytes 0, which leaves id * rs.
+struct PoolMap {
+  uint32_t rs;          // row stride (bytes)
+  uint32_t page_bytes;  // page pitch (bytes)
+  uint32_t shift;
+  uint32_t mask;
+};
+__device__ __forceinline__ uint32_t slot_offset(const PoolMap& m, int id) {
+  return (uint32_t(id) >> m.shift) * m.page_bytes + (uint32_t(id) & m.mask) * m.rs;
+}
+
+// Per-tensor scale of the query (1 for a bf16 q or when none is given).
+__device__ __forceinline__ float q_scale_of(const float* qs) { return qs ? *qs : 1.0f; }
+
 }  // namespace smla

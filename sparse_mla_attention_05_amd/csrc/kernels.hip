@@ -121,17 +121,17 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   {
     const int h = h0 + hg * 16 + l16;
     if (h < p.heads) {
-      const uint16_t* qp = p.q + r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
+      const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
+        qf[s] = load_q8(p.q, p.q_fp8, qp + 32 * s);
     } else {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
 
-  float score_scale = p.sm_log2;
+  float score_scale = p.sm_log2 * q_scale_of(p.q_scale);
   float out_scale = 1.0f;
   if constexpr (FP8) {
     const float ks = *p.kv_scale;
@@ -149,7 +149,8 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
 
   auto gather = [&](u32x4 (&pre)[LPT], int id) {
     if (id >= 0) {
-      const uint8_t* rp = p.pool + int64_t(id) * p.pool_rs_bytes;
+      const uint8_t* rp = p.pool + int64_t(uint32_t(id) >> p.page_shift) * p.page_bytes +
+                          int64_t(uint32_t(id) & p.page_mask) * p.pool_rs_bytes;
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int c = gp + TPK * i;

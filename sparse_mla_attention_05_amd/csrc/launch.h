@@ -69,6 +69,16 @@ struct FwdParams {
   // Output epilogue of the final store (the attention kernel's without
   // splits, the combine kernel's with them); inactive: plain bf16 to out.
   EpiOut epi;
+  // q as float8_e4m3fn codes (q then points at bytes, strides in bytes) and
+  // its per-tensor scale (nullptr: 1).
+  int32_t q_fp8;
+  const float* q_scale;
+  // Paged main pool ([pages, page rows, W] with its own page pitch): slot i
+  // is row i & page_mask of page i >> page_shift. A 2-D pool: shift 31,
+  // mask 0x7fffffff, page_bytes 0. The second segment's pool is 2-D.
+  int32_t page_shift;
+  uint32_t page_mask;
+  int64_t page_bytes;
 };
 
 // The output epilogue as a pass of its own over bf16 rows [rows, heads, 512].

@@ -118,16 +118,16 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   {
     const int h = h0 + hg * 16 + l16;
     if (h < p.heads) {
-      const uint16_t* qp = p.q + r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
+      const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
+        qf[s] = load_q8(p.q, p.q_fp8, qp + 32 * s);
     } else {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
-  float score_scale = p.sm_log2;
+  float score_scale = p.sm_log2 * q_scale_of(p.q_scale);
   float out_scale = 1.0f;
   if constexpr (FP8) {
     const float ks = *p.kv_scale;
@@ -156,8 +156,10 @@ __global__ void __launch_bounds__(kPreWaves * 64, 1) prefill_kernel(const FwdPar
   auto gather = [&](u32x4 (&pre)[LPT], int id, int t) {
     const bool seg2 = two && t >= T1;
     const __amdgpu_buffer_rsrc_t rsrc = seg2 ? pool2_rsrc : pool_rsrc;
-    const uint32_t rs = uint32_t(seg2 ? p.pool2_rs_bytes : p.pool_rs_bytes);
-    const uint32_t off = id >= 0 ? uint32_t(id) * rs : kPreOutOfRange;
+    const PoolMap pm = seg2 ? PoolMap{uint32_t(p.pool2_rs_bytes), 0u, 31u, 0x7fffffffu}
+                            : PoolMap{uint32_t(p.pool_rs_bytes), uint32_t(p.page_bytes),
+                                      uint32_t(p.page_shift), p.page_mask};
+    const uint32_t off = id >= 0 ? slot_offset(pm, id) : kPreOutOfRange;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = min(gp + TPK * i, CH - 1);

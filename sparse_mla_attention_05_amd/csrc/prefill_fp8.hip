@@ -142,10 +142,10 @@ prefill_fp8_kernel(const FwdParams p) {
   for (int hb = 0; hb < 2; ++hb) {
     const int h = h0 + 16 * hb + l16;
     if (h < p.heads) {
-      const uint16_t* qp = p.q + r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
+      const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
-        qf[hb][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
+        qf[hb][s] = load_q8(p.q, p.q_fp8, qp + 32 * s);
     } else {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
@@ -158,7 +158,7 @@ prefill_fp8_kernel(const FwdParams p) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(qf[hb][s]));
   const float kv_scale = *p.kv_scale;
-  const float score_scale = p.sm_log2 * kv_scale;
+  const float score_scale = p.sm_log2 * q_scale_of(p.q_scale) * kv_scale;
 
   // ---- staging role: slot gk of a tile, fp8 chunks gq, gq + 4, ...
   const int gk = tid / C::TPR, gq = tid % C::TPR;
@@ -181,9 +181,9 @@ prefill_fp8_kernel(const FwdParams p) {
   const __amdgpu_buffer_rsrc_t pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.pool), 0, p.pool_bytes, kXBufferWord3);
   u32x4 pre[LPT];
-  auto row_off = [&](int id) -> uint32_t {
-    return id >= 0 ? uint32_t(id) * uint32_t(p.pool_rs_bytes) : kXOutOfRange;
-  };
+  const PoolMap pm{uint32_t(p.pool_rs_bytes), uint32_t(p.page_bytes), uint32_t(p.page_shift),
+                   p.page_mask};
+  auto row_off = [&](int id) -> uint32_t { return id >= 0 ? slot_offset(pm, id) : kXOutOfRange; };
   auto gather_one = [&](int i, uint32_t off) {
     pre[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            pool_rsrc, off + 16u * uint32_t(gq + 4 * i), 0, 0));

@@ -128,7 +128,7 @@ prefill_pp_kernel(const FwdParams p) {
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(ntiles, t_begin + p.tiles_per_split);
   const float kv_scale = *p.kv_scale;
-  const float score_scale = p.sm_log2 * kv_scale;
+  const float score_scale = p.sm_log2 * q_scale_of(p.q_scale) * kv_scale;
   const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
 
   // ---- staging (both roles, same mapping): slot gk of a tile, 8-byte chunks gq + 8i.
@@ -145,9 +145,9 @@ prefill_pp_kernel(const FwdParams p) {
   auto load_idx = [&](int t) -> int { return idx_raw(t) | idx_mask(t); };
   const __amdgpu_buffer_rsrc_t pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.pool), 0, p.pool_bytes, kPBufferWord3);
-  auto row_off = [&](int id) -> uint32_t {
-    return id >= 0 ? uint32_t(id) * uint32_t(p.pool_rs_bytes) : kPOutOfRange;
-  };
+  const PoolMap pm{uint32_t(p.pool_rs_bytes), uint32_t(p.page_bytes), uint32_t(p.page_shift),
+                   p.page_mask};
+  auto row_off = [&](int id) -> uint32_t { return id >= 0 ? slot_offset(pm, id) : kPOutOfRange; };
   const int gperm = pp_perm<DQK>(gk);
   auto chunk_addr = [&](int i) -> int {  // bf16 16-byte chunk gq + 8i of row gk
     const int c = gq + 8 * i;
@@ -180,10 +180,10 @@ prefill_pp_kernel(const FwdParams p) {
     for (int hb = 0; hb < 2; ++hb) {
       const int h = h0 + 16 * hb + l16;
       if (h < p.heads) {
-        const uint16_t* qp = p.q + r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
+        const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
-          qf[hb][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * s));
+          qf[hb][s] = load_q8(p.q, p.q_fp8, qp + 32 * s);
       } else {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});

@@ -4,6 +4,7 @@ before any HIP call, the planner's choices are legal, and the XCD-aware work
 order is a bijection that gives each XCD one contiguous run of work ids.
 No call here reaches a kernel."""
 
+import ctypes
 import os
 import re
 
@@ -371,3 +372,41 @@ def test_indexer_topk_validation(mutate, expected):
              ke=torch.zeros(8, dtype=torch.int32), k=16, indices=torch.zeros(8, 16, dtype=torch.int32))
     mutate(a)
     assert _lib.status_of_indexer_topk(**a) == expected, _lib.last_error()
+
+
+# ------------------------------------------------- fp8 q and paged pools
+
+def test_fp8_q_is_accepted_and_q_scale_needs_it(lib):
+    a = _args(R=0)
+    a["q"] = torch.zeros(0, 16, 576, dtype=torch.float8_e4m3fn)
+    assert _status(a) == _lib.SMLA_OK, _lib.last_error()
+    a = _args(R=0)
+    qs = torch.ones(1)
+    d = [_lib.describe(a[k]) for k in ("q", "kv_pool", "indices", "out", "lse")]
+    opt = _lib._options(q_scale=qs)
+    st = lib.sparse_mla_fwd_ex(_lib._ptr(d[0]), _lib._ptr(d[1]), None, _lib._ptr(d[2]), 0.1,
+                               _lib._ptr(d[3]), _lib._ptr(d[4]), None, ctypes.byref(opt))
+    assert st == INVALID and "q_scale" in _lib.last_error()
+
+
+@pytest.mark.parametrize("pool,expected", [
+    (lambda: torch.zeros(64, 4, 576, dtype=torch.bfloat16), _lib.SMLA_OK),
+    (lambda: torch.zeros(64, 3, 576, dtype=torch.bfloat16), UNSUP),          # 3 rows a page
+    (lambda: torch.zeros(64, 4 * 576 + 64, dtype=torch.bfloat16).as_strided(
+        (64, 4, 576), (4 * 576 + 64, 576, 1)), _lib.SMLA_OK),                 # padded pages
+    (lambda: torch.zeros(64 * 4 * 576, dtype=torch.bfloat16).as_strided(
+        (64, 4, 576), (2 * 576, 576, 1)), INVALID),                          # pages overlap
+    (lambda: torch.zeros(64, 4, 500, dtype=torch.bfloat16), INVALID),         # rows too narrow
+])
+def test_paged_pool_validation(pool, expected):
+    a = _args(R=0)
+    a["kv_pool"] = pool()
+    assert _status(a) == expected, _lib.last_error()
+
+
+def test_paged_extra_pool_is_rejected():
+    a = _args2(pool_dtype=torch.bfloat16)
+    a["extra_pool"] = torch.zeros(32, 4, 576, dtype=torch.bfloat16)
+    for k in ("q", "indices", "extra_indices", "out", "lse"):
+        a[k] = a[k][:0]
+    assert _status2(a) == UNSUP

@@ -1,0 +1,127 @@
+"""GPU parity of the forward's variants (the pages' small extensions):
+an fp8 q widened in the kernels, 8 heads as a masked 16-head program, and a
+paged pool whose page pitch is padded. Same bar as the plain forward
+(max |out - ref| <= 2e-2, relative Frobenius <= 5e-3, |lse - ref| <= 1e-3,
+exact 0 / -inf for rows without a valid slot); outputs start NaN-poisoned.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_05_amd import _lib
+from sparse_mla_attention_05_amd.inputs import custom_workload, make_fp8_q, make_inputs
+from test_gpu_parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, inp, q_scale=None, pool=None, **opts):
+    R, H = q.shape[0], q.shape[1]
+    out = torch.full((R, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((R, H), float("nan"), dtype=torch.float32, device="cuda")
+    s = inp.kv_scale.cuda() if inp.kv_scale is not None else None
+    _lib.sparse_mla_fwd_ex(q.cuda(), (pool if pool is not None else inp.pool.cuda()), s,
+                           inp.indices.cuda(), inp.sm_scale, out, lse,
+                           q_scale=q_scale.cuda() if q_scale is not None else None, **opts)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+FP8Q_CASES = [
+    # kv, d_qk, heads, top-k, overrides: each kernel's Q load
+    ("fp8", 576, 16, 512, {}),                          # decode kernel
+    ("fp8", 576, 16, 300, dict(head_block=16, splits=3)),
+    ("fp8", 576, 64, 512, {}),                          # 64-head fp8 kernel
+    ("fp8", 512, 64, 300, dict(variant=3)),             # role-split kernel
+    ("bf16", 576, 64, 512, {}),                         # 8-wave kernel
+    ("bf16", 576, 16, 200, {}),                         # staged-tile kernel
+    ("bf16", 512, 32, 200, {}),
+]
+
+
+@pytest.mark.parametrize("kv,d_qk,heads,topk,opts", FP8Q_CASES)
+def test_fp8_q(kv, d_qk, heads, topk, opts):
+    print(f"\n[fp8 q] kv={kv} d_qk={d_qk} H={heads} K={topk} {opts}", flush=True)
+    inp = make_inputs(custom_workload(rows=10, heads=heads, d_qk=d_qk, pool_rows=5000, topk=topk,
+                                      kv_dtype=kv, seed=heads + topk, index_mode="causal",
+                                      first_pos=4000, invalid_per_row=4))
+    inp.indices[2] = -1
+    q8, qs = make_fp8_q(inp)
+    out, lse = _run(q8, inp, q_scale=qs, **opts)
+    ref_out, ref_lse = oracle.sparse_mla_fwd_torch(q8, inp.pool, inp.kv_scale, inp.indices,
+                                                   inp.sm_scale, q_scale=qs)
+    print(f"[fp8 q] {assert_parity(out, lse, ref_out, ref_lse, inp.indices)}", flush=True)
+
+
+def test_fp8_q_without_scale_is_scale_one():
+    inp = make_inputs(custom_workload(rows=6, heads=16, d_qk=576, pool_rows=3000, topk=256,
+                                      kv_dtype="fp8", seed=5))
+    q8, _ = make_fp8_q(inp)
+    out, lse = _run(q8, inp)
+    ref_out, ref_lse = oracle.sparse_mla_fwd_torch(q8, inp.pool, inp.kv_scale, inp.indices,
+                                                   inp.sm_scale)
+    assert_parity(out, lse, ref_out, ref_lse, inp.indices)
+
+
+@pytest.mark.parametrize("kv,splits", [("fp8", 0), ("fp8", 3), ("bf16", 0)])
+def test_eight_heads(kv, splits):
+    """8 heads (one TP8 rank of a 64-head model) as a 16-head program with the
+    other 8 masked, with and without split-K, 37 rows."""
+    print(f"\n[8 heads] kv={kv} splits={splits}", flush=True)
+    inp = make_inputs(custom_workload(rows=37, heads=8, d_qk=576, pool_rows=8192, topk=512,
+                                      kv_dtype=kv, seed=37, invalid_per_row=7))
+    inp.indices[5] = -1
+    opts = dict(head_block=16, splits=splits) if splits else {}
+    out, lse = _run(inp.q, inp, **opts)
+    ref_out, ref_lse = oracle.sparse_mla_fwd_torch(inp.q, inp.pool, inp.kv_scale, inp.indices,
+                                                   inp.sm_scale)
+    print(f"[8 heads] {assert_parity(out, lse, ref_out, ref_lse, inp.indices)}", flush=True)
+
+
+def paged_pool(pool, page_rows, pad_bytes):
+    """The same rows in a paged [P, page_rows, W] pool whose page pitch is
+    padded by pad_bytes: (flat buffer kept alive, the strided view)."""
+    N, W = pool.shape
+    raw = pool.view(torch.uint8) if pool.dtype == torch.float8_e4m3fn else pool.view(torch.int16)
+    eb = raw.element_size()
+    P = -(-N // page_rows)
+    pitch = page_rows * W + pad_bytes // eb
+    flat = torch.full((P * pitch,), 0x55, dtype=raw.dtype, device="cuda")
+    view = flat.as_strided((P, page_rows, W), (pitch, W, 1))
+    rows = raw.cuda()
+    for b in range(P):
+        n = min(page_rows, N - b * page_rows)
+        view[b, :n] = rows[b * page_rows:b * page_rows + n]
+    return flat, view.view(pool.dtype)
+
+
+PAGED_CASES = [
+    # kv, d_qk, heads, top-k, rows per page, page padding (bytes), overrides
+    ("fp8", 576, 16, 512, 64, 256, {}),                        # decode kernel
+    ("fp8", 576, 16, 300, 16, 4096, dict(head_block=16, splits=3)),
+    ("fp8", 576, 64, 512, 64, 1024, {}),                       # 64-head fp8 kernel
+    ("fp8", 512, 64, 300, 32, 512, dict(variant=3)),           # role-split kernel
+    ("bf16", 576, 64, 512, 1, 128, {}),                        # one row per page
+    ("bf16", 512, 16, 200, 128, 2048, {}),                     # staged-tile kernel
+]
+
+
+@pytest.mark.parametrize("kv,d_qk,heads,topk,page_rows,pad,opts", PAGED_CASES)
+def test_paged_pool_equals_flat_pool(kv, d_qk, heads, topk, page_rows, pad, opts):
+    """A paged pool with padded pages gives the flat pool's result bit for
+    bit (same plan, same rows), and so the oracle's."""
+    print(f"\n[paged] kv={kv} d_qk={d_qk} H={heads} K={topk} B={page_rows} pad={pad} {opts}",
+          flush=True)
+    inp = make_inputs(custom_workload(rows=10, heads=heads, d_qk=d_qk, pool_rows=5000, topk=topk,
+                                      kv_dtype=kv, seed=3 * heads + topk, index_mode="causal",
+                                      first_pos=4000, invalid_per_row=4))
+    inp.indices[1] = -1
+    flat_out, flat_lse = _run(inp.q, inp, **opts)
+    _keep, paged = paged_pool(inp.pool, page_rows, pad)
+    out, lse = _run(inp.q, inp, pool=paged, **opts)
+    assert torch.equal(out, flat_out) and torch.equal(lse, flat_lse)
+    ref_out, ref_lse = oracle.sparse_mla_fwd_torch(inp.q, inp.pool, inp.kv_scale, inp.indices,
+                                                   inp.sm_scale)
+    print(f"[paged] {assert_parity(out, lse, ref_out, ref_lse, inp.indices)}", flush=True)
