@@ -45,14 +45,17 @@ CSRC = os.path.join(ROOT, "sparse_mla_attention_05_amd", "csrc")
 
 def attention_kernel(plan, d_qk, fp8):
     """(kernel name as rocprofv3 shows it, source file) of the attention
-    kernel a plan launches; mirrors the dispatch in csrc/kernels.hip."""
+    kernel a plan launches without an output epilogue (the instance with
+    `false` last); mirrors the dispatch in csrc/kernels.hip."""
     hb, v = plan["head_block"], plan["variant"]
     if hb == 16 and fp8 and v == 0:
-        return f"smla::decode_kernel<{d_qk}>", "decode.hip"
+        return f"smla::decode_kernel<{d_qk}, false>", "decode.hip"
     if hb == 64 and v != 1:
         if fp8 and v == 0:
-            return f"smla::prefill_fp8_kernel<{d_qk}>", "prefill_fp8.hip"
-        return f"smla::prefill_kernel<{d_qk}, {str(fp8).lower()}>", "prefill.hip"
+            return f"smla::prefill_fp8_kernel<{d_qk}, false>", "prefill_fp8.hip"
+        if fp8 and v == 3:
+            return f"smla::prefill_pp_kernel<{d_qk}, false>", "prefill_pp.hip"
+        return f"smla::prefill_kernel<{d_qk}, {str(fp8).lower()}, false>", "prefill.hip"
     return "smla::fwd_kernel (staged tile)", "kernels.hip"
 
 
