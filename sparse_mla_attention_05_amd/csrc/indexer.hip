@@ -9,8 +9,8 @@
 // 4096-key column of the output; Q (4 rows x 32 heads x 128 fp8 = 64 VGPRs)
 // and w stay in registers, and all waves walk the same K sequence through
 // LDS (64-key stages, double-buffered, chunk-XOR swizzled rows), so K is read
-// once per 16 rows; two workgroups share a CU, so one wave's relu and head
-// sums run under the other's MFMAs. One v_mfma_f32_16x16x128_f8f6f4 computes
+// once per 16 rows; three workgroups share a CU (168 VGPRs, no spills), so
+// one wave's relu and head sums run under the others' MFMAs. One v_mfma_f32_16x16x128_f8f6f4 computes
 // 16 heads x 16 keys over all 128 dims (A = Q rows, B = K rows, the same
 // lane->k mapping on both sides). A lane's accumulator holds heads 4g..4g+3 of one key; relu
 // and the head weight are applied there, the four lanes g of a key are summed
@@ -53,7 +53,7 @@ __device__ __forceinline__ v8i cat(u32x4 a, u32x4 b) {
   return v8i{int(a.x), int(a.y), int(a.z), int(a.w), int(b.x), int(b.y), int(b.z), int(b.w)};
 }
 
-__global__ void __launch_bounds__(kIxWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kIxWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 ix_logits_kernel(const IxParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][kIxTileBytes];
   __shared__ float ksc[2][kIxTile];
