@@ -9,11 +9,16 @@
 // split-K reduce. With 16 heads the work per gathered byte is small, so the
 // kernel is built to keep gathers in flight and spend few cycles per slot:
 //
-//  * One workgroup = (row, 16-head block, split), 4 wavefronts, one per SIMD.
-//    Each wave walks its own quarter of the split's slots in 16-slot steps
-//    (steps w, w+4, ...) with its own running max, row sum and O, like an
-//    independent split; the four are merged once at the end. No barrier
-//    inside the walk.
+//  * One workgroup = (row, 16-head block, split), 4 wavefronts; two
+//    workgroups per CU (256 VGPRs and 61 KB of LDS each), so one
+//    workgroup's start (index staging, first gathers) and end (merge, store)
+//    overlap the other's walk. Each wave walks its own quarter of the split's
+//    slots in 16-slot steps (steps w, w+4, ...) with its own running max, row
+//    sum and O, like an independent split; the four are merged once at the
+//    end, through LDS, a quarter of the columns at a time. No barrier inside
+//    the walk.
+//  * Q^T is kept in LDS and each k-step's fragment is read one k-step ahead
+//    of its dot, which is what leaves the registers to two workgroups.
 //  * Gathers go straight into VGPRs, two steps in flight per wave. Lane
 //    (l16, g) loads 16-byte chunks 4i+g (i = 0..8) of the step's slot l16, so
 //    every load instruction reads 64 contiguous bytes of 16 rows. Those
@@ -50,20 +55,24 @@ constexpr int kDecStep = 16;        // slots per wave step
 constexpr int kDecBufs = 2;         // steps of gathers in flight per wave
 constexpr int kVPitch = 544;        // V staging row pitch (bytes): 512 + 32
 constexpr int kVWave = 16 * kVPitch;  // V staging bytes per wave
-constexpr int kIdxChunk = 4096;     // slot indices staged in LDS at a time
+constexpr int kIdxChunk = 2048;     // slot indices staged in LDS at a time
 constexpr int kIdxOffset = kDecWaves * kVWave;  // their LDS offset (bytes)
-constexpr int kOPitch = 528;        // partial-O row pitch (floats): 2112 B = 64 mod 256
-constexpr int kOWave = 16 * kOPitch * 4;        // partial-O bytes per wave
-constexpr int kDecSmem = (kDecWaves * kOWave > kIdxOffset + 4 * kIdxChunk)
-                             ? kDecWaves * kOWave
-                             : kIdxOffset + 4 * kIdxChunk;
+constexpr int kQOffset = kIdxOffset + 4 * kIdxChunk;  // Q^T fragments (bytes)
+constexpr int kDecSmem = kQOffset + (576 / 32) * 64 * 16;
+// The four waves' O are merged through LDS a quarter of the columns at a
+// time, in the V staging area: [wave][head][128 columns], row pitch 132
+// floats (4 * 132 = 16 mod 64 banks, so a wave's 64 lanes hit 64 banks).
+constexpr int kMCols = kDv / 4;
+constexpr int kMPitch = kMCols + 4;
+constexpr int kMWave = 16 * kMPitch * 4;
+static_assert(kDecWaves * kMWave <= kIdxOffset, "merge area");
 constexpr float kLazyMax = 8.0f;    // log2-domain slack before the reference max moves
 constexpr uint32_t kOutOfRange = 0xFFFFF000u;  // buffer offset of an invalid slot's row
 constexpr int kBufferWord3 = 0x00020000;       // raw buffer descriptor word 3 (gfx9 family)
 
 // EPI: the final store goes through the output epilogue (epilogue.h).
 template <int DQK, bool EPI>
-__global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdParams p) {
+__global__ void __launch_bounds__(kDecWaves * 64, 2) decode_kernel(const FwdParams p) {
   constexpr int NCH = DQK / 16;  // 16-byte fp8 chunks per row
   constexpr int NI = NCH / 4;    // chunks per lane per step
   constexpr int KS = DQK / 32;   // k-steps of the QK dot
@@ -95,9 +104,11 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
 
   const int h0 = hb * 16;
 
-  // Q^T fragments in the gather's column order.
+  // Q^T fragments in the gather's column order, kept in LDS (fragment s of
+  // lane l at kQOffset + (64 s + l) 16 bytes) and read back a k-step ahead of
+  // their dots, which leaves the registers to two workgroups per CU.
   bf16x8 qf[KS];
-  {
+  if (wave == 0) {
     const int h = h0 + l16;
     if (h < p.heads) {
       const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 16 * g;
@@ -108,7 +119,11 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      reinterpret_cast<u32x4*>(smem + kQOffset)[64 * s + lane] = __builtin_bit_cast(u32x4, qf[s]);
   }
+  const u32x4* q_lds = reinterpret_cast<const u32x4*>(smem + kQOffset) + lane;
   const float kv_scale = *p.kv_scale;
   const float qs = q_scale_of(p.q_scale);
   float c = p.sm_log2 * qs * kv_scale;  // raw dot -> log2-domain score (per segment)
@@ -153,12 +168,18 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
 
     // S^T = K Q^T, two accumulators.
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 qa = __builtin_bit_cast(bf16x8, q_lds[0]), qb = __builtin_bit_cast(bf16x8, q_lds[64]);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_fp8x8(kr[i].x, kr[i].y), qf[2 * i], s0,
-                                                    0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_fp8x8(kr[i].z, kr[i].w), qf[2 * i + 1],
-                                                    s1, 0, 0, 0);
+      bf16x8 na = qa, nb = qb;
+      if (i + 1 < NI) {
+        na = __builtin_bit_cast(bf16x8, q_lds[64 * (2 * i + 2)]);
+        nb = __builtin_bit_cast(bf16x8, q_lds[64 * (2 * i + 3)]);
+      }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_fp8x8(kr[i].x, kr[i].y), qa, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen_fp8x8(kr[i].z, kr[i].w), qb, s1, 0, 0, 0);
+      qa = na;
+      qb = nb;
       // Keep each k-step's widening next to its MFMAs: hoisting all of them
       // would hold 18 widened operands (72 VGPRs) at once.
       __builtin_amdgcn_sched_barrier(0);
@@ -217,7 +238,22 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
     for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
       const int c1 = min(hi, c0 + kIdxChunk);
       __syncthreads();  // every wave is done with the previous chunk's indices
-      for (int t = tid; t < c1 - c0; t += kDecWaves * 64) idx_s[t] = idx_seg[c0 - sb + t];
+      {
+        // All of a thread's index loads are issued before the first is
+        // waited on (a plain strided copy loop waits on each load in turn:
+        // that many memory round trips before the walk's first gather).
+        // Loads past the chunk's end read 0 through the buffer range.
+        constexpr int PER = kIdxChunk / (kDecWaves * 64);
+        const __amdgpu_buffer_rsrc_t ir = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t*>(idx_seg + (c0 - sb)), 0, 4 * (c1 - c0), kBufferWord3);
+        int v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          v[k] = __builtin_amdgcn_raw_buffer_load_b32(
+              ir, 4u * uint32_t(tid + kDecWaves * 64 * k), 0, 0);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) idx_s[tid + kDecWaves * 64 * k] = v[k];
+      }
       __syncthreads();
       const int nst = (c1 - c0 + kDecStep - 1) / kDecStep;
       const int nj = nst > wave ? (nst - wave + kDecWaves - 1) / kDecWaves : 0;
@@ -293,7 +329,8 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
   }
   __syncthreads();  // also: every wave is done with its V staging area
 
-  float* part = reinterpret_cast<float*>(smem) + wave * (kOWave / 4);
+  // Per-head weight of this wave's O: 2^(m_w - M) * vs / L.
+  float fw[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int head = 4 * g + i;
@@ -307,30 +344,37 @@ __global__ void __launch_bounds__(kDecWaves * 64, 1) decode_kernel(const FwdPara
       L += mw == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mw - M) * red_l[w * 16 + head];
     }
     const float mine = red_m[wave * 16 + head];
-    const float f = (L > 0.f && mine != kNegInf) ? __builtin_amdgcn_exp2f(mine - M) * vs / L : 0.f;
-    float* prow = part + head * kOPitch + l16;
-#pragma unroll
-    for (int nb = 0; nb < 32; ++nb) prow[16 * nb] = o[nb][i] * f;
+    fw[i] = (L > 0.f && mine != kNegInf) ? __builtin_amdgcn_exp2f(mine - M) * vs / L : 0.f;
   }
-  __syncthreads();
 
-  // 16 heads x 64 chunks of 8 columns; thread t takes chunk t % 64 of heads
-  // t / 64 + 4k, so consecutive threads store consecutive 16-byte pieces.
+  // Four passes of 128 columns: each wave writes its weighted O, then thread
+  // t sums the waves for head t / 16, columns 8 (t % 16) .. +7 of the pass,
+  // so consecutive threads store consecutive 16-byte pieces of one head.
   const bool split_mode = p.part_o != nullptr;  // partials for the combine kernel
+  float* part = reinterpret_cast<float*>(smem) + wave * (kMWave / 4);
   const float* parts = reinterpret_cast<const float*>(smem);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int head = (tid >> 6) + 4 * k;
-    const int col = 8 * (tid & 63);
+  for (int pass = 0; pass < kDv / kMCols; ++pass) {
+    if (pass > 0) __syncthreads();  // the previous pass's sums are read
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* prow = part + (4 * g + i) * kMPitch + l16;
+#pragma unroll
+      for (int nb = 0; nb < kMCols / 16; ++nb) prow[16 * nb] = o[pass * (kMCols / 16) + nb][i] * fw[i];
+    }
+    __syncthreads();
+    const int head = tid >> 4;
+    const int cl = 8 * (tid & 15);
+    const int col = pass * kMCols + cl;
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      const float* src = parts + w * (kOWave / 4) + head * kOPitch + col;
+      const float* src = parts + w * (kMWave / 4) + head * kMPitch + cl;
       s0 += *reinterpret_cast<const floatx4*>(src);
       s1 += *reinterpret_cast<const floatx4*>(src + 4);
     }
     const int h = h0 + head;
-    if (h < p.heads) {  // uniform over the wave: one head per wave
+    if (h < p.heads) {  // uniform over each group of 16 lanes
       if (EPI && !split_mode) {
         float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         epi_store<8>(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, r, h, col, v);
