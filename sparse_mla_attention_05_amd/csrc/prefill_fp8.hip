@@ -34,9 +34,9 @@
 //    0's softmax weights are computed between block 1's dots. Two barriers
 //    per tile: P swap, buffer reuse.
 //  * Fixed reference: a head's reference max is the max over the first tile
-//    that has a valid slot, from a scoring pre-pass over that tile (the pair
-//    agrees on it through LDS), so O is never rescaled and stays in the MFMA
-//    accumulators. P = exp2(s - ref) is exact in real arithmetic whatever the
+//    that has a valid slot, taken by the walk's first step from that tile's
+//    scores before any weight (the pair agrees on it through LDS), so O is
+//    never rescaled and stays in the MFMA accumulators. P = exp2(s - ref) is exact in real arithmetic whatever the
 //    reference; the bf16 P and fp32 sums stay in range while every weight is
 //    at most 2^64. Every weight a lane adds is at most the lane's partial
 //    row sum, so if no partial sum passes 2^64 none did; otherwise the
@@ -44,6 +44,8 @@
 //    slots a second time with that as the reference.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "epilogue.h"
@@ -75,7 +77,8 @@ struct XCfg {
   static constexpr int NQB = SWB / 4;              // K-operand address bases
   static constexpr int NVB = SWB / 2;              // V-operand address bases
   static constexpr int NSB = SWB / 8;              // staging address bases per half
-  static constexpr int LDS_BYTES = 2 * TILE + 2 * TK * 4 + kXWaves * 2 * 64 * 16 + 64;
+  static constexpr int LDS_BYTES = 2 * TILE + 2 * TK * 4 + kXWaves * 2 * 64 * 16 + 64 +
+                                    kXWaves * 2 * 64 * 4;
   static_assert(SRC_CH % TPR == 0, "staging split");
   static_assert(LPT % NSB == 0, "staging bases");
   static_assert(4 * LPT <= 2 * KSTEPS, "staging spread over the k-steps");
@@ -109,6 +112,9 @@ prefill_fp8_kernel(const FwdParams p) {
   // [wave][head block][lane] 16 bytes.
   __shared__ __attribute__((aligned(16))) u32x4 xch[kXWaves * 2 * 64];
   __shared__ uint32_t redo[1];
+  // The pair's head maxima of the first tile, when the walk fixes the
+  // reference itself: [wave][head block][lane].
+  __shared__ float mxch[kXWaves * 2 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -136,27 +142,31 @@ prefill_fp8_kernel(const FwdParams p) {
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(ntiles, t_begin + p.tiles_per_split);
 
-  // Q^T operands: head h0 + 16hb + l16, columns 8g + 32s .. +7.
+  // Q^T operands: head h0 + 16hb + l16, columns 8g + 32s .. +7. Loaded by
+  // the walk right after the gathers of its first tile, so the two loads'
+  // latencies overlap.
   bf16x8 qf[2][KSTEPS];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int h = h0 + 16 * hb + l16;
-    if (h < p.heads) {
-      const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        qf[hb][s] = load_q8(p.q, p.q_fp8, qp + 32 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
-  }
-  // Keep Q^T in VGPRs: left to itself the allocator parks it in AGPRs (the
-  // dots can read it there) and then has no AGPRs left for O^T and S^T.
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(qf[hb][s]));
+    for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  auto load_q = [&]() {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = h0 + 16 * hb + l16;
+      if (h < p.heads) {
+        const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = load_q8(p.q, p.q_fp8, qp + 32 * s);
+      }
+    }
+    // Keep Q^T in VGPRs: left to itself the allocator parks it in AGPRs (the
+    // dots can read it there) and then has no AGPRs left for O^T and S^T.
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(qf[hb][s]));
+  };
   const float kv_scale = *p.kv_scale;
   const float score_scale = p.sm_log2 * q_scale_of(p.q_scale) * kv_scale;
 
@@ -226,7 +236,7 @@ prefill_fp8_kernel(const FwdParams p) {
     vbase[b] = vrow * ROW + 16 * 32 * kh + 16 * ((2 * b + ((l16 >> 1) & 1)) ^ vperm) + 8 * (l16 & 1);
 
   floatx4 o[NDW][2];
-  float m_ref[2];    // reference max (log2 domain) of head 16hb + l16, shared by the pair
+  float m_ref[2] = {kNegInf, kNegInf};  // reference max (log2) of head 16hb + l16, shared by the pair
   float nmu[2];      // -m_ref, or 0 when the split has no valid slot
   float l_part[2];   // this lane's share of the head's row sum over the wave's slots
 
@@ -387,8 +397,9 @@ prefill_fp8_kernel(const FwdParams p) {
     __syncthreads();  // the exchange area is free again
   };
 
-  // One walk over tiles [t0, t_end) with the references in m_ref.
-  auto walk = [&](int t0) {
+  // One walk over tiles [t0, t_end) with the references in m_ref, or, with
+  // fix_ref, with the references fixed by the walk's first tile.
+  auto walk = [&](int t0, bool fix_ref) {
 #pragma unroll
     for (int d = 0; d < NDW; ++d) o[d][0] = o[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -397,6 +408,7 @@ prefill_fp8_kernel(const FwdParams p) {
     if (t0 >= t_end) return;
     int id_a = load_idx(t0);
     gather(id_a);
+    if (fix_ref) load_q();  // the first walk; a second one reuses Q
 #pragma unroll
     for (int i = 0; i < LPT; ++i) stage_chunk(i, tile0);
     if (gq == 0) kbias[gk] = id_a >= 0 ? 0.f : kNegInf;
@@ -409,13 +421,39 @@ prefill_fp8_kernel(const FwdParams p) {
     // which every wave finished before the last barrier; softmax; P swap;
     // PV. The index of tile t+3 is loaded before the gathers of tile t+2, so
     // waiting for it never waits for them.
-    auto step = [&](int t, const uint8_t* cur, uint8_t* nxt, int buf) {
+    auto step = [&](auto first, int t, const uint8_t* cur, uint8_t* nxt, int buf) {
+      constexpr bool FIRST = decltype(first)::value;
       const int raw_f = idx_raw(t + 3);
       __builtin_amdgcn_sched_barrier(0);
       const int id_n = raw_n | idx_mask(t + 2);
       float bias[8];
       load_bias(buf * TK, bias);
-      qk(cur, nxt, row_off(id_n), true, true, bias);
+      qk(cur, nxt, row_off(id_n), true, !FIRST, bias);
+      if constexpr (FIRST) {
+        // The walk's first tile fixes the reference: each head's max score
+        // over the tile (valid slots), agreed by the pair; then block 0's
+        // weights, which the other steps compute between the QK dots.
+        float mx[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          mx[hb] = kNegInf;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            mx[hb] = fmaxf(mx[hb], __builtin_fmaf(sacc[i / 4][hb][i % 4], score_scale, bias[i]));
+          mx[hb] = fmaxf(mx[hb], __shfl_xor(mx[hb], 16));
+          mx[hb] = fmaxf(mx[hb], __shfl_xor(mx[hb], 32));
+          mxch[(wave * 2 + hb) * 64 + lane] = mx[hb];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          m_ref[hb] = fmaxf(mx[hb], mxch[(partner * 2 + hb) * 64 + lane]);
+          nmu[hb] = m_ref[hb] == kNegInf ? 0.f : -m_ref[hb];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) weight(k / 4, k % 4, bias);
+        pack_block0();
+      }
       if (gq == 0) kbias[(buf ^ 1) * TK + gk] = id_b >= 0 ? 0.f : kNegInf;
       id_b = id_n;
       raw_n = raw_f;
@@ -444,9 +482,17 @@ prefill_fp8_kernel(const FwdParams p) {
     };
     // Tiles go in pairs (static buffer roles); an odd count ends with one
     // tile past the end, all slots invalid, which adds exactly nothing.
-    for (int t = t0; t < t_end; t += 2) {
-      step(t, tile0, tile1, 0);
-      step(t + 1, tile1, tile0, 1);
+    const std::integral_constant<bool, true> first_tile{};
+    const std::integral_constant<bool, false> later_tile{};
+    int t = t0;
+    if (fix_ref) {
+      step(first_tile, t, tile0, tile1, 0);
+      step(later_tile, t + 1, tile1, tile0, 1);
+      t += 2;
+    }
+    for (; t < t_end; t += 2) {
+      step(later_tile, t, tile0, tile1, 0);
+      step(later_tile, t + 1, tile1, tile0, 1);
     }
   };
 
@@ -461,8 +507,8 @@ prefill_fp8_kernel(const FwdParams p) {
   // (the loop body is emitted once).
 #pragma clang loop unroll(disable)
   for (int pass = 0; pass < 2; ++pass) {
-    max_pass(t0, pass == 0 ? min(t0 + 1, t_end) : t_end);
-    walk(t0);
+    if (pass == 1) max_pass(t0, t_end);
+    walk(t0, pass == 0);
     if (pass == 1) break;
     if (tid == 0) redo[0] = 0u;
     __syncthreads();
