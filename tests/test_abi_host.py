@@ -154,6 +154,18 @@ def test_plan_head_block_choice_and_overrides():
         _plan(4, 16, splits=65)
 
 
+def test_plan_counts_workgroups_per_cu():
+    # The fp8 decode kernel fits two workgroups per CU. They share the CU's
+    # memory traffic, so a launch that already gives every CU work stays
+    # unsplit (768 rows on 256 CUs measured 176 us unsplit, 193 us with two
+    # splits), while a launch that leaves CUs idle is still split.
+    p = _plan(768, 16, num_cus=256)
+    assert (p["head_block"], p["waves"], p["splits"]) == (16, 4, 1)
+    assert 2 * p["lds_bytes"] <= 160 * 1024
+    assert _plan(256, 16, num_cus=256)["splits"] == 1
+    assert _plan(32, 16, num_cus=256)["splits"] > 1
+
+
 @pytest.mark.parametrize("grid", [1, 7, 8, 9, 63, 64, 100, 513, 768, 1536])
 def test_xcd_work_order_is_contiguous_bijection(grid):
     works = [_lib.sparse_mla_work_of(pid, grid, 1) for pid in range(grid)]
