@@ -282,6 +282,22 @@ def test_decode_fp8_variants(variant, topk, splits):
     _check(inp, variant=variant, splits=splits)
 
 
+@pytest.mark.parametrize("topk,splits,heads,d_qk", [
+    (5000, 1, 16, 576), (5000, 2, 12, 576), (4097, 1, 16, 512), (2049, 3, 5, 576), (6144, 4, 16, 512)])
+def test_decode_index_chunks(topk, splits, heads, d_qk):
+    """The fp8 decode kernel stages a row's indices 2048 at a time and merges
+    its four waves a quarter of the columns at a time: top-k past one and two
+    chunks, splits that straddle chunk boundaries, partial head blocks."""
+    print(f"\n[parity] decode chunks topk={topk} splits={splits} heads={heads} d_qk={d_qk}", flush=True)
+    inp = _case(rows=6, heads=heads, d_qk=d_qk, topk=topk, pool_rows=16384, kv_dtype="fp8",
+                invalid_per_row=50, seed=topk + heads)
+    idx = inp.indices.clone()
+    idx[1, 2040:2060] = -1          # invalid slots across the first chunk boundary
+    idx[4, :] = -1                  # a row with no valid slot
+    inp.indices = idx
+    _check(inp, variant=0, splits=splits)
+
+
 @pytest.mark.parametrize("variant", [0, 1, 2, 3])
 @pytest.mark.parametrize("d_qk,kv,heads", [(576, "fp8", 64), (512, "fp8", 80), (576, "bf16", 64)])
 @pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (17, 1), (1000, 3)])
