@@ -112,9 +112,15 @@ __global__ void __launch_bounds__(kDecWaves * 64, 2) decode_kernel(const FwdPara
     const int h = h0 + l16;
     if (h < p.heads) {
       const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 16 * g;
+      // Fragment s holds columns 64 (s / 2) + 8 (s % 2) + 16g .. +8.
+      bf16x8 qe[KS / 2], qo[KS / 2];
+      load_q_frags(p.q, p.q_fp8, qp, 64, qe);
+      load_q_frags(p.q, p.q_fp8, qp + 8, 64, qo);
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qf[s] = load_q8(p.q, p.q_fp8, qp + 64 * (s >> 1) + 8 * (s & 1));
+      for (int s = 0; s < KS / 2; ++s) {
+        qf[2 * s] = qe[s];
+        qf[2 * s + 1] = qo[s];
+      }
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});

@@ -69,15 +69,27 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Eight query elements starting at element offset `off` as an MFMA bf16
-// operand: a bf16 q as it is (16 bytes), a float8_e4m3fn q (q8 != 0) widened
-// exactly from 8 codes; its per-tensor scale is applied to the scores.
-__device__ __forceinline__ bf16x8 load_q8(const uint16_t* q, int32_t q8, int64_t off) {
+// N MFMA bf16 operands of eight query elements each, starting at element
+// offsets base + stride * s: a bf16 q as it is (16 bytes), a float8_e4m3fn
+// q (q8 != 0) widened exactly from 8 codes (its per-tensor scale is applied
+// to the scores). The dtype branch is taken once, outside the loads, and the
+// codes are widened only after all of them are issued: a branch per load
+// makes the compiler wait for each load in turn.
+template <int N>
+__device__ __forceinline__ void load_q_frags(const uint16_t* q, int32_t q8, int64_t base,
+                                             int64_t stride, bf16x8 (&dst)[N]) {
   if (q8) {
-    const u32x2 c = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(q) + off);
-    return widen_fp8x8(c.x, c.y);
+    u32x2 c[N];
+#pragma unroll
+    for (int s = 0; s < N; ++s)
+      c[s] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(q) + base + stride * s);
+#pragma unroll
+    for (int s = 0; s < N; ++s) dst[s] = widen_fp8x8(c[s].x, c[s].y);
+  } else {
+#pragma unroll
+    for (int s = 0; s < N; ++s)
+      dst[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + base + stride * s));
   }
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + off));
 }
 
 // Byte offset of pool slot `id` in a paged pool: row id & mask of page

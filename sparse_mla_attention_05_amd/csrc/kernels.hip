@@ -122,9 +122,7 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
     const int h = h0 + hg * 16 + l16;
     if (h < p.heads) {
       const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        qf[s] = load_q8(p.q, p.q_fp8, qp + 32 * s);
+      load_q_frags(p.q, p.q_fp8, qp, 32, qf);
     } else {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});

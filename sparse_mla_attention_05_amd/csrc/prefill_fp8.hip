@@ -156,8 +156,7 @@ prefill_fp8_kernel(const FwdParams p) {
       const int h = h0 + 16 * hb + l16;
       if (h < p.heads) {
         const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = load_q8(p.q, p.q_fp8, qp + 32 * s);
+        load_q_frags(p.q, p.q_fp8, qp, 32, qf[hb]);
       }
     }
     // Keep Q^T in VGPRs: left to itself the allocator parks it in AGPRs (the
