@@ -241,6 +241,7 @@ ix_logits_kernel(const IxParams p) {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkUnroll = 8;  // keys per thread in flight in a histogram pass
 
 // Order-preserving integer image of an fp32 value (-0 taken as +0, so the two
 // zeros tie as they do as numbers).
@@ -299,9 +300,20 @@ __global__ void __launch_bounds__(kTkThreads) topk_kernel(const TopkParams p) {
     for (int i = tid; i < 2048; i += kTkThreads) hist[i] = 0u;
     __syncthreads();
     const int hs = lv == 0 ? 32 : kShift[lv - 1];  // candidates match `prefix` above bit hs
-    for (int n = lo + tid; n < hi; n += kTkThreads) {
-      const uint32_t u = order_key(row[n]);
-      if (lv == 0 || (u >> hs) == prefix) atomicAdd(&hist[(u >> sh) & uint32_t(bins - 1)], 1u);
+    // kTkUnroll keys per thread in flight: the loads are unconditional (the
+    // key index is clamped into the window) and masked where they are used;
+    // one key per iteration would wait on each load in turn.
+    for (int64_t n0 = lo + tid; n0 < hi; n0 += kTkUnroll * kTkThreads) {
+      uint32_t u[kTkUnroll];
+#pragma unroll
+      for (int j = 0; j < kTkUnroll; ++j)
+        u[j] = order_key(row[min(n0 + int64_t(j) * kTkThreads, int64_t(hi) - 1)]);
+#pragma unroll
+      for (int j = 0; j < kTkUnroll; ++j) {
+        const bool in = n0 + int64_t(j) * kTkThreads < hi;
+        if (in && (lv == 0 || (u[j] >> hs) == prefix))
+          atomicAdd(&hist[(u[j] >> sh) & uint32_t(bins - 1)], 1u);
+      }
     }
     __syncthreads();
     // thread t owns bins 2t (lower) and 2t + 1
@@ -324,9 +336,13 @@ __global__ void __launch_bounds__(kTkThreads) topk_kernel(const TopkParams p) {
 
   // ---- output in ascending index order: 1024 keys per round.
   uint32_t eq_base = 0, sel_base = 0;
+  // Each round's keys are loaded one round ahead (clamped into the window).
+  float cur = row[min(lo + tid, hi - 1)];
   for (int base = lo, round = 0; base < hi; base += kTkThreads, ++round) {
     const int n = base + tid;
-    const uint32_t u = n < hi ? order_key(row[n]) : 0u;
+    const float nxt = row[min(int64_t(n) + kTkThreads, int64_t(hi) - 1)];
+    const uint32_t u = n < hi ? order_key(cur) : 0u;
+    cur = nxt;
     const bool eq = n < hi && u == T;
     const uint64_t eqm = __ballot(eq);
     const uint32_t eq_in_wave = __popcll(eqm & ((uint64_t(1) << lane) - 1));
