@@ -20,7 +20,9 @@ sliding window over a second pool with its own scale, next to the same
 workload's one-segment time) under "two_segment", and with the output
 epilogue (inverse RoPE of the last 64 columns and an MXFP8 store) fused into
 the forward's store, next to the plain forward followed by the separate
-epilogue pass, under "epilogue". The indexer that produces index rows (fp8
+epilogue pass, under "epilogue". The headline decode is timed again on a
+pool that does not fit the MALL (each request's top-k from its own
+16384-row context of a 1.2 GB pool) under "sensitivity". The indexer that produces index rows (fp8
 MQA logits over [ks, ke) windows, then a per-row top-k) is timed on the
 shapes of its own kernel-time table under "indexer".
 """
@@ -76,6 +78,9 @@ def parse():
                     help="indexer workloads timed (fp8 MQA logits, then the top-k)")
     ap.add_argument("--epilogue", default="decode_bf16,decode_fp8",
                     help="workloads also timed with the fused inverse-RoPE + MXFP8 store")
+    ap.add_argument("--sensitivity", default="decode_fp8_ctx",
+                    help="decode workloads whose pool does not fit the MALL, reported next to "
+                         "the headline ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
@@ -370,6 +375,18 @@ def main():
             "kernel_avg_us": round(kernel_us, 2),
         },
     }
+    sens = []
+    for name in [s for s in args.sensitivity.split(",") if s]:
+        r = time_workload(name, args.steps, 3, cold)
+        sus = statistics.median(r["times"])
+        sens.append({"workload": name, "description": r["inp"].workload.description,
+                     "us_per_call": round(sus, 1), "warm_us_per_call": round(r["warm_us"], 1),
+                     "alg_tbs": round(r["alg"]["bytes"] / (sus * 1e-6) / 1e12, 2),
+                     "hbm_frac": round(r["alg"]["bytes"] / (sus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "plan": r["plan"]})
+        del r
+    if sens:
+        line["sensitivity"] = sens
     prefill = []
     for name in [s for s in args.prefill.split(",") if s]:
         r = time_workload(name, max(3, args.steps // 2), 2, cold)

@@ -96,6 +96,23 @@ WORKLOADS: dict[str, Workload] = {
 }
 
 
+# Measurement-only variants (drawn by the benchmark, not by the tests: the
+# pool below is 1.2 GB). decode_fp8 draws its indices over the whole 151 MB
+# pool, which a cold call still finds largely in the 256 MB MALL after its
+# first touches (every pool row is gathered about six times per call); here
+# each request owns its own 16384-row context, as a serving pool of 128
+# requests would, so the pool does not fit.
+SENSITIVITY_WORKLOADS: dict[str, Workload] = {
+    "decode_fp8_ctx": Workload(
+        name="decode_fp8_ctx", rows=768, heads=16, d_qk=576, pool_rows=2097152, topk=2048,
+        kv_dtype="fp8", seed=5, index_mode="request", rows_per_request=6,
+        ctx_per_request=16384,
+        description="fp8 decode, MALL sensitivity: 128 requests x (5+1) rows, 16 heads, fp8 "
+                    "pool 2097152x576 (1.2 GB), each request's top-k 2048 from its own "
+                    "16384-row context, no invalid"),
+}
+
+
 @dataclass
 class Inputs:
     q: torch.Tensor          # bf16 [R, H, D]
@@ -198,7 +215,7 @@ def make_inputs(w: Workload | str, rows: int | None = None) -> Inputs:
     byte-identical to the same rows of the full draw.
     """
     if isinstance(w, str):
-        w = WORKLOADS[w]
+        w = WORKLOADS[w] if w in WORKLOADS else SENSITIVITY_WORKLOADS[w]
     gen = torch.Generator(device="cpu").manual_seed(w.seed)
     q = torch.randn((w.rows, w.heads, w.d_qk), generator=gen, dtype=torch.float32)
     q = q.to(torch.bfloat16)
