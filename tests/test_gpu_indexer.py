@@ -99,7 +99,7 @@ def test_logits_workloads_sampled_rows(name):
     print(f"[indexer logits] {name}: {assert_logits(got, inp, rows)}", flush=True)
 
 
-@pytest.mark.parametrize("R,N,k", [(30, 500, 64), (12, 5000, 2048), (6, 70000, 2048),
+@pytest.mark.parametrize("R,N,k", [(30, 500, 64), (12, 5000, 2048), (6, 70000, 2048), (20, 40000, 2048),
                                    (18, 3000, 512)])
 def test_topk_equals_oracle(R, N, k):
     print(f"\n[indexer topk] R={R} N={N} k={k}", flush=True)
