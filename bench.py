@@ -55,8 +55,6 @@ def attention_kernel(plan, d_qk, fp8):
     if hb == 64 and v != 1:
         if fp8 and v == 0:
             return f"smla::prefill_fp8_kernel<{d_qk}, false>", "prefill_fp8.hip"
-        if fp8 and v == 3:
-            return f"smla::prefill_pp_kernel<{d_qk}, false>", "prefill_pp.hip"
         return f"smla::prefill_kernel<{d_qk}, {str(fp8).lower()}, false>", "prefill.hip"
     return "smla::fwd_kernel (staged tile)", "kernels.hip"
 

@@ -75,13 +75,11 @@ typedef struct smla_options {
   int32_t head_block;      /* 0 = planner's choice, else 16, 32 or 64 heads per workgroup */
   int32_t splits;          /* 0 = planner's choice, else 1..64 splits of each row's slots */
   int32_t remap;           /* 0 = planner's choice, 1 = XCD-aware order, 2 = grid order */
-  int32_t variant;         /* kernel instance; 0 = default. 16-head fp8: 1 = 4-wave
-                              64-slot staged-tile kernel, 2 = 8-wave 128-slot staged-tile
-                              kernel with two tiles of gathers in flight. 64-head: 1 =
-                              single-buffered staged-tile kernel, 2 = 8-wave
-                              double-buffered kernel (the default over bf16 pools; the
-                              fp8 default is the 4-wave kernel), 3 = fp8 only: 8 waves
-                              with the QK and PV work on separate wavefronts */
+  int32_t variant;         /* kernel instance; 0 = default. 1 = the staged-tile kernel
+                              (any head block; also what pools past the 32-bit buffer
+                              range use). 2 = 64 heads only: the 8-wave double-buffered
+                              kernel (the default over bf16 pools; the fp8 default is
+                              the 4-wave kernel) */
   void* workspace;         /* optional caller device buffer for split partials */
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
   const void* q_scale;     /* fp32 [1] device pointer: per-tensor scale of a float8_e4m3fn q
@@ -318,6 +316,11 @@ SMLA_API int sparse_mla_plan(const smla_tensor* q, const smla_tensor* kv_pool, c
  * (remap = 1) or grid order (remap = 0). Host-side copy of the device map,
  * exported so the order can be checked without a GPU. Returns -1 on bad input. */
 SMLA_API int64_t sparse_mla_work_of(int64_t pid, int64_t grid, int32_t remap);
+
+/* Bytes of the library-owned split workspace currently held for `device`
+ * (0 before the first split call there; -1 for a device id outside
+ * [0, 64)). Host-only; makes no HIP call. */
+SMLA_API int64_t sparse_mla_workspace_bytes(int32_t device);
 
 /* Thread-local text for the last non-OK status of the calling thread. */
 SMLA_API const char* sparse_mla_last_error(void);

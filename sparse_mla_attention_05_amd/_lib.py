@@ -22,6 +22,7 @@ UNKNOWN_DTYPE = 1000  # any dtype the library does not know (e.g. float8_e4m3fnu
 
 EXPORTED = (
     "sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_fwd2", "sparse_mla_fwd_epi",
+    "sparse_mla_workspace_bytes",
     "sparse_mla_out_epilogue", "sparse_mla_is_supported", "sparse_mla_plan", "sparse_mla_plan2",
     "sparse_mla_work_of", "sparse_mla_last_error", "sparse_mla_version",
     "sparse_mla_indexer_logits", "sparse_mla_indexer_topk",
@@ -79,6 +80,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_fwd_ex.argtypes = [T, T, T, T, ctypes.c_float, T, T, ctypes.c_void_p,
                                       ctypes.POINTER(SmlaOptions)]
     lib.sparse_mla_fwd_ex.restype = ctypes.c_int
+    lib.sparse_mla_workspace_bytes.argtypes = [ctypes.c_int32]
+    lib.sparse_mla_workspace_bytes.restype = ctypes.c_int64
     lib.sparse_mla_fwd2.argtypes = [T, T, T, T, T, T, T, ctypes.c_float, T, T, ctypes.c_void_p,
                                     ctypes.POINTER(SmlaOptions)]
     lib.sparse_mla_fwd2.restype = ctypes.c_int
@@ -195,6 +198,11 @@ def sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd_ex(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), _ptr(ds[3]),
                                  float(sm_scale), _ptr(ds[4]), _ptr(ds[5]), st, ctypes.byref(opt)))
+
+
+def workspace_bytes(device: int = 0) -> int:
+    """Bytes of the library-owned split workspace held for `device`."""
+    return int(load().sparse_mla_workspace_bytes(int(device)))
 
 
 def status_of_fwd(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None) -> int:

@@ -230,14 +230,16 @@ struct Workspace {
   int64_t bytes = 0;
 };
 std::mutex g_ws_mutex;
-Workspace g_ws[64];
+Workspace g_ws[kMaxDevices];
 
 int device_workspace(int dev, int64_t need, void** out) {
-  if (dev < 0 || dev >= 64) return fail(SMLA_ERR_UNSUPPORTED, "device id beyond 63");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SMLA_ERR_UNSUPPORTED, "device id beyond 63");
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace& w = g_ws[dev];
   if (w.bytes < need) {
     hipError_t e;
+    // At least double, so a run of growing requests reallocates O(log) times.
+    const int64_t grow = std::max<int64_t>(need, 2 * w.bytes);
     if (w.ptr) {
       if ((e = hipDeviceSynchronize()) != hipSuccess)
         return fail(SMLA_ERR_HIP, std::string("hipDeviceSynchronize: ") + hipGetErrorString(e));
@@ -246,7 +248,6 @@ int device_workspace(int dev, int64_t need, void** out) {
       w.ptr = nullptr;
       w.bytes = 0;
     }
-    const int64_t grow = std::max<int64_t>(need, 2 * w.bytes);
     if ((e = hipMalloc(&w.ptr, size_t(grow))) != hipSuccess) {
       w.ptr = nullptr;
       return fail(SMLA_ERR_HIP, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
@@ -257,10 +258,10 @@ int device_workspace(int dev, int64_t need, void** out) {
   return SMLA_OK;
 }
 
-int g_cu_count[64] = {0};
+int g_cu_count[kMaxDevices] = {0};
 
 int device_cus(int dev) {
-  if (dev < 0 || dev >= 64) return 256;
+  if (dev < 0 || dev >= kMaxDevices) return 256;
   if (g_cu_count[dev] == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -515,8 +516,9 @@ int fwd_one(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
   if (plan.splits > 1) {
     void* ws = nullptr;
     int64_t lse_off = 0;
-    const int64_t need = partial_bytes(plan.splits, c.pb.rows, c.pb.heads, &lse_off);
-    if ((s = get_workspace(dev, opt, std::max(need, plan.workspace_bytes), &ws))) return s;
+    const int64_t need = std::max(partial_bytes(plan.splits, c.pb.rows, c.pb.heads, &lse_off),
+                                  plan.workspace_bytes);
+    if ((s = get_workspace(dev, opt, need, &ws))) return s;
     p.part_o = static_cast<float*>(ws);
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_off);
   }
@@ -838,6 +840,12 @@ int sparse_mla_plan(const smla_tensor* q, const smla_tensor* kv_pool, const smla
 int64_t sparse_mla_work_of(int64_t pid, int64_t grid, int32_t remap) {
   if (grid <= 0 || pid < 0 || pid >= grid) return -1;
   return remap ? smla_xcd_work(pid, grid) : pid;
+}
+
+int64_t sparse_mla_workspace_bytes(int32_t device) {
+  if (device < 0 || device >= kMaxDevices) return -1;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  return g_ws[device].bytes;
 }
 
 const char* sparse_mla_last_error(void) { return g_last_error.c_str(); }

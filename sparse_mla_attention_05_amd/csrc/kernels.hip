@@ -74,9 +74,8 @@ struct Cfg {
 };
 
 // One workgroup: (row, block of HB = 16*NHG heads, split). NW waves, TK-slot
-// tiles. DBUF keeps two tiles of gathers in flight (two register buffers,
-// the tile loop unrolled by two); otherwise one.
-template <int NHG, int NW, int TK_, bool DBUF, int DQK, bool FP8, bool EPI>
+// tiles, one tile of gathers in flight.
+template <int NHG, int NW, int TK_, int DQK, bool FP8, bool EPI>
 __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   using C = Cfg<NHG, NW, TK_, DQK, FP8>;
   constexpr int HB = C::HB, TK = C::TK, PITCH = C::PITCH, PP = C::PP;
@@ -285,39 +284,15 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_kernel(const FwdParams p) {
   u32x4 pre0[LPT];
   int id0 = load_idx(t_begin);
   gather(pre0, id0);
-  if constexpr (!DBUF) {
-    int id_next = load_idx(t_begin + 1);
-    for (int t = t_begin; t < t_end; ++t) {
-      __syncthreads();  // every wave is done with the previous tile, P and alpha
-      stage(pre0, id0);
-      id0 = id_next;
-      if (t + 1 < t_end) gather(pre0, id0);
-      id_next = load_idx(t + 2);
-      __syncthreads();  // tile visible
-      compute();
-    }
-  } else {
-    u32x4 pre1[LPT];
-    int id1 = load_idx(t_begin + 1);
-    if (t_begin + 1 < t_end) gather(pre1, id1);
-    int id_next = load_idx(t_begin + 2);
-    for (int t = t_begin; t < t_end; t += 2) {
-      __syncthreads();
-      stage(pre0, id0);
-      id0 = id_next;
-      if (t + 2 < t_end) gather(pre0, id0);
-      id_next = load_idx(t + 3);
-      __syncthreads();
-      compute();
-      if (t + 1 >= t_end) break;
-      __syncthreads();
-      stage(pre1, id1);
-      id1 = id_next;
-      if (t + 3 < t_end) gather(pre1, id1);
-      id_next = load_idx(t + 4);
-      __syncthreads();
-      compute();
-    }
+  int id_next = load_idx(t_begin + 1);
+  for (int t = t_begin; t < t_end; ++t) {
+    __syncthreads();  // every wave is done with the previous tile, P and alpha
+    stage(pre0, id0);
+    id0 = id_next;
+    if (t + 1 < t_end) gather(pre0, id0);
+    id_next = load_idx(t + 2);
+    __syncthreads();  // tile visible
+    compute();
   }
 
   // ---- epilogue: combine the per-wave row sums, normalise, store
@@ -428,37 +403,32 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
   if (tid == 0) p.lse[r * p.lse_rs + int64_t(h) * p.lse_hs] = m + __logf(tot);
 }
 
-// Kernel instances per (head block, pool dtype, variant): waves, tile size,
-// whether two tiles of gathers are kept in flight. For 16 heads over an fp8
-// pool, variant 0 is the decode kernel (decode.hip); variant 1 is the
-// 4-wave, 64-slot instance below and variant 2 runs 8 waves over 128-slot
-// tiles, one workgroup per CU (its bf16 tile takes 146 KB of LDS), with two
-// tiles of gathers in flight. For 64 heads, variant 0 is the 4-wave kernel
-// of prefill_fp8.hip over fp8 pools and the 8-wave kernel of prefill.hip
-// over bf16 pools, variant 1 the 8-wave staged-tile instance below and
-// variant 2 the 8-wave kernel of prefill.hip. Elsewhere every variant is
-// variant 0.
-template <int NHG, int NW, int TK, bool DBUF>
+// Kernel instances per (head block, pool dtype, variant): waves and tile size. For 16 heads over an fp8
+// pool, variant 0 is the decode kernel (decode.hip) and variant 1 the
+// 4-wave, 64-slot instance below. For 64 heads, variant 0 is the 4-wave
+// kernel of prefill_fp8.hip over fp8 pools and the 8-wave kernel of
+// prefill.hip over bf16 pools, variant 1 the 8-wave staged-tile instance
+// below and variant 2 the 8-wave kernel of prefill.hip. Elsewhere every
+// variant is variant 0.
+template <int NHG, int NW, int TK>
 struct Inst {
   static constexpr int kNHG = NHG, kNW = NW, kTK = TK;
-  static constexpr bool kDBUF = DBUF;
 };
 template <int HB, bool FP8, int V> struct InstFor;
-template <int V> struct InstFor<16, true, V> : Inst<1, 4, 64, false> {};
-template <> struct InstFor<16, true, 2> : Inst<1, 8, 128, true> {};
-template <int V> struct InstFor<16, false, V> : Inst<1, 4, 64, false> {};
-template <bool FP8, int V> struct InstFor<32, FP8, V> : Inst<2, 8, 64, false> {};
-template <bool FP8, int V> struct InstFor<64, FP8, V> : Inst<4, 8, 64, false> {};
+template <int V> struct InstFor<16, true, V> : Inst<1, 4, 64> {};
+template <int V> struct InstFor<16, false, V> : Inst<1, 4, 64> {};
+template <bool FP8, int V> struct InstFor<32, FP8, V> : Inst<2, 8, 64> {};
+template <bool FP8, int V> struct InstFor<64, FP8, V> : Inst<4, 8, 64> {};
 
 template <int HB, int V, int DQK, bool FP8>
 hipError_t launch_inst(const FwdParams& p, hipStream_t st) {
   using I = InstFor<HB, FP8, V>;
   const dim3 grid(uint32_t(p.grid)), block(I::kNW * 64);
   if (epi_active(p.epi) && p.part_o == nullptr)
-    hipLaunchKernelGGL((fwd_kernel<I::kNHG, I::kNW, I::kTK, I::kDBUF, DQK, FP8, true>), grid,
+    hipLaunchKernelGGL((fwd_kernel<I::kNHG, I::kNW, I::kTK, DQK, FP8, true>), grid,
                        block, 0, st, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<I::kNHG, I::kNW, I::kTK, I::kDBUF, DQK, FP8, false>), grid,
+    hipLaunchKernelGGL((fwd_kernel<I::kNHG, I::kNW, I::kTK, DQK, FP8, false>), grid,
                        block, 0, st, p);
   return hipGetLastError();
 }
@@ -479,12 +449,11 @@ hipError_t launch_by_head_block(int head_block, int variant, const FwdParams& p,
   switch (head_block) {
     case 16:
       if (FP8 && variant == 0) return static_cast<hipError_t>(launch_decode(p, DQK, st));
-      return variant == 2 ? launch_inst<16, 2, DQK, FP8>(p, st) : launch_inst<16, 0, DQK, FP8>(p, st);
+      return launch_inst<16, 0, DQK, FP8>(p, st);
     case 32: return launch_inst<32, 0, DQK, FP8>(p, st);
     case 64:
       if (variant == 1) return launch_inst<64, 0, DQK, FP8>(p, st);
       if (FP8 && variant == 0) return static_cast<hipError_t>(launch_prefill_fp8(p, DQK, st));
-      if (FP8 && variant == 3) return static_cast<hipError_t>(launch_prefill_pp(p, DQK, st));
       return static_cast<hipError_t>(launch_prefill(p, DQK, FP8, st));
     default: return hipErrorInvalidValue;
   }
@@ -497,13 +466,11 @@ KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant) {
   switch (head_block) {
     case 16:
       if (fp8 && variant == 0) return decode_shape(dqk);
-      if (variant == 2) return fp8 ? shape_of<16, true, 2>(dqk) : shape_of<16, false, 2>(dqk);
       return fp8 ? shape_of<16, true, 0>(dqk) : shape_of<16, false, 0>(dqk);
     case 32: return fp8 ? shape_of<32, true, 0>(dqk) : shape_of<32, false, 0>(dqk);
     case 64:
       if (variant == 1) return fp8 ? shape_of<64, true, 0>(dqk) : shape_of<64, false, 0>(dqk);
       if (fp8 && variant == 0) return prefill_fp8_shape(dqk);
-      if (fp8 && variant == 3) return prefill_pp_shape(dqk);
       return prefill_shape(dqk, fp8);
     default: return KernelShape{};
   }

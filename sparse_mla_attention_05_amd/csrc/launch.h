@@ -11,6 +11,7 @@ constexpr int kDv = 512;        // value width: the first 512 columns of a row
 constexpr int kMaxSplits = 64;
 constexpr int kMaxHeads = 1024;
 constexpr int64_t kMaxTopk = int64_t(1) << 20;
+constexpr int kMaxDevices = 64;
 
 // Where and how the output epilogue stores (epilogue.h): the inverse RoPE of
 // columns 448..511 when pos is set, and an MXFP8 store (codes in q8, E8M0
@@ -162,10 +163,6 @@ int launch_prefill(const FwdParams& p, int dqk, bool fp8, void* stream);
 // The 4-wave 64-head kernel for fp8 pools (prefill_fp8.hip).
 KernelShape prefill_fp8_shape(int dqk);
 int launch_prefill_fp8(const FwdParams& p, int dqk, void* stream);
-
-// 64 heads, fp8 pools, QK and PV on separate wavefronts (prefill_pp.hip).
-KernelShape prefill_pp_shape(int dqk);
-int launch_prefill_pp(const FwdParams& p, int dqk, void* stream);
 
 // True when the (head block, pool dtype, variant) instance addresses the pool
 // through a buffer descriptor with 32-bit offsets (pools up to

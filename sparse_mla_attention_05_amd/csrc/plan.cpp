@@ -36,7 +36,7 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   static const char* kBadSplit = "splits override must be in [0, 64]";
   static const char* kBadRemap = "remap override must be 0, 1 or 2";
   static const char* kBadGrid = "launch grid exceeds 2^31 - 1 workgroups";
-  static const char* kBadVariant = "variant override must be 0, 1, 2 or 3 (3: 64 heads, fp8 only)";
+  static const char* kBadVariant = "variant override must be 0, 1 or 2 (2: 64 heads only)";
   if (num_cus <= 0) num_cus = 256;
   *plan = smla_plan{};
 
@@ -52,8 +52,7 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   }
   int variant = 0;
   if (opt && opt->variant) {
-    if (opt->variant < 1 || opt->variant > 3 ||
-        (opt->variant == 3 && !(hb == 64 && pb.kv_fp8))) {
+    if (opt->variant < 1 || opt->variant > 2 || (opt->variant == 2 && hb != 64)) {
       *err = kBadVariant;
       return SMLA_ERR_INVALID_ARG;
     }

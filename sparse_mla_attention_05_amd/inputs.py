@@ -96,8 +96,8 @@ WORKLOADS: dict[str, Workload] = {
 }
 
 
-# Measurement-only variants (drawn by the benchmark, not by the tests: the
-# pool below is 1.2 GB). decode_fp8 draws its indices over the whole 151 MB
+# Workloads beyond the five (the benchmark's MALL-sensitivity line; its GPU
+# parity test checks sampled rows, since the pool below is 1.2 GB). decode_fp8 draws its indices over the whole 151 MB
 # pool, which a cold call still finds largely in the 256 MB MALL after its
 # first touches (every pool row is gathered about six times per call); here
 # each request owns its own 16384-row context, as a serving pool of 128

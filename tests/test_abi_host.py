@@ -422,3 +422,18 @@ def test_paged_extra_pool_is_rejected():
     for k in ("q", "indices", "extra_indices", "out", "lse"):
         a[k] = a[k][:0]
     assert _status2(a) == UNSUP
+
+
+def test_workspace_query_without_a_gpu():
+    assert _lib.workspace_bytes(-1) == -1
+    assert _lib.workspace_bytes(64) == -1
+    assert _lib.workspace_bytes(0) == 0           # nothing allocated without a split call
+
+
+def test_plan_rejects_removed_variants():
+    with pytest.raises(_lib.SparseMLAError):
+        _plan(64, 64, variant=3)
+    with pytest.raises(_lib.SparseMLAError):
+        _plan(64, 16, variant=2)                   # 2 is a 64-head kernel
+    assert _plan(64, 64, variant=2)["variant"] == 2
+    assert _plan(64, 16, variant=1)["variant"] == 1

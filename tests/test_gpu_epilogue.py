@@ -7,7 +7,7 @@ MXFP8 store), through the C ABI.
    both sides take every rounding and every e4m3 decision in the same
    precision.
 2. The fused store of every kernel path (decode, 64-head fp8 and bf16, the
-   role-split kernel, the staged-tile kernel, split-K through the combine
+   8-wave kernel over fp8, the staged-tile kernel, split-K through the combine
    kernel, both two-segment routes) equals the same call's plain bf16 output
    run through the separate pass, bit for bit.
 3. The fused output against the fp64 attention oracle followed by the
@@ -211,7 +211,6 @@ PATHS = [
     ("fp8", 576, 20, 256, {}),                                  # 16-head blocks, one partial
     ("fp8", 576, 64, 512, {}),                                  # 64-head fp8 kernel
     ("fp8", 512, 64, 300, {}),
-    ("fp8", 576, 64, 512, dict(variant=3)),                     # QK / PV role-split kernel
     ("fp8", 576, 64, 512, dict(variant=2)),                     # 8-wave kernel over fp8
     ("fp8", 576, 64, 512, dict(variant=1)),                     # staged-tile kernel, 64 heads
     ("bf16", 576, 64, 512, {}),                                 # 8-wave kernel over bf16

@@ -109,6 +109,44 @@ def test_prefill_parity_on_sampled_rows(name):
     print(f"[parity] {name}: {stats}", flush=True)
 
 
+def test_decode_past_the_mall_on_sampled_rows():
+    """decode_fp8_ctx: the headline decode over a 1.2 GB pool (2,097,152 rows,
+    each request's top-k from its own 16,384-row context), in the launch the
+    benchmark times; pool offsets reach about 1.2e9 bytes. The oracle checks
+    every 8th row plus the last one."""
+    print("\n[parity] workload=decode_fp8_ctx (sampled rows)", flush=True)
+    inp = make_inputs("decode_fp8_ctx")
+    out, lse = run_gpu(inp)
+    R = inp.q.shape[0]
+    rows = np.unique(np.r_[np.arange(0, R, 8), R - 1])
+    ref_out, ref_lse = run_oracle(inp, rows=rows)
+    stats = assert_parity(out, lse, ref_out, ref_lse, inp.indices, rows=torch.from_numpy(rows))
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    assert int(inp.indices.max()) > 2_000_000   # rows near the pool's end are read
+    print(f"[parity] decode_fp8_ctx: {stats}", flush=True)
+
+
+def test_library_workspace_grows_by_doubling():
+    """Three split calls with growing partials: the library-owned workspace
+    grows to at least twice its size when it grows, so the last two calls
+    reallocate at most once."""
+    dev = torch.cuda.current_device()
+    b0 = _lib.workspace_bytes(dev)
+    sizes = []
+    rows0 = max(8, b0 // (16 * 4 * 513 * 4) + 1)   # partials past the current buffer
+    for i, rows in enumerate([rows0, rows0 + rows0 // 4, rows0 + rows0 // 2]):
+        inp = _case(rows=int(rows), heads=16, topk=256, pool_rows=2000, kv_dtype="fp8", seed=90 + i)
+        dev_inp = _dev(inp)
+        need = _lib.sparse_mla_plan(dev_inp[0], dev_inp[1], dev_inp[3], splits=4)["workspace_bytes"]
+        run_gpu(inp, dev=dev_inp, splits=4)
+        sizes.append((need, _lib.workspace_bytes(dev)))
+    print(f"\n[workspace] start {b0}, (need, held) per call: {sizes}", flush=True)
+    (n1, b1), (n2, b2), (n3, b3) = sizes
+    assert b1 >= n1 and b1 >= 2 * b0
+    assert b2 >= n2 and (b2 == b1 or b2 >= 2 * b1)
+    assert n3 <= 2 * n1 and b3 == b2, "the third call must fit what the growth left"
+
+
 # ------------------------------------------------------------- edge cases
 
 def _case(**kw):
@@ -267,12 +305,12 @@ def test_zero_rows_noop():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (129, 1), (17, 1), (1000, 3), (2048, 5)])
 def test_decode_fp8_variants(variant, topk, splits):
-    """The three 16-head fp8 kernels (the decode kernel; the staged-tile kernel
-    with 4 waves over 64-slot tiles; with 8 waves over 128-slot tiles and two
-    tiles in flight) on ragged top-k, with and without splits."""
+    """The two 16-head fp8 kernels (the decode kernel; the staged-tile kernel
+    with 4 waves over 64-slot tiles) on ragged top-k, with and without
+    splits."""
     inp = _case(rows=7, heads=16, topk=topk, pool_rows=8192, kv_dtype="fp8", invalid_per_row=37,
                 seed=topk + splits)
     idx = inp.indices.clone()
@@ -298,17 +336,14 @@ def test_decode_index_chunks(topk, splits, heads, d_qk):
     _check(inp, variant=0, splits=splits)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("d_qk,kv,heads", [(576, "fp8", 64), (512, "fp8", 80), (576, "bf16", 64)])
 @pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (17, 1), (1000, 3)])
 def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
     """The 64-head kernels (variant 0: the 4-wave kernel over fp8 pools, the
     8-wave kernel over bf16 pools; 1: the single-buffered staged-tile kernel;
-    2: the 8-wave kernel; 3: the kernel with separate QK and PV waves, fp8
-    only) on ragged top-k, odd tile counts, a partial head block, leading
-    invalid tiles and an empty row, with and without splits."""
-    if variant == 3 and kv != "fp8":
-        pytest.skip("variant 3 is the fp8 kernel only")
+    2: the 8-wave kernel) on ragged top-k, odd tile counts, a partial head
+    block, leading invalid tiles and an empty row, with and without splits."""
     inp = _case(rows=5, heads=heads, d_qk=d_qk, topk=topk, pool_rows=8192, kv_dtype=kv,
                 invalid_per_row=29, seed=topk + splits + d_qk)
     idx = inp.indices.clone()
@@ -320,7 +355,7 @@ def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
     _check(inp, variant=variant, splits=splits, head_block=64)
 
 
-@pytest.mark.parametrize("kv,variant", [("fp8", 0), ("bf16", 0), ("fp8", 3)])
+@pytest.mark.parametrize("kv,variant", [("fp8", 0), ("bf16", 0), ("fp8", 2)])
 @pytest.mark.parametrize("splits", [1, 2])
 def test_score_jump_after_first_tile(kv, variant, splits):
     """Every head's first 64 slots point at near-zero keys and later slots at
