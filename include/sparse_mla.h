@@ -151,6 +151,29 @@ SMLA_API int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
                       void* stream, const smla_options* opt);
 
 /*
+ * sparse_mla_fwd_noalloc - sparse_mla_fwd_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): it calls no hipMalloc, hipFree or allocating
+ * library routine. Split partials go to a fixed device array of
+ * SMLA_NOALLOC_SCRATCH_BYTES that each GPU holds from the first call on it
+ * until the process ends. Every rule of sparse_mla_fwd_ex holds, except:
+ *   - opt->workspace must be NULL and opt->workspace_bytes 0 (else
+ *     SMLA_ERR_INVALID_ARG);
+ *   - a plan whose partials (smla_plan.workspace_bytes) exceed
+ *     SMLA_NOALLOC_SCRATCH_BYTES returns SMLA_ERR_UNSUPPORTED before any
+ *     launch; force fewer splits (opt->splits) or use sparse_mla_fwd_ex.
+ * All calls on one GPU share its array: calls whose work overlaps on one GPU
+ * (different streams, or host threads) race and must be serialised by the
+ * caller. Nothing in the array needs to start at zero: each split writes its
+ * partial output and LSE in full before the combine kernel reads them.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES (32ll * 1024 * 1024)
+SMLA_API int sparse_mla_fwd_noalloc(const smla_tensor* q, const smla_tensor* kv_pool,
+                           const smla_tensor* kv_scale, const smla_tensor* indices,
+                           float sm_scale, smla_tensor* out, smla_tensor* lse, void* stream,
+                           const smla_options* opt);
+
+/*
  * sparse_mla_fwd2 - two-segment forward, after "[Triton/Gluon] GFX950 sparse
  * mla optimizations" (aiter PR 6159), the commit notes on the per-tensor fp8
  * two-loop route: a row attends, under one softmax, to the valid slots of its

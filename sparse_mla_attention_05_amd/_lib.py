@@ -21,8 +21,8 @@ STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTE
 UNKNOWN_DTYPE = 1000  # any dtype the library does not know (e.g. float8_e4m3fnuz)
 
 EXPORTED = (
-    "sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_fwd2", "sparse_mla_fwd_epi",
-    "sparse_mla_workspace_bytes",
+    "sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_fwd_noalloc", "sparse_mla_fwd2",
+    "sparse_mla_fwd_epi", "sparse_mla_workspace_bytes",
     "sparse_mla_out_epilogue", "sparse_mla_is_supported", "sparse_mla_plan", "sparse_mla_plan2",
     "sparse_mla_work_of", "sparse_mla_last_error", "sparse_mla_version",
     "sparse_mla_indexer_logits", "sparse_mla_indexer_topk",
@@ -80,6 +80,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_fwd_ex.argtypes = [T, T, T, T, ctypes.c_float, T, T, ctypes.c_void_p,
                                       ctypes.POINTER(SmlaOptions)]
     lib.sparse_mla_fwd_ex.restype = ctypes.c_int
+    lib.sparse_mla_fwd_noalloc.argtypes = [T, T, T, T, ctypes.c_float, T, T, ctypes.c_void_p,
+                                           ctypes.POINTER(SmlaOptions)]
+    lib.sparse_mla_fwd_noalloc.restype = ctypes.c_int
     lib.sparse_mla_workspace_bytes.argtypes = [ctypes.c_int32]
     lib.sparse_mla_workspace_bytes.restype = ctypes.c_int64
     lib.sparse_mla_fwd2.argtypes = [T, T, T, T, T, T, T, ctypes.c_float, T, T, ctypes.c_void_p,
@@ -198,6 +201,28 @@ def sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd_ex(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), _ptr(ds[3]),
                                  float(sm_scale), _ptr(ds[4]), _ptr(ds[5]), st, ctypes.byref(opt)))
+
+
+def sparse_mla_fwd_noalloc(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None,
+                           head_block=0, splits=0, remap=0, variant=0, q_scale=None) -> None:
+    """sparse_mla_fwd_ex without any device allocation: split partials go to
+    the library's fixed per-device scratch (SMLA_NOALLOC_SCRATCH_BYTES)."""
+    _check(status_of_fwd_noalloc(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream,
+                                 head_block, splits, remap, variant, q_scale))
+
+
+def status_of_fwd_noalloc(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None,
+                          head_block=0, splits=0, remap=0, variant=0, q_scale=None,
+                          workspace=None, workspace_bytes=None) -> int:
+    """Raw status of sparse_mla_fwd_noalloc (a workspace may be passed only to
+    test its rejection)."""
+    lib = load()
+    ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, out, lse)]
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale)
+    st = _stream_handle(stream, q, out)
+    return lib.sparse_mla_fwd_noalloc(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), _ptr(ds[3]),
+                                      float(sm_scale), _ptr(ds[4]), _ptr(ds[5]), st,
+                                      ctypes.byref(opt))
 
 
 def workspace_bytes(device: int = 0) -> int:

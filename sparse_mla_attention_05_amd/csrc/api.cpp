@@ -489,10 +489,13 @@ int plan_two(const Checked& c1, const Checked& c2, const smla_options* opt, int 
   return SMLA_OK;
 }
 
-// One-segment forward with an optional output epilogue.
+// One-segment forward with an optional output epilogue. With `noalloc` the
+// split partials go to the fixed device scratch (noalloc.hip) and nothing is
+// allocated; a plan whose partials do not fit it is rejected.
 int fwd_one(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,
             const smla_tensor* indices, float sm_scale, const smla_epilogue* epi,
-            smla_tensor* out, smla_tensor* lse, void* stream, const smla_options* opt) {
+            smla_tensor* out, smla_tensor* lse, void* stream, const smla_options* opt,
+            bool noalloc = false) {
   Checked c;
   int s = validate_all(q, kv_pool, kv_scale, indices, sm_scale, out, lse, &c, epi_out_dtype(epi));
   if (s) return s;
@@ -518,7 +521,18 @@ int fwd_one(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
     int64_t lse_off = 0;
     const int64_t need = std::max(partial_bytes(plan.splits, c.pb.rows, c.pb.heads, &lse_off),
                                   plan.workspace_bytes);
-    if ((s = get_workspace(dev, opt, need, &ws))) return s;
+    if (noalloc) {
+      if (need > kScratchBytes)
+        return fail(SMLA_ERR_UNSUPPORTED,
+                    "split partials need " + std::to_string(need) +
+                        " bytes, more than the no-allocation scratch (" +
+                        std::to_string(kScratchBytes) +
+                        " bytes): force fewer splits or use sparse_mla_fwd_ex");
+      std::string err;
+      if ((s = scratch_buffer(dev, &ws, &err))) return fail(s, err);
+    } else if ((s = get_workspace(dev, opt, need, &ws))) {
+      return s;
+    }
     p.part_o = static_cast<float*>(ws);
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_off);
   }
@@ -631,6 +645,16 @@ int sparse_mla_fwd_ex(const smla_tensor* q, const smla_tensor* kv_pool,
                       smla_tensor* out, smla_tensor* lse, void* stream,
                       const smla_options* opt) {
   return fwd_one(q, kv_pool, kv_scale, indices, sm_scale, nullptr, out, lse, stream, opt);
+}
+
+int sparse_mla_fwd_noalloc(const smla_tensor* q, const smla_tensor* kv_pool,
+                           const smla_tensor* kv_scale, const smla_tensor* indices,
+                           float sm_scale, smla_tensor* out, smla_tensor* lse, void* stream,
+                           const smla_options* opt) {
+  if (opt && (opt->workspace || opt->workspace_bytes))
+    return fail(SMLA_ERR_INVALID_ARG,
+                "workspace: must be NULL/0 (this entry point uses the library's fixed scratch)");
+  return fwd_one(q, kv_pool, kv_scale, indices, sm_scale, nullptr, out, lse, stream, opt, true);
 }
 
 int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor* kv_scale,

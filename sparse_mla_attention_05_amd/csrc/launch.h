@@ -3,6 +3,8 @@
 #pragma once
 #include <stdint.h>
 
+#include <string>
+
 #include "../../include/sparse_mla.h"
 
 namespace smla {
@@ -12,6 +14,13 @@ constexpr int kMaxSplits = 64;
 constexpr int kMaxHeads = 1024;
 constexpr int64_t kMaxTopk = int64_t(1) << 20;
 constexpr int kMaxDevices = 64;
+// Bytes of the fixed device scratch of the no-allocation forward.
+constexpr int64_t kScratchBytes = SMLA_NOALLOC_SCRATCH_BYTES;
+
+// The calling thread's current device's copy of that scratch (noalloc.hip):
+// its device address, resolved once per device. Returns a status and sets
+// *err on failure. Makes no allocation.
+int scratch_buffer(int dev, void** out, std::string* err);
 
 // Where and how the output epilogue stores (epilogue.h): the inverse RoPE of
 // columns 448..511 when pos is set, and an MXFP8 store (codes in q8, E8M0

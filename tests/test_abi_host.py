@@ -424,6 +424,26 @@ def test_paged_extra_pool_is_rejected():
     assert _status2(a) == UNSUP
 
 
+# ------------------------------------------------------- no-allocation entry
+
+def test_noalloc_validates_before_any_hip_call():
+    """The no-allocation forward takes the forward's checks, and a caller
+    workspace is refused (its partials go to the library's fixed scratch)."""
+    a = _args()
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    st = _lib.status_of_fwd_noalloc(a["q"], a["kv_pool"], a["kv_scale"], a["indices"],
+                                    a["sm_scale"], a["out"], a["lse"], workspace=ws)
+    assert st == INVALID
+    b = _args()
+    st = _lib.status_of_fwd_noalloc(b["q"].float(), b["kv_pool"], b["kv_scale"], b["indices"],
+                                    b["sm_scale"], b["out"], b["lse"])
+    assert st == UNSUP
+    c = _args(R=0)
+    st = _lib.status_of_fwd_noalloc(c["q"], c["kv_pool"], c["kv_scale"], c["indices"],
+                                    c["sm_scale"], c["out"], c["lse"])
+    assert st == _lib.SMLA_OK                     # R == 0: a no-op, no HIP call
+
+
 def test_workspace_query_without_a_gpu():
     assert _lib.workspace_bytes(-1) == -1
     assert _lib.workspace_bytes(64) == -1
