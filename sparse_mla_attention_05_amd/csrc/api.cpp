@@ -169,6 +169,8 @@ int validate_inputs(const smla_tensor* q, const smla_tensor* kv, const smla_tens
   c->pb.dqk = int32_t(D);
   c->pb.topk = int32_t(K);
   c->pb.kv_fp8 = kv->dtype == SMLA_FP8_E4M3FN;
+  c->pb.pool_rs_bytes = rs * eb;
+  c->pb.page_bytes = paged ? kv->stride[0] * eb : 0;
   c->fp8 = c->pb.kv_fp8 != 0;
   c->q_fp8 = q->dtype == SMLA_FP8_E4M3FN;
   // bytes from the base to the end of the last row read

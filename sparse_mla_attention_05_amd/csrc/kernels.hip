@@ -408,8 +408,8 @@ __global__ void __launch_bounds__(128) combine_kernel(const FwdParams p) {
 // 4-wave, 64-slot instance below. For 64 heads, variant 0 is the 4-wave
 // kernel of prefill_fp8.hip over fp8 pools and the 8-wave kernel of
 // prefill.hip over bf16 pools, variant 1 the 8-wave staged-tile instance
-// below and variant 2 the 8-wave kernel of prefill.hip. Elsewhere every
-// variant is variant 0.
+// below, variant 2 the 8-wave kernel of prefill.hip and variant 3 (fp8 pools)
+// the fp8-dot kernel of prefill_mx.hip. Elsewhere every variant is variant 0.
 template <int NHG, int NW, int TK>
 struct Inst {
   static constexpr int kNHG = NHG, kNW = NW, kTK = TK;
@@ -454,6 +454,7 @@ hipError_t launch_by_head_block(int head_block, int variant, const FwdParams& p,
     case 64:
       if (variant == 1) return launch_inst<64, 0, DQK, FP8>(p, st);
       if (FP8 && variant == 0) return static_cast<hipError_t>(launch_prefill_fp8(p, DQK, st));
+      if (FP8 && variant == 3) return static_cast<hipError_t>(launch_prefill_mx(p, DQK, st));
       return static_cast<hipError_t>(launch_prefill(p, DQK, FP8, st));
     default: return hipErrorInvalidValue;
   }
@@ -471,6 +472,7 @@ KernelShape kernel_shape(int head_block, int dqk, bool fp8, int variant) {
     case 64:
       if (variant == 1) return fp8 ? shape_of<64, true, 0>(dqk) : shape_of<64, false, 0>(dqk);
       if (fp8 && variant == 0) return prefill_fp8_shape(dqk);
+      if (fp8 && variant == 3) return prefill_mx_shape(dqk);
       return prefill_shape(dqk, fp8);
     default: return KernelShape{};
   }

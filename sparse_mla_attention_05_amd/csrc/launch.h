@@ -145,6 +145,8 @@ struct Problem {
   int32_t topk;
   int32_t kv_fp8;
   int64_t pool_bytes;       // bytes from pool to the end of its last row read
+  int64_t pool_rs_bytes;    // row stride (bytes)
+  int64_t page_bytes;       // page pitch of a paged pool (bytes), 0 for a 2-D pool
 };
 
 // Largest pool (bytes) the decode kernel addresses through a buffer
@@ -172,6 +174,18 @@ int launch_prefill(const FwdParams& p, int dqk, bool fp8, void* stream);
 // The 4-wave 64-head kernel for fp8 pools (prefill_fp8.hip).
 KernelShape prefill_fp8_shape(int dqk);
 int launch_prefill_fp8(const FwdParams& p, int dqk, void* stream);
+
+// The 64-head kernel for fp8 pools with fp8 dots on two-term splits and LDS
+// DMA tiles (prefill_mx.hip).
+KernelShape prefill_mx_shape(int dqk);
+int launch_prefill_mx(const FwdParams& p, int dqk, void* stream);
+
+// The pool layouts prefill_mx.hip can address: rows through a structured
+// buffer whose stride field holds at most 14 bits, pages a whole number of
+// rows apart.
+inline bool mx_pool_ok(int64_t rs_bytes, int64_t page_bytes) {
+  return rs_bytes > 0 && rs_bytes < (1 << 14) && (page_bytes == 0 || page_bytes % rs_bytes == 0);
+}
 
 // True when the (head block, pool dtype, variant) instance addresses the pool
 // through a buffer descriptor with 32-bit offsets (pools up to

@@ -36,7 +36,8 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   static const char* kBadSplit = "splits override must be in [0, 64]";
   static const char* kBadRemap = "remap override must be 0, 1 or 2";
   static const char* kBadGrid = "launch grid exceeds 2^31 - 1 workgroups";
-  static const char* kBadVariant = "variant override must be 0, 1 or 2 (2: 64 heads only)";
+  static const char* kBadVariant =
+      "variant override must be 0, 1, 2 or 3 (2: 64 heads only; 3: 64 heads, fp8 pools only)";
   if (num_cus <= 0) num_cus = 256;
   *plan = smla_plan{};
 
@@ -52,7 +53,8 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   }
   int variant = 0;
   if (opt && opt->variant) {
-    if (opt->variant < 1 || opt->variant > 2 || (opt->variant == 2 && hb != 64)) {
+    if (opt->variant < 1 || opt->variant > 3 || (opt->variant == 2 && hb != 64) ||
+        (opt->variant == 3 && !(hb == 64 && pb.kv_fp8))) {
       *err = kBadVariant;
       return SMLA_ERR_INVALID_ARG;
     }
@@ -62,6 +64,9 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   // 32-bit buffer range; a larger pool takes the staged-tile kernel.
   if (uses_buffer_range(hb, pb.kv_fp8 != 0, variant) && pb.pool_bytes > kMaxBufferBytes)
     variant = 1;
+  // The fp8-dot kernel addresses rows through a structured buffer; other pool
+  // layouts take the 4-wave kernel.
+  if (variant == 3 && !mx_pool_ok(pb.pool_rs_bytes, pb.page_bytes)) variant = 0;
   const KernelShape ks = kernel_shape(hb, pb.dqk, pb.kv_fp8 != 0, variant);
   const int waves = ks.waves;
   const int lds = ks.lds_bytes;

@@ -450,10 +450,31 @@ def test_workspace_query_without_a_gpu():
     assert _lib.workspace_bytes(0) == 0           # nothing allocated without a split call
 
 
-def test_plan_rejects_removed_variants():
+def test_plan_rejects_unknown_variants():
     with pytest.raises(_lib.SparseMLAError):
-        _plan(64, 64, variant=3)
+        _plan(64, 64, variant=4)
     with pytest.raises(_lib.SparseMLAError):
         _plan(64, 16, variant=2)                   # 2 is a 64-head kernel
     assert _plan(64, 64, variant=2)["variant"] == 2
     assert _plan(64, 16, variant=1)["variant"] == 1
+
+
+def test_plan_fp8_dot_kernel_eligibility():
+    """Variant 3 (the fp8-dot 64-head kernel) addresses pool rows through a
+    structured buffer: 64-head blocks over fp8 pools only, row pitch under
+    16 KB, pages a whole number of rows apart; other layouts take variant 0."""
+    assert _plan(64, 64, variant=3)["variant"] == 3
+    with pytest.raises(_lib.SparseMLAError):
+        _plan(64, 64, dtype=torch.bfloat16, variant=3)
+    q = torch.zeros(8, 64, 576, dtype=torch.bfloat16)
+    idx = torch.zeros(8, 256, dtype=torch.int32)
+    flat = torch.zeros(4096, 576, dtype=torch.float8_e4m3fn)
+    paged_ok = torch.zeros(64 * 65 * 576, dtype=torch.float8_e4m3fn).as_strided(
+        (64, 64, 576), (65 * 576, 576, 1))
+    paged_odd = torch.zeros(64 * (64 * 576 + 1024), dtype=torch.float8_e4m3fn).as_strided(
+        (64, 64, 576), (64 * 576 + 1024, 576, 1))
+    wide = torch.zeros(16, 20000, dtype=torch.float8_e4m3fn)[:, :576]
+    assert _lib.sparse_mla_plan(q, flat, idx, variant=3)["variant"] == 3
+    assert _lib.sparse_mla_plan(q, paged_ok, idx, variant=3)["variant"] == 3
+    assert _lib.sparse_mla_plan(q, paged_odd, idx, variant=3)["variant"] == 0
+    assert _lib.sparse_mla_plan(q, wide, idx, variant=3)["variant"] == 0

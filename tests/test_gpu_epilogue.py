@@ -212,6 +212,8 @@ PATHS = [
     ("fp8", 576, 64, 512, {}),                                  # 64-head fp8 kernel
     ("fp8", 512, 64, 300, {}),
     ("fp8", 576, 64, 512, dict(variant=2)),                     # 8-wave kernel over fp8
+    ("fp8", 576, 64, 512, dict(variant=3)),                     # fp8-dot kernel
+    ("fp8", 512, 64, 300, dict(variant=3, head_block=64, splits=2)),  # fp8-dot, combine
     ("fp8", 576, 64, 512, dict(variant=1)),                     # staged-tile kernel, 64 heads
     ("bf16", 576, 64, 512, {}),                                 # 8-wave kernel over bf16
     ("bf16", 512, 64, 700, dict(head_block=64, splits=2)),      # split-K: combine

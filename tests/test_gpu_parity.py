@@ -94,13 +94,15 @@ def test_workload_full_parity(name):
     print(f"[parity] {name}: {stats}", flush=True)
 
 
+@pytest.mark.parametrize("variant", [0, 3])
 @pytest.mark.parametrize("name", ["prefill_fp8", "prefill_glm"])
-def test_prefill_parity_on_sampled_rows(name):
+def test_prefill_parity_on_sampled_rows(name, variant):
     """The whole workload runs in the launch the benchmark times; the oracle
-    checks every 64th row plus the last one."""
-    print(f"\n[parity] workload={name} (sampled rows)", flush=True)
+    checks every 64th row plus the last one (variant 3: the fp8-dot 64-head
+    kernel)."""
+    print(f"\n[parity] workload={name} variant={variant} (sampled rows)", flush=True)
     inp = make_inputs(name)
-    out, lse = run_gpu(inp)
+    out, lse = run_gpu(inp, **({"variant": variant} if variant else {}))
     R = inp.q.shape[0]
     rows = np.unique(np.r_[np.arange(0, R, 64), R - 1])
     ref_out, ref_lse = run_oracle(inp, rows=rows)
@@ -336,14 +338,19 @@ def test_decode_index_chunks(topk, splits, heads, d_qk):
     _check(inp, variant=0, splits=splits)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
-@pytest.mark.parametrize("d_qk,kv,heads", [(576, "fp8", 64), (512, "fp8", 80), (576, "bf16", 64)])
-@pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (17, 1), (1000, 3)])
+VARIANT_SHAPES = [(v, d, kv, h) for v in (0, 1, 2, 3)
+                  for d, kv, h in [(576, "fp8", 64), (512, "fp8", 80), (576, "bf16", 64)]
+                  if not (v == 3 and kv == "bf16")]
+
+
+@pytest.mark.parametrize("variant,d_qk,kv,heads", VARIANT_SHAPES)
+@pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (17, 1), (1000, 3), (300, 2)])
 def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
     """The 64-head kernels (variant 0: the 4-wave kernel over fp8 pools, the
     8-wave kernel over bf16 pools; 1: the single-buffered staged-tile kernel;
-    2: the 8-wave kernel) on ragged top-k, odd tile counts, a partial head
-    block, leading invalid tiles and an empty row, with and without splits."""
+    2: the 8-wave kernel; 3: the fp8-dot kernel, fp8 pools only) on ragged
+    top-k, odd tile counts, a partial head block, leading invalid tiles and
+    an empty row, with and without splits."""
     inp = _case(rows=5, heads=heads, d_qk=d_qk, topk=topk, pool_rows=8192, kv_dtype=kv,
                 invalid_per_row=29, seed=topk + splits + d_qk)
     idx = inp.indices.clone()
@@ -355,7 +362,7 @@ def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
     _check(inp, variant=variant, splits=splits, head_block=64)
 
 
-@pytest.mark.parametrize("kv,variant", [("fp8", 0), ("bf16", 0), ("fp8", 2)])
+@pytest.mark.parametrize("kv,variant", [("fp8", 0), ("bf16", 0), ("fp8", 2), ("fp8", 3)])
 @pytest.mark.parametrize("splits", [1, 2])
 def test_score_jump_after_first_tile(kv, variant, splits):
     """Every head's first 64 slots point at near-zero keys and later slots at

@@ -34,6 +34,7 @@ FP8Q_CASES = [
     ("fp8", 576, 16, 512, {}),                          # decode kernel
     ("fp8", 576, 16, 300, dict(head_block=16, splits=3)),
     ("fp8", 576, 64, 512, {}),                          # 64-head fp8 kernel
+    ("fp8", 576, 64, 512, dict(variant=3)),             # fp8-dot kernel
     ("fp8", 512, 64, 300, dict(variant=2)),             # 8-wave kernel over fp8
     ("bf16", 576, 64, 512, {}),                         # 8-wave kernel
     ("bf16", 576, 16, 200, {}),                         # staged-tile kernel
@@ -102,6 +103,8 @@ PAGED_CASES = [
     ("fp8", 576, 16, 512, 64, 256, {}),                        # decode kernel
     ("fp8", 576, 16, 300, 16, 4096, dict(head_block=16, splits=3)),
     ("fp8", 576, 64, 512, 64, 1024, {}),                       # 64-head fp8 kernel
+    ("fp8", 576, 64, 512, 64, 576, dict(variant=3)),           # fp8-dot kernel: pages of whole rows
+    ("fp8", 512, 64, 300, 32, 512, dict(variant=3)),           # fp8-dot kernel, 512-wide
     ("fp8", 512, 64, 300, 32, 512, dict(variant=2)),           # 8-wave kernel over fp8
     ("bf16", 576, 64, 512, 1, 128, {}),                        # one row per page
     ("bf16", 512, 16, 200, 128, 2048, {}),                     # staged-tile kernel
