@@ -173,6 +173,27 @@ __device__ __forceinline__ void epi_store_c16x2(const EpiOut& e, const float* cs
   epi_emit<4>(e, r, h, col_a + 16, vb, sc, inv);
 }
 
+// The store of an MFMA 32x32 accumulator layout in which a lane holds four
+// groups of 4 consecutive columns at col_a + 8j (j = 0..3, col_a = 32m + 4h,
+// h = lane bit 5): the 32-column block [32m, 32m + 32) is spread over the
+// two lanes l and l ^ 32, which must make this call together.
+__device__ __forceinline__ void epi_store_c32x4(const EpiOut& e, const float* cs_row, int64_t r,
+                                                int h, int col_a, float (&v)[4][4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) epi_prepare<4>(cs_row, col_a + 8 * j, v[j]);
+  uint32_t sc = 0u;
+  float inv = 1.f;
+  if (e.q8 != nullptr) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, abs_max<4>(v[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    sc = e8m0_code(amax, &inv);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) epi_emit<4>(e, r, h, col_a + 8 * j, v[j], sc, inv);
+}
+
 // A workgroup's block of nh heads of row r staged in LDS as bf16 rows of
 // kEpiPitch elements: local head i < split at lo + i * kEpiPitch, the others
 // at hi + (i - split) * kEpiPitch. Thread tid of nt stores 32-column pieces

@@ -1,5 +1,6 @@
 // gfx950 64-head kernel of the sparse MLA forward over an fp8 e4m3fn pool,
-// 576- or 512-wide rows, with both products on the fp8 matrix cores.
+// 576- or 512-wide rows, with both products on the fp8 matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4).
 //
 // The method (per row r, head h, over the row's valid slots j):
 //   s_j = sm_scale * q[r,h] . K[idx_j] (D_qk columns), out = softmax(s) V
@@ -10,12 +11,11 @@
 // per-tensor fp8 scale taken off in the epilogue).
 //
 // The pages widen the fp8 keys to bf16 for their dots and reject fp8 dots on
-// accuracy grounds (a single fp8 P). This kernel keeps the dots on
-// v_mfma_scale_f32_16x16x128_f8f6f4, which on gfx950 does four times the
-// work of a bf16 16x16x32 dot in about twice its time, and keeps bf16-class
-// accuracy by splitting the bf16/fp32 operands into two e4m3 terms:
+// accuracy grounds (a single fp8 P). This kernel keeps the dots on the fp8
+// matrix cores and keeps bf16-class accuracy by splitting the bf16/fp32
+// operands into two e4m3 terms:
 //  * q (bf16, 8 significant bits) times a power of two 2^e that puts the
-//    wave's largest |q| in [128, 256) is q' = hi + lo/16 with hi = e4m3(q')
+//    head's largest |q| in [128, 256) is q' = hi + lo/16 with hi = e4m3(q')
 //    and lo = e4m3((q' - hi) * 16). The residual q' - hi is a multiple of
 //    q's last bit no larger than half of hi's, so it has at most 4
 //    significant bits and lo holds it exactly: the split is exact except for
@@ -27,38 +27,50 @@
 //  * The fp8 keys and values are used as stored (exact), so tiles stay fp8
 //    in LDS: half the bytes of a bf16 tile, and no widening anywhere.
 //
-// Layout of the work (gfx950 specific, not from the pages):
+// Layout of the work (gfx950 specific, not from the pages; the rates below
+// were measured with probe kernels):
 //  * One workgroup = (row, 64 heads, split), 4 wavefronts, one per SIMD, one
-//    workgroup per CU. Wave w owns heads 16w..16w+15 for the whole walk: it
-//    scores all 128 slots of a tile for its heads, keeps its own softmax
-//    state and accumulates O for all 512 columns. The waves share only the
-//    LDS tile, so nothing is exchanged between them.
-//  * Tiles of 128 slots are gathered by LDS DMA (buffer_load ... lds)
-//    straight from the pool into LDS, double buffered: a structured buffer
-//    of stride = the pool's row pitch turns each slot index into a row, and
-//    a negative index falls outside its records and reads zeros. One
-//    barrier per tile publishes the next tile and frees the last one.
-//  * Tile row p of LDS holds slot 32(p/32) + 16(p%2) + (p%32)/2, chosen so
-//    that a wave's DMA reads 16 consecutive indices per lane and the eight
-//    rows of each transposed byte read (ds_read_b64_tr_b8) are adjacent. The
-//    16-byte chunk c of row p sits at c ^ (p & 15), which keeps the key reads
-//    (16 rows, stride 2) and the value reads (16 adjacent rows) free of bank
-//    conflicts on gfx950, where a ds_read_b128 serves in one cycle the 16
-//    lanes with equal lane bit 5 and equal parity of lane bits 2..4
-//    (measured). The 64 rope bytes of a 576-wide row go to a separate region,
-//    row = slot, chunk c at c ^ ((row >> 2) & 2).
-//  * S^T = K Q^T leaves lane (head l16, group g) slots 16j + 4g + i of
-//    block j; P^T is packed in exactly that lane (byte 8m + t of the PV B
-//    operand = slot 32m + 16(t & 1) + 4g + t/2), and the value fragment's
-//    transposed reads deliver the matching slot order, so P never moves.
-//  * The rope columns run as one MFMA per block whose 128-deep k holds the
-//    64 rope columns twice: once against q's hi term, once against its lo
-//    term, the two halves scaled by their own E8M0 block scales.
-//  * Online softmax in the exp2 domain with a lazy reference: a wave keeps
-//    its head's reference m while every weight stays below 2^8; when a tile
-//    would exceed it (or at the first tile with a valid slot) the wave takes
-//    the tile's maximum, rescales O and its sums, and recomputes the tile's
-//    weights. Exact in real arithmetic.
+//    workgroup per CU. Wave (hp, kh) holds q of heads 32hp..32hp+31: it
+//    scores slot half kh of each 64-slot tile (S^T = K Q^T, one 32x32 block)
+//    and accumulates O^T for column half kh over all 64 slots; the two waves
+//    of a head half swap their P through LDS (2 KB each way per tile).
+//  * The 32x32x64 dot is chosen over the 16x16x128 one because a wave's own
+//    vector work only issues in the part of a dot that follows its operand
+//    reads (about 16 cycles): a 64-cycle 32x32x64 dot leaves room for about
+//    eight vector instructions, a 32-cycle 16x16x128 dot for about three,
+//    and the softmax and the P split need about six per dot.
+//  * Tiles of 64 slots are gathered by LDS DMA (buffer_load ... lds)
+//    straight from the pool into LDS: a structured buffer of stride = the
+//    pool's row pitch turns each slot index into a row, and a negative index
+//    falls outside its records and reads zeros. The indices come the same
+//    way, a tile's 64 in one instruction. The DMA is issued as inline
+//    assembly: the compiler, which cannot tell which LDS bytes a DMA writes,
+//    would otherwise wait for every DMA in flight before the next LDS access
+//    of any kind; every wait on them is the explicit one at the tile
+//    barrier. A ring of four tiles: while
+//    a wave scores tile t + 1 and weighs tile t (one phase), then multiplies
+//    tile t's values (the next), tile t + 2 is landing and tile t + 3 is
+//    being requested. One barrier per tile publishes P and the next tile.
+//  * Within each 16-row group, tile row 2k + e holds slot 8e + k, so that a
+//    wave's DMA reads 8 consecutive indices per lane and each transposed
+//    byte read of the values (ds_read_b64_tr_b8) covers 8 adjacent rows. The
+//    16-byte chunk c of row p sits at c ^ (2 (p & 7) + ((p >> 3) & 1)), which
+//    keeps the key reads (ds_read_b128: one cycle serves the 16 lanes with
+//    equal lane bit 5 and equal parity of lane bits 2..4) and the value reads
+//    (a 32-lane half per cycle) free of bank conflicts. The 64 rope bytes of
+//    a 576-wide row go to a separate three-tile ring, chunk c at
+//    c ^ ((p >> 2) & 3).
+//  * S^T leaves lane (head c, half h) the 16 slots 8(i/4) + 4h + i%4 of its
+//    block; byte i of the P^T operand's half b is exactly S^T register i of
+//    wave (hp, b), and the transposed value reads deliver the same slot
+//    order, so P is never permuted, only copied to the partner.
+//  * Online softmax in the exp2 domain with two integer references per
+//    head: m_o for O and the row sums (shared by the wave pair, fixed at the
+//    pair's first tile with a valid slot), and m_w for each wave's weights,
+//    raised when a weight would pass 2^8. Each half's P enters the PV dot
+//    through its own E8M0 block scale 2^(m_w - m_o), so O is never rescaled;
+//    if a gap passes 2^64, the workgroup walks again from the final
+//    references. Exact in real arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,32 +83,54 @@ namespace smla {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kMWaves = 4;
-constexpr int kMTile = 128;       // slots per tile
-constexpr int kMRow = 512;        // LDS bytes per tile row of the first 512 columns
-constexpr int kMRope = 64;        // LDS bytes per tile row of the rope columns
-constexpr int kMWord3 = 0x00020000;
-constexpr int kE8One = 127;       // E8M0 code of 1
-constexpr float kMLimit = 8.0f;   // weights stay below 2^kMLimit
-// Largest gap (log2) between the weights' reference and O's: P enters O
-// scaled by 2^gap, and 2^20 slots x 2^8 x 448 x 2^64 stays far below fp32's
-// range.
-constexpr float kMMaxDrift = 64.0f;
+constexpr int kXWaves = 4;
+constexpr int kXTile = 64;     // slots per tile
+constexpr int kXRing = 4;      // tiles held in LDS (first 512 columns)
+constexpr int kXRopeRing = 3;  // tiles held in LDS (rope columns)
+constexpr int kXRow = 512;     // LDS bytes per tile row of the first 512 columns
+constexpr int kXRope = 64;     // LDS bytes per tile row of the rope columns
+constexpr int kXWord3 = 0x00020000;
+constexpr int kE8One = 127;      // E8M0 code of 1
+constexpr float kXLimit = 8.0f;  // weights stay below 2^kXLimit
+// Largest gap (log2) between a weights' reference and O's: P enters O scaled
+// by 2^gap, and 2^20 slots x 2^8 x 448 x 2^64 stays far below fp32's range.
+constexpr float kXMaxDrift = 64.0f;
+// Smallest gap applied (weights further below O's reference are below fp32's
+// resolution of the sums); keeps the lo term's scale code 123 + gap >= 0.
+constexpr float kXMinDrift = -123.0f;
 
 template <int DQK>
-struct MCfg {
+struct XCfg {
   static constexpr bool ROPE = DQK == 576;
-  static constexpr int NOPE = kMTile * kMRow;  // 64 KB
-  static constexpr int BUF = NOPE + (ROPE ? kMTile * kMRope : 0);
-  static constexpr int LDS = 2 * BUF + 2 * kMTile * 4 + 64 * 4;
+  static constexpr int NSTEP = ROPE ? 9 : 8;  // 64-deep k-steps of a score block
+  static constexpr int NOPE = kXTile * kXRow;
+  static constexpr int ROPEB = kXTile * kXRope;
+  static constexpr int XPB = kXWaves * 64 * 32;  // P exchange of one tile
+  static constexpr int OFF_ROPE = kXRing * NOPE;
+  static constexpr int OFF_XP = OFF_ROPE + (ROPE ? kXRopeRing * ROPEB : 0);  // [2][XPB]
+  static constexpr int OFF_XM = OFF_XP + 2 * XPB;                   // [2][4 waves][32] f32
+  static constexpr int OFF_BIAS = OFF_XM + 2 * kXWaves * 32 * 4;    // [ring][64] f32
+  static constexpr int OFF_XL = OFF_BIAS + kXRing * kXTile * 4;     // [4 waves][32] f32
+  static constexpr int OFF_IDX = OFF_XL + kXWaves * 32 * 4;         // [ring][64] i32
+  static constexpr int OFF_EPI = OFF_IDX + kXRing * kXTile * 4;     // 64 f32
+  static constexpr int LDS = OFF_EPI + 64 * 4;
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// Chunk permutation of tile row p (nope region).
-__device__ __forceinline__ int row_perm(int p) { return p & 15; }
+// Tile row of slot s (within each group of 16 rows, row 2k + e holds slot
+// 8e + k).
+__device__ __forceinline__ int row_of_slot(int s) {
+  return (s & ~15) | ((s & 7) << 1) | ((s >> 3) & 1);
+}
+// Chunk permutations: chunk c of tile row p sits at c ^ perm(p).
+__device__ __forceinline__ int nope_perm(int p) { return ((p & 7) << 1) | ((p >> 3) & 1); }
+__device__ __forceinline__ int rope_perm(int p) { return (p >> 2) & 3; }
 
 // Two fp32 values to two e4m3fn codes in half HI of `old` (round to
 // nearest even; callers keep |v| <= 256, so nothing saturates).
@@ -107,62 +141,98 @@ __device__ __forceinline__ s16x2 cvt2(s16x2 old, float a, float b, float scale =
   return __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, a, b, scale, HI);
 }
 
-// Four fp32 values (a0, a1, b0, b1 -> bytes 0..3) to their hi and lo e4m3
-// terms: v = hi + lo / 16 up to lo's rounding.
-__device__ __forceinline__ void split4(float a0, float a1, float b0, float b1, uint32_t& hi,
+// Four fp32 values (bytes 0..3 in order) to their hi and lo e4m3 terms:
+// v = hi + lo / 16 up to lo's rounding.
+__device__ __forceinline__ void split4(float a0, float a1, float a2, float a3, uint32_t& hi,
                                        uint32_t& lo) {
   s16x2 h = cvt2<false>(s16x2{0, 0}, a0, a1);
-  h = cvt2<true>(h, b0, b1);
+  h = cvt2<true>(h, a2, a3);
   const uint32_t hw = __builtin_bit_cast(uint32_t, h);
   const auto ha = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, 1.0f, false);
   const auto hb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, 1.0f, true);
   s16x2 l = cvt2<false>(s16x2{0, 0}, a0 - ha[0], a1 - ha[1], 0.0625f);
-  l = cvt2<true>(l, b0 - hb[0], b1 - hb[1], 0.0625f);
+  l = cvt2<true>(l, a2 - hb[0], a3 - hb[1], 0.0625f);
   hi = hw;
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
-// D += A B on the fp8 matrix cores; A's block scale 1, B's 2^(sb - 127).
-__device__ __forceinline__ floatx4 mx(const i32x8& a, const i32x8& b, floatx4 c, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kE8One, 0, sb);
+// Buffer resource of `records` records of `stride` bytes at base (stride 0:
+// a raw buffer of `records` bytes); word 3 as the loads here need it.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t stride, uint32_t records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{int(uint32_t(a)), int((uint32_t(a >> 32) & 0xFFFFu) | (stride << 16)), int(records),
+               kXWord3};
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((lds_void*)p));
+}
+
+// LDS DMA, 16 bytes per lane: record `index` (out of range: zeros), byte
+// `voff`, to LDS at lds + 16 lane. lds must be wave-uniform. No vector
+// register is written, so nothing in flight can be overwritten; completion
+// is waited for explicitly (sync_tile).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here and read by the same statement
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds, int index, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 idxen offen lds"
+               :: "s"(lds), "v"(i32x2{index, int(voff)}), "s"(rsrc) : "memory", "m0");
+}
+
+// LDS DMA, 4 bytes per lane from byte voff of a raw buffer (out of range:
+// zero) to LDS at lds + 4 lane.
+__device__ __forceinline__ void dma4(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// D += A B on the fp8 matrix cores; A's block scale 1, B's 2^(sb - 127)
+// (lane j gives the scale of column j % 32, k-block j / 32).
+__device__ __forceinline__ floatx16 mx32(const i32x8& a, const i32x8& b, floatx16 c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8One, 0, sb);
 }
 
 __device__ __forceinline__ i32x8 cat(const u32x4& a, const u32x4& b) {
   return i32x8{int(a.x), int(a.y), int(a.z), int(a.w), int(b.x), int(b.y), int(b.z), int(b.w)};
 }
 
-// Every wave's LDS DMA and LDS writes are complete and visible, and every
-// wave is past its reads of the buffer being refilled next. The memory
-// clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void sync_tile() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ i32x8 pack8(const uint32_t (&w)[8]) {
+  return i32x8{int(w[0]), int(w[1]), int(w[2]), int(w[3]), int(w[4]), int(w[5]), int(w[6]), int(w[7])};
 }
 
-// 16 scaled values to 16 hi codes (dwords 0..3) and 16 lo codes.
-__device__ __forceinline__ void split16(const float (&v)[16], float sc, uint32_t (&hi)[4],
-                                        uint32_t (&lo)[4]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    split4(v[4 * k] * sc, v[4 * k + 1] * sc, v[4 * k + 2] * sc, v[4 * k + 3] * sc, hi[k], lo[k]);
+// Every wave's LDS DMA and LDS writes are complete and visible, and every
+// wave is past its reads before the barrier. The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void sync_tile() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // the same wait, visible to the compiler (no cost: the counters are zero),
+  // so that it adds none of its own for loads issued before this point
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // PAGED: slot indices of a paged pool are mapped to rows (a separate
 // instance, so the plain pool's walk carries none of it).
 template <int DQK, bool EPI, bool PAGED>
-__global__ void __launch_bounds__(kMWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kXWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 prefill_mx_kernel(const FwdParams p) {
-  using C = MCfg<DQK>;
+  using C = XCfg<DQK>;
   constexpr bool ROPE = C::ROPE;
-  constexpr int BUF = C::BUF, NOPE = C::NOPE;
+  constexpr int NSTEP = C::NSTEP;
+  constexpr int NNOPE = 8;  // k-steps over the first 512 columns
 
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2 * BUF];
-  __shared__ __attribute__((aligned(16))) float kbias[2 * kMTile];  // 0 (valid slot) or -inf
-  __shared__ float epi_cs[64];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+  float* const kbias = reinterpret_cast<float*>(smem + C::OFF_BIAS);  // 0 (valid) or -inf
+  float* const xm = reinterpret_cast<float*>(smem + C::OFF_XM);
+  float* const xl = reinterpret_cast<float*>(smem + C::OFF_XL);
+  float* const epi_cs = reinterpret_cast<float*>(smem + C::OFF_EPI);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar offsets
-  const int l16 = lane & 15, g = lane >> 4, hh = lane >> 5;
+  const int hp = wave >> 1, kh = wave & 1;
+  const int c32 = lane & 31, h = lane >> 5;
 
   int64_t work = p.remap ? smla_xcd_work(blockIdx.x, p.grid) : int64_t(blockIdx.x);
   const int hblk = int(work % p.head_blocks);
@@ -174,57 +244,54 @@ prefill_mx_kernel(const FwdParams p) {
     if (p.epi.pos != nullptr && tid < 64) cs_pre = epi_cs_row(p.epi, r)[tid];
   }
 
-  const int head = hblk * 64 + 16 * wave + l16;
+  const int head = hblk * 64 + 32 * hp + c32;
   const bool head_ok = head < p.heads;
-  const int ntiles = (p.topk + kMTile - 1) / kMTile;
+  const int ntiles = (p.topk + kXTile - 1) / kXTile;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(ntiles, t_begin + p.tiles_per_split);
-  const int slot_end = min(p.topk, t_end * kMTile);
+  const int slot_end = min(p.topk, t_end * kXTile);
 
   // ---- index rows and the tile DMA
-  const __amdgpu_buffer_rsrc_t idx_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(p.idx + r * p.idx_rs), 0, 4 * slot_end, kMWord3);
+  const i32x4 idx_rsrc = make_rsrc(p.idx + r * p.idx_rs, 0, 4u * uint32_t(slot_end));
   const uint32_t rs = uint32_t(p.pool_rs_bytes);
   const uint32_t records = p.pool_bytes >= uint32_t(DQK) ? (p.pool_bytes - DQK) / rs + 1 : 0u;
-  const __amdgpu_buffer_rsrc_t pool_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.pool), int16_t(rs), int(records), kMWord3);
+  const i32x4 pool_rsrc = make_rsrc(p.pool, rs, records);
   const uint32_t page_rows = PAGED ? uint32_t(p.page_bytes / p.pool_rs_bytes) : 0u;
+  const uint32_t lds0 = lds_addr(smem);
+  const int32_t* const idx_ring = reinterpret_cast<const int32_t*>(smem + C::OFF_IDX);
 
-  // This lane's slots of a tile (relative to t * 128 + 32 * wave): the DMA
-  // rows 16 hh + k (k < 16), the rope rows 16 k' + lane / 4, the bias slot
-  // lane % 32.
-  int idn[16], idr[2], idb;
-  // The whole offset goes in the vector operand, which the range check
-  // covers (reads past slot_end return 0).
-  auto load_idx = [&](int t) {
-    const uint32_t base = uint32_t(4 * (t * kMTile + 32 * wave));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 v = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(idx_rsrc, base + uint32_t(4 * (16 * hh + 4 * q)), 0, 0));
-#pragma unroll
-      for (int k = 0; k < 4; ++k) idn[4 * q + k] = int(v[k]);
-    }
-    if constexpr (ROPE) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        idr[k] = __builtin_amdgcn_raw_buffer_load_b32(idx_rsrc, base + uint32_t(4 * (16 * k + (lane >> 2))), 0, 0);
-    }
-    idb = __builtin_amdgcn_raw_buffer_load_b32(idx_rsrc, base + uint32_t(4 * (lane & 31)), 0, 0);
+  // The indices of tile t (64 of them; past slot_end the range check reads
+  // 0) to the index ring; one instruction, issued by wave 0.
+  auto idx_dma = [&](int tt, int t) {
+    if (wave == 0)
+      dma4(idx_rsrc, lds0 + C::OFF_IDX + (tt % kXRing) * kXTile * 4, uint32_t(4 * (t * kXTile + lane)));
   };
-  // Slots past the split's end read 0 through the index range: mark them
-  // invalid; then map slot indices of a paged pool to rows of page_rows.
-  auto fix_idx = [&](int t) {
-    const int base = t * kMTile + 32 * wave;
-    if (base + 32 > slot_end) {
+  // This lane's slots of a tile (relative to 16 * wave): the DMA slots
+  // 8h + k (k < 8; rows 2k + h), the rope slot of rope row lane / 4, the
+  // flag slot lane % 16.
+  const int rope_slot = 8 * ((lane >> 2) & 1) + ((lane >> 3) & 7);
+  int idn[8], idr = -1, idb;
+  // The lane's indices of tile t (ring place tt) from the ring; slots past
+  // the split's end read 0 there: mark them invalid; then map slot indices
+  // of a paged pool to rows of page_rows.
+  auto read_idx = [&](int tt, int t) {
+    const int32_t* ir = idx_ring + (tt % kXRing) * kXTile + 16 * wave;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(ir + 8 * h);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(ir + 8 * h + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      idn[k] = int(a[k]);
+      idn[4 + k] = int(b[k]);
+    }
+    if constexpr (ROPE) idr = ir[rope_slot];
+    idb = ir[lane & 15];
+    const int base = t * kXTile + 16 * wave;
+    if (base + 16 > slot_end) {
       asm volatile("" ::: "memory");  // a branch, not selects on every tile
 #pragma unroll
-      for (int k = 0; k < 16; ++k) idn[k] = base + 16 * hh + k < slot_end ? idn[k] : -1;
-      if constexpr (ROPE) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) idr[k] = base + 16 * k + (lane >> 2) < slot_end ? idr[k] : -1;
-      }
-      idb = base + (lane & 31) < slot_end ? idb : -1;
+      for (int k = 0; k < 8; ++k) idn[k] = base + 8 * h + k < slot_end ? idn[k] : -1;
+      if constexpr (ROPE) idr = base + rope_slot < slot_end ? idr : -1;
+      idb = base + (lane & 15) < slot_end ? idb : -1;
     }
     if constexpr (PAGED) {
       auto map = [&](int i) -> int {
@@ -232,436 +299,501 @@ prefill_mx_kernel(const FwdParams p) {
                      : int((uint32_t(i) >> p.page_shift) * page_rows + (uint32_t(i) & p.page_mask));
       };
 #pragma unroll
-      for (int k = 0; k < 16; ++k) idn[k] = map(idn[k]);
-      if constexpr (ROPE) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) idr[k] = map(idr[k]);
-      }
+      for (int k = 0; k < 8; ++k) idn[k] = map(idn[k]);
+      if constexpr (ROPE) idr = map(idr);
     }
   };
-  // DMA of tile t into buffer b (indices loaded and fixed), and its slot
-  // validity into kbias.
-  const uint32_t dma_vb = (16u * uint32_t(lane & 31)) ^ (16u * uint32_t(hh));
-  const uint32_t dma_rope = 512u + 16u * uint32_t((lane & 3) ^ ((lane >> 4) & 2));
-  auto issue_dma = [&](int b) {
-    uint8_t* buf = tiles + b * BUF;
+  // DMA of the walk's tile tt (indices read) into its ring places, and its
+  // slot flags.
+  const uint32_t dma_rope = 512u + 16u * uint32_t((lane & 3) ^ ((lane >> 4) & 3));
+  auto issue_dma = [&](int tt) {
+    const uint32_t nb = lds0 + (tt % kXRing) * C::NOPE + 16 * wave * kXRow;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t voff = dma_vb ^ uint32_t(32 * (k & 7));
-      __builtin_amdgcn_struct_ptr_buffer_load_lds(
-          pool_rsrc, (lds_void*)(buf + (32 * wave + 2 * k) * kMRow), 16, idn[k], int(voff), 0, 0, 0);
-    }
-    if constexpr (ROPE) {
+    for (int k = 0; k < 8; ++k)
+      dma16(pool_rsrc, nb + 2 * k * kXRow, idn[k], 16u * uint32_t((lane & 31) ^ nope_perm(2 * k + h)));
+    if constexpr (ROPE)
+      dma16(pool_rsrc, lds0 + C::OFF_ROPE + (tt % kXRopeRing) * C::ROPEB + 16 * wave * kXRope, idr,
+            dma_rope);
+    if (lane < 16) kbias[(tt % kXRing) * kXTile + 16 * wave + lane] = idb >= 0 ? 0.f : kNegInf;
+  };
+  // A walk's start: the indices of its first four tiles, then (indices
+  // landed) the DMAs of the first three. `between` runs after the barrier
+  // that lands the indices, before the DMAs.
+  auto start_walk = [&](int nt, auto&& between) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-        __builtin_amdgcn_struct_ptr_buffer_load_lds(
-            pool_rsrc, (lds_void*)(buf + NOPE + (32 * wave + 16 * k) * kMRope), 16, idr[k],
-            int(dma_rope), 0, 0, 0);
+    for (int tt = 0; tt < 4; ++tt)
+      if (tt < nt) idx_dma(tt, t_begin + tt);
+    sync_tile();
+    between();
+#pragma unroll
+    for (int tt = 0; tt < 3; ++tt) {
+      if (tt < nt) {
+        read_idx(tt, t_begin + tt);
+        issue_dma(tt);  // waits for the read: ring place tt may be refilled after this
+      }
     }
-    if (lane < 32) kbias[b * kMTile + 32 * wave + lane] = idb >= 0 ? 0.f : kNegInf;
+    if (nt > 4) idx_dma(4, t_begin + 4);
   };
 
-  // q of this lane's head (computed once, while the first tile's DMA runs):
-  // k-step s takes columns 128s + 16g and 128s + 64 + 16g (16 each); the
-  // rope part columns 512 + 16g.
-  i32x8 qhi[4], qlo[4], qrope;
-  int sb_hi = 0, sb_lo = 0, sb_rope = 0;
-  auto make_q = [&]() {
-    // Every load is issued before any is used (one dtype branch, the
-    // address of a masked head clamped into q): a branch per load would make
-    // the compiler wait for each in turn.
-    constexpr int NCH = ROPE ? 9 : 8;  // 16-column chunks: (s, h) = chunk 2s + h, then rope
-    const int hq = head_ok ? head : p.heads - 1;
-    const int64_t qp = r * p.q_rs + int64_t(hq) * p.q_hs;
-    auto col_of = [&](int c) { return c < 8 ? 128 * (c >> 1) + 64 * (c & 1) + 16 * g : 512 + 16 * g; };
-    float v[NCH][16];
-    if (p.q_fp8) {
-      u32x4 raw[NCH];
+  // q of this lane's head: k-step st takes columns 64 st + 16h and
+  // 64 st + 32 + 16h (16 each), split into hi and lo e4m3 terms under the
+  // head's power of two (2^e puts its largest |q| in [128, 256)). The loads
+  // are issued before the walk's first barrier and all consumed (the
+  // largest magnitude) right after it, before any DMA is in flight, so the
+  // compiler's waits for them wait for nothing else.
+  i32x8 qhi[NSTEP], qlo[NSTEP];
+  int sb_hi = kE8One, sb_lo = kE8One;
+  const int hq = head_ok ? head : p.heads - 1;  // a masked head reads a real one, scaled by 0
+  const int64_t qp = r * p.q_rs + int64_t(hq) * p.q_hs;
+  auto q_col = [&](int st, int d) { return 64 * st + 32 * d + 16 * h; };
+  auto q_exponent = [&](float amax) {
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int e = 8 - __builtin_amdgcn_frexp_expf(amax);
+    return amax > 0.f && head_ok ? min(max(e, -100), 100) : 0;
+  };
+  // q given as 8 bf16 bit patterns per u32x4 pair: (hi, lo) terms of k-step st
+  auto split_q = [&](int st, const u32x4 (&raw)[2][2], float sc) {
+    uint32_t hw[8], lw[8];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        raw[c] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + qp + col_of(c));
+    for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const u32x2 w = widen_fp8x4(raw[c][k]);
-          v[c][4 * k] = __uint_as_float(w.x << 16);
-          v[c][4 * k + 1] = __uint_as_float(w.x & 0xFFFF0000u);
-          v[c][4 * k + 2] = __uint_as_float(w.y << 16);
-          v[c][4 * k + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t w0 = raw[d][hf][2 * k], w1 = raw[d][hf][2 * k + 1];
+          split4(__uint_as_float(w0 << 16) * sc, __uint_as_float(w0 & 0xFFFF0000u) * sc,
+                 __uint_as_float(w1 << 16) * sc, __uint_as_float(w1 & 0xFFFF0000u) * sc,
+                 hw[4 * d + 2 * hf + k], lw[4 * d + 2 * hf + k]);
         }
-    } else {
-      u32x4 raw[NCH][2];
+    qhi[st] = pack8(hw);
+    qlo[st] = pack8(lw);
+  };
+  auto start_first_walk = [&](int nt) {
+    if (p.q_fp8) {
+      u32x4 raw[NSTEP][2];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
+      for (int st = 0; st < NSTEP; ++st)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          raw[c][h] = *reinterpret_cast<const u32x4*>(p.q + qp + col_of(c) + 8 * h);
+        for (int d = 0; d < 2; ++d)
+          raw[st][d] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + qp +
+                                                       q_col(st, d));
+      float sc = 0.f;
+      start_walk(nt, [&]() {
+        float amax = 0.f;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
+        for (int st = 0; st < NSTEP; ++st)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+          for (int d = 0; d < 2; ++d)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[c][8 * h + 2 * k] = __uint_as_float(raw[c][h][k] << 16);
-            v[c][8 * h + 2 * k + 1] = __uint_as_float(raw[c][h][k] & 0xFFFF0000u);
-          }
-    }
-    float amax = 0.f;
+            for (int k = 0; k < 4; ++k) {
+              const u32x2 w = widen_fp8x4(raw[st][d][k]);
+              amax = fmaxf(amax, fmaxf(fmaxf(fabsf(__uint_as_float(w.x << 16)),
+                                             fabsf(__uint_as_float(w.x & 0xFFFF0000u))),
+                                       fmaxf(fabsf(__uint_as_float(w.y << 16)),
+                                             fabsf(__uint_as_float(w.y & 0xFFFF0000u)))));
+            }
+        const int e = q_exponent(amax);
+        sc = head_ok ? __builtin_ldexpf(1.0f, e) : 0.f;
+        sb_hi = kE8One - e;
+        sb_lo = kE8One - e - 4;
+      });
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
+      for (int st = 0; st < NSTEP; ++st) {
+        u32x4 bf[2][2];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        v[c][k] = head_ok ? v[c][k] : 0.f;
-        amax = fmaxf(amax, fabsf(v[c][k]));
+        for (int d = 0; d < 2; ++d) {
+          const u32x2 a = widen_fp8x4(raw[st][d][0]), b = widen_fp8x4(raw[st][d][1]);
+          const u32x2 c = widen_fp8x4(raw[st][d][2]), e = widen_fp8x4(raw[st][d][3]);
+          bf[d][0] = u32x4{a.x, a.y, b.x, b.y};
+          bf[d][1] = u32x4{c.x, c.y, e.x, e.y};
+        }
+        split_q(st, bf, sc);
       }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-    // 2^e puts the wave's largest |q| in [128, 256)
-    int e = 8 - __builtin_amdgcn_frexp_expf(amax);
-    e = amax > 0.f ? min(max(e, -100), 100) : 0;
-    const float sc = __builtin_ldexpf(1.0f, e);
-    sb_hi = kE8One - e;
-    sb_lo = kE8One - e - 4;
-    sb_rope = hh == 0 ? sb_hi : sb_lo;  // k blocks 0,1: hi term; 2,3: lo term
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint32_t ha[4], la[4], hb[4], lb[4];
-      split16(v[2 * s], sc, ha, la);
-      split16(v[2 * s + 1], sc, hb, lb);
-      qhi[s] = i32x8{int(ha[0]), int(ha[1]), int(ha[2]), int(ha[3]),
-                     int(hb[0]), int(hb[1]), int(hb[2]), int(hb[3])};
-      qlo[s] = i32x8{int(la[0]), int(la[1]), int(la[2]), int(la[3]),
-                     int(lb[0]), int(lb[1]), int(lb[2]), int(lb[3])};
-    }
-    if constexpr (ROPE) {
-      uint32_t h4[4], l4[4];
-      split16(v[8], sc, h4, l4);
-      qrope = i32x8{int(h4[0]), int(h4[1]), int(h4[2]), int(h4[3]),
-                    int(l4[0]), int(l4[1]), int(l4[2]), int(l4[3])};
     } else {
-      qrope = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      u32x4 raw[NSTEP][2][2];
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            raw[st][d][hf] = *reinterpret_cast<const u32x4*>(p.q + qp + q_col(st, d) + 8 * hf);
+      float sc = 0.f;
+      start_walk(nt, [&]() {
+        float amax = 0.f;
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+          for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[st][d][hf][k] << 16)),
+                                         fabsf(__uint_as_float(raw[st][d][hf][k] & 0xFFFF0000u))));
+        const int e = q_exponent(amax);
+        sc = head_ok ? __builtin_ldexpf(1.0f, e) : 0.f;
+        sb_hi = kE8One - e;
+        sb_lo = kE8One - e - 4;
+      });
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) split_q(st, raw[st], sc);
     }
   };
   const float kv_scale = *p.kv_scale;
   const float cscale = p.sm_log2 * q_scale_of(p.q_scale) * kv_scale;
 
-  // ---- per-lane LDS addresses (without the buffer base)
-  // keys: block j reads tile row 32(j/2) + 2 l16 + (j & 1); its chunks are
-  // permuted by row_perm of that row, which depends on l16 and j & 1 only.
-  int kro[2], kperm[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    kro[par] = (2 * l16 + par) * kMRow;
-    kperm[par] = row_perm(2 * l16 + par);
-  }
-  // values: read m of a 16-column block covers tile rows 32m + 8g .. +7; the
-  // lane pair (2t, 2t+1) of a group points at row 32m + 8g + t.
-  const int vrow = 8 * g + (l16 >> 1);
-  const int vro = vrow * kMRow + 8 * (l16 & 1);
-  const int vperm16 = 16 * row_perm(vrow);
-  // rope: block j reads rope row 16j + l16, chunk g permuted by its row.
-  const int rro = NOPE + l16 * kMRope + 16 * (g ^ ((l16 >> 2) & 2));
+  // ---- per-lane LDS offsets (without the tile's base)
+  // keys: this lane's score row is slot 32kh + c32; k-step st, half d reads
+  // chunk 4st + 2d + h of its tile row (the rope k-step: rope chunk 2d + h).
+  const int krow = row_of_slot(32 * kh + c32);
+  const int kperm = nope_perm(krow);
+  const int kro = krow * kXRow;
+  const int rro = krow * kXRope;
+  const int rperm = rope_perm(krow);
+  // values: read v (0..3) of column block m covers tile rows
+  // 32(v/2) + 16(v%2) + 8h .. +7; the lane pair (2t, 2t+1) of a 16-lane group
+  // points at row 8h + 2(t & 3) + t/2 of that group of 16, bytes 8(lane & 1)
+  // of chunk 16kh + 2m + (lane bit 4).
+  const int vt = (lane & 15) >> 1;
+  const int vplow = 8 * h + 2 * (vt & 3) + (vt >> 2);
+  const int vperm = nope_perm(vplow);
+  const int vro = vplow * kXRow + 256 * kh + 8 * (lane & 1);
+  const int ve = (lane >> 4) & 1;
 
-  floatx4 o[32];
+  floatx16 o[8];
   float m_o = kNegInf;  // reference (log2 domain, an integer) of O and the row sums
-  float m_w = kNegInf;  // reference of the weights, m_w >= m_o
-  float l_run = 0.f;    // this lane's share of the head's row sum (reference m_o)
+  float m_w = kNegInf;  // reference of this wave's weights
+  float l_run = 0.f;    // this lane's share of its slots' row sum (reference m_o)
   int redo = 0;
+
+  // Key fragment (k-step st, half d) of the walk's tile tt: chunk 4st + 2d + h
+  // of this lane's tile row (the rope k-step: rope chunk 2d + h).
+  int kro_i = kro, kperm_i = kperm, rro_i = rro, rperm_i = rperm;  // refreshed per tile
+  auto kread = [&](int tt, int st, int d) -> u32x4 {
+    if (ROPE && st == NNOPE)
+      return *reinterpret_cast<const u32x4*>(smem + C::OFF_ROPE + (tt % kXRopeRing) * C::ROPEB +
+                                             rro_i + 16 * ((2 * d + h) ^ rperm_i));
+    return *reinterpret_cast<const u32x4*>(smem + (tt % kXRing) * C::NOPE + kro_i +
+                                           16 * ((4 * st + 2 * d + h) ^ kperm_i));
+  };
+  // One k-step of S^T: both terms of q against one key fragment.
+  auto kstep = [&](floatx16& s, int st, const u32x4 (&kf)[2]) {
+    const i32x8 a = cat(kf[0], kf[1]);
+    s = mx32(a, qhi[st], s, sb_hi);
+    s = mx32(a, qlo[st], s, sb_lo);
+  };
+  // Slot flags (0 or -inf) of this lane's 16 slots of the walk's tile tt.
+  auto read_bias = [&](int tt, floatx4 (&b)[4]) {
+    const float* kb = kbias + (tt % kXRing) * kXTile + 32 * kh + 4 * h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const floatx4*>(kb + 8 * j);
+  };
+  // Per-iteration copies of the lane's LDS offsets: recomputing what is
+  // derived from them is cheaper than holding it across the iteration.
+  auto fresh = [](int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
 
   // One walk over the split's tiles. The first walk fixes the references as
   // it goes; a second one (only when a score jumped by more than
-  // kMMaxDrift above the first valid tile's maximum) starts from the first
-  // walk's last weight reference, which no later score exceeds by 2^kMLimit.
+  // kXMaxDrift above the pair's first valid tile's maximum) starts from the
+  // first walk's final references, which no later score exceeds by
+  // 2^kXLimit.
   auto walk = [&](bool first) {
 #pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 8; ++c) o[c] = floatx16{};
     l_run = 0.f;
-    if (!first) m_o = m_w;
-    float nm = m_o == kNegInf ? 0.f : -m_w;
-    const int t0 = t_begin;
-    if (t0 < t_end) {
-      load_idx(t0);
-      fix_idx(t0);
-      issue_dma(0);
-    }
-    if (t0 + 1 < t_end) load_idx(t0 + 1);
-    if (first) make_q();
-    sync_tile();  // tile t0 and its flags visible
-    if (t0 + 1 < t_end) {
-      fix_idx(t0 + 1);
-      issue_dma(1);
-    }
-    if (t0 + 2 < t_end) load_idx(t0 + 2);
-    for (int t = t0; t < t_end; ++t) {
-      const int b = (t - t0) & 1;
-      const uint8_t* B = tiles + b * BUF;
-      const float* kb = kbias + b * kMTile + 4 * g;
+    const int nt = t_end - t_begin;
+    if (nt <= 0) return;
+    // start: the first tiles requested (and, on the first walk, q split
+    // while they land)
+    if (first)
+      start_first_walk(nt);
+    else
+      start_walk(nt, [&]() {});
+    sync_tile();
 
-      // ---- S^T = K Q^T over pairs of blocks (2m, 2m + 1): per pair, one
-      // unit per k-step (unit 4: the rope) of four dots (two for the rope),
-      // the two blocks' dots alternating. With one wavefront per SIMD the
-      // wave issues in order and an MFMA only runs alongside what the wave
-      // issues before the next one, so every dot is followed by its share of
-      // the other work: a quarter of the key fragment reads for two units
-      // ahead, and one of the previous pair's ten softmax jobs (eight
-      // weights, two splits into P^T bytes) spread over the pair's dots. The
-      // scheduling fences keep exactly that order.
-      constexpr int UPP = ROPE ? 5 : 4;  // units per pair of blocks
-      constexpr int NU = 4 * UPP;
-      constexpr int MPP = ROPE ? 18 : 16;  // dots per pair
-      constexpr int KR = 3;                // units of key fragments in the ring
-      floatx4 sacc[8];
-      float pprev[4], pcur[4];
-      float xmax = kNegInf, lt = 0.f;
-      uint32_t phi[8], plo[8];
-      // key fragment f (0, 1: block 2pm, 2pm + 1) of unit u, half hf (the
-      // 16 bytes at columns 128s + 16g, then 128s + 64 + 16g; the rope unit
-      // reads its chunk twice)
-      auto kread = [&](int u, int f, int hf) -> u32x4 {
-        const int j = 2 * (u / UPP) + f, sj = u % UPP, par = j & 1;
-        if (ROPE && sj == 4) return *reinterpret_cast<const u32x4*>(B + rro + 16 * j * kMRope);
-        const uint8_t* krow = B + kro[par] + 32 * (j >> 1) * kMRow;
-        return *reinterpret_cast<const u32x4*>(krow + 16 * ((8 * sj + 4 * hf + g) ^ kperm[par]));
-      };
-      // Slot validity (0 or -inf) of block j's four slots of this lane, read
-      // a pair of blocks ahead of its use: a read issued just before its use
-      // would make the wait drain every key fragment read in flight.
-      floatx4 bias_v[8];
-      // weight i of block j
-      auto weight = [&](int j, int i) {
-        const float x = __builtin_fmaf(sacc[j][i], cscale, bias_v[j][i] + nm);
-        xmax = fmaxf(xmax, x);
-        pcur[i] = __builtin_amdgcn_exp2f(x);
-        lt += pcur[i];
-        if (i == 3 && !(j & 1)) {
+    floatx16 s_cur = floatx16{}, s_next;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) pprev[k] = pcur[k];
+    for (int st = 0; st < NSTEP; ++st) {
+      u32x4 kf[2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) kf[d] = kread(0, st, d);
+      kstep(s_cur, st, kf);
+    }
+    float nm = m_w == kNegInf ? 0.f : -m_w;
+    // carried from one step to the next: slot flag - m_w of the next tile's
+    // 16 slots of this lane
+    float bn[4][4];
+    auto make_bn = [&](int tt) {
+      floatx4 b[4];
+      read_bias(tt, b);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bn[i / 4][i % 4] = b[i / 4][i % 4] + nm;
+    };
+    make_bn(0);
+    for (int tt = 0; tt < nt; ++tt) {
+      const int par = tt & 1;
+      const bool has_next = tt + 1 < nt;
+      float xmax, lt;
+      uint32_t phi[4], plo[4];
+      // The tile's weights (exp2 domain) and their split into P^T bytes
+      // (byte i of this half's 16 is weight i), as 20 stages over groups g
+      // of 4 weights: stage 0 the exponents, 1 the powers and the group
+      // maximum, 2 the group sum and the hi codes, 3 the residuals, 4 the lo
+      // codes. A stage depends only on earlier stages of its group.
+      float x[16], w[16], m4[4], l4[4], ra[4][4];
+      uint32_t hw[4];
+      auto stage = [&](int st, int g) {
+        if (st == 0) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[4 * g + u] = __builtin_fmaf(s_cur[4 * g + u], cscale, bn[g][u]);
+        } else if (st == 1) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) w[4 * g + u] = __builtin_amdgcn_exp2f(x[4 * g + u]);
+          m4[g] = fmaxf(fmaxf(x[4 * g], x[4 * g + 1]), fmaxf(x[4 * g + 2], x[4 * g + 3]));
+        } else if (st == 2) {
+          l4[g] = (w[4 * g] + w[4 * g + 1]) + (w[4 * g + 2] + w[4 * g + 3]);
+          s16x2 hc = cvt2<false>(s16x2{0, 0}, w[4 * g], w[4 * g + 1]);
+          hw[g] = __builtin_bit_cast(uint32_t, cvt2<true>(hc, w[4 * g + 2], w[4 * g + 3]));
+        } else if (st == 3) {
+          const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[g], 1.0f, false);
+          const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[g], 1.0f, true);
+          ra[g][0] = w[4 * g] - a[0];
+          ra[g][1] = w[4 * g + 1] - a[1];
+          ra[g][2] = w[4 * g + 2] - b[0];
+          ra[g][3] = w[4 * g + 3] - b[1];
+        } else {
+          s16x2 lc = cvt2<false>(s16x2{0, 0}, ra[g][0], ra[g][1], 0.0625f);
+          plo[g] = __builtin_bit_cast(uint32_t, cvt2<true>(lc, ra[g][2], ra[g][3], 0.0625f));
+          phi[g] = hw[g];
         }
       };
-      // half h of the P^T bytes 8m .. 8m + 7 from the weights of blocks 2m
-      // (pprev) and 2m + 1 (pcur)
-      auto split_half = [&](int m, int h) {
-        split4(pprev[2 * h], pcur[2 * h], pprev[2 * h + 1], pcur[2 * h + 1], phi[2 * m + h],
-               plo[2 * m + h]);
+      auto finish = [&]() {
+        xmax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        lt = (l4[0] + l4[1]) + (l4[2] + l4[3]);
       };
-      // softmax job k (0..9) of pair pm: weights of block 2pm (k < 4), of
-      // block 2pm + 1 (k = 4, 5, 7, 8), splits (k = 6, 9)
-      auto job = [&](int pm, int k) {
-        if (k < 4) weight(2 * pm, k);
-        else if (k == 4 || k == 5) weight(2 * pm + 1, k - 4);
-        else if (k == 6) split_half(pm, 0);
-        else if (k == 7 || k == 8) weight(2 * pm + 1, k - 5);
-        else split_half(pm, 1);
-        // computed here, between the dots: left alone the compiler sinks the
-        // weights below the rare-path branch, after all the dots
-        asm volatile("" : "+v"(pcur[0]), "+v"(pcur[1]), "+v"(pcur[2]), "+v"(pcur[3]), "+v"(lt));
+      // stage instance j (0..19) in dependency order with a gap between
+      // the stages of a group
+      auto stage_of = [](int j, int& st, int& g) {
+        constexpr int kSt[20] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 2, 3, 4, 2, 3, 4, 3, 4, 4};
+        constexpr int kG[20] = {0, 1, 0, 2, 1, 0, 3, 2, 1, 0, 3, 2, 1, 0, 3, 2, 1, 3, 2, 3};
+        st = kSt[j];
+        g = kG[j];
       };
-      {
-        u32x4 kring[KR][2][2];
+      auto softmax = [&]() {
 #pragma unroll
-        for (int u = 0; u < KR - 1; ++u)
+        for (int j = 0; j < 20; ++j) {
+          int st, g;
+          stage_of(j, st, g);
+          stage(st, g);
+        }
+        finish();
+      };
+
+      // ---- S^T of the next tile over all but its last k-step, with this
+      // tile's softmax stages between the dots
+      u32x4 kr[3][2];
+      if (has_next) {
+        s_next = floatx16{};
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) kring[u][f][hf] = kread(u, f, hf);
-        bias_v[0] = *reinterpret_cast<const floatx4*>(kb);
-        bias_v[1] = *reinterpret_cast<const floatx4*>(kb + 16);
+          for (int d = 0; d < 2; ++d) kr[st][d] = kread(tt + 1, st, d);
+        // the first two stages while the fragments arrive
+        {
+          int sst, g;
+          stage_of(0, sst, g);
+          stage(sst, g);
+          stage_of(1, sst, g);
+          stage(sst, g);
+        }
+        constexpr int ND = 2 * (NSTEP - 1);  // dots before the barrier
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int pm = u / UPP, sj = u % UPP, j0 = 2 * pm, j1 = 2 * pm + 1;
-          const bool rope_u = ROPE && sj == 4;
-          const int nmf = rope_u ? 2 : 4;  // dots of this unit
-          const int un = u + KR - 1;       // unit whose fragments this one reads
-          const i32x8 f0 = cat(kring[u % KR][0][0], kring[u % KR][0][1]);
-          const i32x8 f1 = cat(kring[u % KR][1][0], kring[u % KR][1][1]);
-          if (sj == 0) sacc[j0] = sacc[j1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < NSTEP - 1; ++st) {
+          const i32x8 a = cat(kr[st % 3][0], kr[st % 3][1]);
 #pragma unroll
-          for (int mi = 0; mi < nmf; ++mi) {
-            if (rope_u) {
-              if (mi == 0) sacc[j0] = mx(f0, qrope, sacc[j0], sb_rope);
-              else sacc[j1] = mx(f1, qrope, sacc[j1], sb_rope);
-            } else {
-              const int f = mi & 1;
-              const i32x8& kf = f ? f1 : f0;
-              floatx4& acc = f ? sacc[j1] : sacc[j0];
-              acc = mx(kf, mi < 2 ? qhi[sj] : qlo[sj], acc, mi < 2 ? sb_hi : sb_lo);
-            }
+          for (int term = 0; term < 2; ++term) {
+            s_next = mx32(a, term ? qlo[st] : qhi[st], s_next, term ? sb_lo : sb_hi);
             __builtin_amdgcn_sched_barrier(0);
-            // this dot's share of the key reads of unit un (4 reads per unit)
-            if (un < NU) {
+            if (st + 2 < NSTEP) kr[(st + 2) % 3][term] = kread(tt + 1, st + 2, term);
+            const int di = 2 * st + term;
 #pragma unroll
-              for (int r = 0; r < 4 / nmf; ++r) {
-                const int q = mi * (4 / nmf) + r;  // read q: fragment q / 2, half q % 2
-                kring[un % KR][q >> 1][q & 1] = kread(un, q >> 1, q & 1);
+            for (int j = 2; j < 20; ++j)
+              if (((j - 2) * ND) / 18 == di) {
+                int sst, g;
+                stage_of(j, sst, g);
+                stage(sst, g);
               }
-            }
-            // the next pair's slot validity, at this pair's first dot
-            if (sj == 0 && mi == 0 && pm < 3) {
-              bias_v[2 * pm + 2] = *reinterpret_cast<const floatx4*>(kb + 32 * pm + 32);
-              bias_v[2 * pm + 3] = *reinterpret_cast<const floatx4*>(kb + 32 * pm + 48);
-            }
-            // the previous pair's softmax jobs assigned to this dot
-            if (pm > 0) {
-              const int oi = (rope_u ? 16 : 4 * sj) + mi;  // dot index within the pair
-#pragma unroll
-              for (int k = 0; k < 10; ++k)
-                if ((k * MPP) / 10 == oi) job(pm - 1, k);
-            }
+            if (di == ND - 1) finish();
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+      } else {
+        softmax();
       }
-#pragma unroll
-      for (int k = 0; k < 10; ++k) job(3, k);
+      // computed here, before the rare-path branch
+      asm volatile("" :: "v"(phi[0]), "v"(phi[1]), "v"(phi[2]), "v"(phi[3]), "v"(plo[0]),
+                   "v"(plo[1]), "v"(plo[2]), "v"(plo[3]), "v"(lt), "v"(xmax));
 
       // ---- reference moves (rare): the first tile with a valid slot sets
-      // both references to its maximum (rounded up to an integer); a tile
-      // whose weights would pass 2^kMLimit moves the weights' reference m up
-      // to its maximum, and the tile's weights are taken again. O and the row
-      // sums keep the reference m_o: P enters them through the E8M0 block
-      // scale 2^(m - m_o) of the P^T operand, so O is never rescaled.
-      const bool move = xmax > kMLimit || (m_o == kNegInf && xmax != kNegInf);
+      // the weights' reference to its maximum (rounded up to an integer); a
+      // tile whose weights would pass 2^kXLimit raises it to its maximum;
+      // the tile's weights are then taken again.
+      const bool move = xmax > kXLimit || (m_w == kNegInf && xmax != kNegInf);
       if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        float tmax = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            tmax = fmaxf(tmax, __builtin_fmaf(sacc[j][i], cscale, kb[16 * j + i]));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        // the tile's largest score (this lane's, then the head's): its
+        // exponents less the reference they were taken against
+        float tmax = xmax - nm;
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        if (tmax != kNegInf) {
-          if (m_o == kNegInf) {
-            m_o = m_w = __builtin_ceilf(tmax);
-          } else if (tmax > m_w + kMLimit) {
-            m_w = __builtin_ceilf(tmax);
-          }
-        }
-        if (m_w - m_o > kMMaxDrift) redo = 1;  // past what O can absorb: walk again
-        nm = m_o == kNegInf ? 0.f : -m_w;
-        xmax = kNegInf;
-        lt = 0.f;
+        if (tmax != kNegInf && (m_w == kNegInf || tmax > m_w + kXLimit))
+          m_w = __builtin_ceilf(tmax);
+        const float dn = (m_w == kNegInf ? 0.f : -m_w) - nm;
+        nm += dn;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bias_v[j] = *reinterpret_cast<const floatx4*>(kb + 16 * j);
-#pragma unroll
-        for (int pm = 0; pm < 4; ++pm)
-#pragma unroll
-          for (int k = 0; k < 10; ++k) job(pm, k);
+        for (int i = 0; i < 16; ++i) bn[i / 4][i % 4] += dn;
+        softmax();
       }
-      const int drift = m_o == kNegInf ? 0 : int(fminf(m_w - m_o, kMMaxDrift));
-      l_run += __builtin_ldexpf(lt, drift);
-      const int sb_ph = kE8One + drift, sb_pl = kE8One - 4 + drift;
 
-      // ---- O^T += V^T P^T for the 32 column blocks; each value fragment
-      // feeds both terms of P and is read VR - 1 blocks ahead.
+      // ---- publish this half's P^T bytes and weight reference
       {
-        const i32x8 ph = i32x8{int(phi[0]), int(phi[1]), int(phi[2]), int(phi[3]),
-                               int(phi[4]), int(phi[5]), int(phi[6]), int(phi[7])};
-        const i32x8 pl = i32x8{int(plo[0]), int(plo[1]), int(plo[2]), int(plo[3]),
-                               int(plo[4]), int(plo[5]), int(plo[6]), int(plo[7])};
-        const uint8_t* vb = B + vro;
-        // read m (0..3) of column block c: 8 bytes, slots of tile rows
-        // 32m + 8g .. 32m + 8g + 7
-        auto vread = [&](int c, int m) -> u32x2 {
-          return lds_read_tr8(vb + ((16 * c) ^ vperm16) + 32 * m * kMRow);
+        uint8_t* xp = smem + C::OFF_XP + par * C::XPB + (wave * 64 + lane) * 32;
+        *reinterpret_cast<u32x4*>(xp) = u32x4{phi[0], phi[1], phi[2], phi[3]};
+        *reinterpret_cast<u32x4*>(xp + 16) = u32x4{plo[0], plo[1], plo[2], plo[3]};
+        xm[(par * kXWaves + wave) * 32 + c32] = m_w;
+      }
+      sync_tile();  // P and references visible; tile tt + 2 landed; tile tt - 1 free
+
+      // ---- both halves' P^T and references (their latency covered by the
+      // next tile's last k-step and the DMA issue)
+      u32x4 xh0, xl0, xh1, xl1;
+      float m_blk, m_other;
+      {
+        const uint8_t* xp = smem + C::OFF_XP + par * C::XPB + (2 * hp * 64 + lane) * 32;
+        xh0 = *reinterpret_cast<const u32x4*>(xp);
+        xl0 = *reinterpret_cast<const u32x4*>(xp + 16);
+        xh1 = *reinterpret_cast<const u32x4*>(xp + 64 * 32);
+        xl1 = *reinterpret_cast<const u32x4*>(xp + 64 * 32 + 16);
+        m_blk = xm[(par * kXWaves + 2 * hp + h) * 32 + c32];           // half h's
+        m_other = xm[(par * kXWaves + 2 * hp + (kh ^ 1)) * 32 + c32];  // the partner's
+      }
+      if (tt + 3 < nt) read_idx(tt + 3, t_begin + tt + 3);
+      if (has_next) kstep(s_next, NSTEP - 1, kr[(NSTEP - 1) % 3]);
+      if (tt + 3 < nt) issue_dma(tt + 3);
+      if (tt + 5 < nt) idx_dma(tt + 5, t_begin + tt + 5);
+
+      if (m_o == kNegInf) m_o = fmaxf(m_w, m_other);  // the pair's first valid tile
+      float d_blk = 0.f, d_own = 0.f;
+      if (m_o != kNegInf) {
+        redo |= int((m_blk - m_o > kXMaxDrift) || (m_w - m_o > kXMaxDrift));
+        d_blk = fminf(fmaxf(m_blk - m_o, kXMinDrift), kXMaxDrift);
+        d_own = fminf(fmaxf(m_w - m_o, kXMinDrift), kXMaxDrift);
+      }
+      l_run += __builtin_ldexpf(lt, int(d_own));
+      const int sb_ph = kE8One + int(d_blk), sb_pl = kE8One - 4 + int(d_blk);
+      const i32x8 ph = cat(xh0, xh1), pl = cat(xl0, xl1);
+
+      // ---- O^T += V^T P^T over this wave's 8 column blocks; each value
+      // fragment feeds both terms of P and is read two blocks ahead. The
+      // next step's carried reads go out before the last two blocks.
+      {
+        const uint8_t* vb = smem + (tt % kXRing) * C::NOPE + vro;
+        auto vread = [&](int m, int v) -> u32x2 {
+          return lds_read_tr8(vb + 16 * ((2 * m + ve) ^ vperm) +
+                              (32 * (v >> 1) + 16 * (v & 1)) * kXRow);
         };
-        // two column blocks per unit, their dots alternating; each dot is
-        // followed by two of the eight value reads of the unit two ahead
         constexpr int VR = 3;
-        u32x2 vring[VR][2][4];
+        u32x2 vr[VR][4];
 #pragma unroll
-        for (int u = 0; u < VR - 1; ++u)
+        for (int m = 0; m < VR - 1; ++m)
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) vring[u][f][m] = vread(2 * u + f, m);
+          for (int v = 0; v < 4; ++v) vr[m][v] = vread(m, v);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int c = 2 * u, un = u + VR - 1;
-          i32x8 vf[2];
+        for (int m = 0; m < 8; ++m) {
+          const u32x2* q = vr[m % VR];
+          const i32x8 vf = i32x8{int(q[0].x), int(q[0].y), int(q[1].x), int(q[1].y),
+                                 int(q[2].x), int(q[2].y), int(q[3].x), int(q[3].y)};
+          const int mn = m + VR - 1;
 #pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            const u32x2* w = vring[u % VR][f];
-            vf[f] = i32x8{int(w[0].x), int(w[0].y), int(w[1].x), int(w[1].y),
-                          int(w[2].x), int(w[2].y), int(w[3].x), int(w[3].y)};
-          }
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            const int f = mi & 1;
-            o[c + f] = mx(vf[f], mi < 2 ? ph : pl, o[c + f], mi < 2 ? sb_ph : sb_pl);
+          for (int term = 0; term < 2; ++term) {
+            o[m] = mx32(vf, term ? pl : ph, o[m], term ? sb_pl : sb_ph);
             __builtin_amdgcn_sched_barrier(0);
-            if (un < 16) {
-#pragma unroll
-              for (int r = 0; r < 2; ++r) {
-                const int q = 2 * mi + r;  // read q: block q / 4, read q % 4
-                vring[un % VR][q >> 2][q & 3] = vread(2 * un + (q >> 2), q & 3);
-              }
+            if (mn < 8) {
+              vr[mn % VR][2 * term] = vread(mn, 2 * term);
+              vr[mn % VR][2 * term + 1] = vread(mn, 2 * term + 1);
             }
+            if (m == 6 && term == 0 && has_next) make_bn(tt + 1);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
-
-      // O and q stay in the accumulator registers, which MFMA operands may
-      // come from, leaving the vector registers to the operand rings (left
-      // alone, the allocator copies them between the two files).
+      // O and the first seven k-steps of q stay in the accumulator
+      // registers, which MFMA operands may come from (the other 16 hold the
+      // score accumulator), leaving the vector registers to the operand
+      // rings.
 #pragma unroll
-      for (int c = 0; c < 32; ++c) asm volatile("" : "+a"(o[c]));
+      for (int c = 0; c < 8; ++c) asm volatile("" : "+a"(o[c]));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) asm volatile("" : "+a"(qhi[s]), "+a"(qlo[s]));
-      asm volatile("" : "+a"(qrope));
-
-      sync_tile();  // buffer b free; tile t+1 and its flags visible
-      if (t + 2 < t_end) {
-        fix_idx(t + 2);
-        issue_dma(b);
-      }
-      if (t + 3 < t_end) load_idx(t + 3);
+      for (int st = 0; st < 7; ++st) asm volatile("" : "+a"(qhi[st]), "+a"(qlo[st]));
+      s_cur = s_next;
     }
   };
 #pragma clang loop unroll(disable)
   for (int pass = 0; pass < 2; ++pass) {
     walk(pass == 0);
     if (pass == 1 || __syncthreads_or(redo) == 0) break;
+    // the second walk starts from the pair's final weight references
+    const int par = (t_end - t_begin - 1) & 1;
+    m_o = fmaxf(m_w, xm[(par * kXWaves + (wave ^ 1)) * 32 + c32]);
+    __syncthreads();  // every wave has read them before the walk reuses the area
   }
 
-  // ---- epilogue: the head's row sum over the four lane groups; normalise;
-  // store.
-  float lt_tot = l_run + __shfl_xor(l_run, 16);
-  lt_tot += __shfl_xor(lt_tot, 32);
+  // ---- epilogue: the head's row sum over both lane halves and both waves
+  // of the pair; normalise; store.
+  const float l_lane = l_run + __shfl_xor(l_run, 32);
+  xl[wave * 32 + c32] = l_lane;
   if constexpr (EPI) {
     if (tid < 64) epi_cs[tid] = cs_pre;
-    __syncthreads();
   }
+  __syncthreads();
+  const float lt_tot = l_lane + xl[(wave ^ 1) * 32 + c32];
   if (!head_ok) return;
   const float inv = lt_tot > 0.f ? kv_scale / lt_tot : 0.f;
   const bool split_mode = p.part_o != nullptr;
+  const int colh = 256 * kh + 4 * h;  // column of register 0 of block 0
   if (EPI && !split_mode) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const floatx4 ra = o[2 * m] * inv, rb = o[2 * m + 1] * inv;
-      float va[4] = {ra[0], ra[1], ra[2], ra[3]}, vb2[4] = {rb[0], rb[1], rb[2], rb[3]};
-      epi_store_c16x2(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, r, head, 32 * m + 4 * g, va,
-                      vb2);
+    for (int m = 0; m < 8; ++m) {
+      float v[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[j][u] = o[m][4 * j + u] * inv;
+      epi_store_c32x4(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, r, head, colh + 32 * m, v);
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      const floatx4 res = o[c] * inv;
-      const int col = 16 * c + 4 * g;
-      if (!split_mode) {
-        *reinterpret_cast<u32x2*>(p.out + r * p.out_rs + int64_t(head) * p.out_hs + col) =
-            u32x2{pack_bf16(res[0], res[1]), pack_bf16(res[2], res[3])};
-      } else {
-        *reinterpret_cast<floatx4*>(
-            p.part_o + ((int64_t(split) * p.rows + r) * p.heads + head) * kDv + col) = res;
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = colh + 32 * m + 8 * j;
+        const float a0 = o[m][4 * j] * inv, a1 = o[m][4 * j + 1] * inv;
+        const float a2 = o[m][4 * j + 2] * inv, a3 = o[m][4 * j + 3] * inv;
+        if (!split_mode) {
+          *reinterpret_cast<u32x2*>(p.out + r * p.out_rs + int64_t(head) * p.out_hs + col) =
+              u32x2{pack_bf16(a0, a1), pack_bf16(a2, a3)};
+        } else {
+          *reinterpret_cast<floatx4*>(
+              p.part_o + ((int64_t(split) * p.rows + r) * p.heads + head) * kDv + col) =
+              floatx4{a0, a1, a2, a3};
+        }
       }
-    }
   }
-  if (g == 0) {
+  if (kh == 0 && h == 0) {
     const float lse = lt_tot > 0.f ? (m_o + __log2f(lt_tot)) * kLn2 : kNegInf;
     if (!split_mode)
       p.lse[r * p.lse_rs + int64_t(head) * p.lse_hs] = lse;
@@ -674,12 +806,12 @@ prefill_mx_kernel(const FwdParams p) {
 
 KernelShape prefill_mx_shape(int dqk) {
   KernelShape k;
-  k.waves = kMWaves;
-  k.tile = kMTile;
+  k.waves = kXWaves;
+  k.tile = kXTile;
   if (dqk == 576)
-    k.lds_bytes = MCfg<576>::LDS;
+    k.lds_bytes = XCfg<576>::LDS;
   else if (dqk == 512)
-    k.lds_bytes = MCfg<512>::LDS;
+    k.lds_bytes = XCfg<512>::LDS;
   else
     k = KernelShape{};
   return k;
@@ -697,7 +829,7 @@ int launch_prefill_mx(const FwdParams& p, int dqk, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool epi = epi_active(p.epi) && p.part_o == nullptr;
   const bool paged = p.page_shift != 31;
-  const dim3 grid(uint32_t(p.grid)), block(kMWaves * 64);
+  const dim3 grid(uint32_t(p.grid)), block(kXWaves * 64);
   if (dqk == 576)
     paged ? launch_mx<576, true>(p, epi, grid, block, st) : launch_mx<576, false>(p, epi, grid, block, st);
   else if (dqk == 512)
