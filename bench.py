@@ -13,18 +13,23 @@ launches on. Rank 0 prints one JSON line.
 
 Headline workload: fp8 decode, 128 requests x (5+1) rows = 768 rows, 16 heads,
 576-wide rows, pool 262144 x 576 e4m3fn + per-tensor scale, top-k 2048 (the
-decode shape the HBM-roofline target is set on). The two 64-head prefill
-workloads are timed too and reported under "prefill" with their MFMA fraction,
-and the two decode workloads again as two-segment calls (a seeded 128-slot
-sliding window over a second pool with its own scale, next to the same
-workload's one-segment time) under "two_segment", and with the output
-epilogue (inverse RoPE of the last 64 columns and an MXFP8 store) fused into
-the forward's store, next to the plain forward followed by the separate
-epilogue pass, under "epilogue". The headline decode is timed again on a
-pool that does not fit the MALL (each request's top-k from its own
-16384-row context of a 1.2 GB pool) under "sensitivity". The indexer that produces index rows (fp8
-MQA logits over [ks, ke) windows, then a per-row top-k) is timed on the
-shapes of its own kernel-time table under "indexer".
+decode shape the HBM-roofline target is set on). Every configuration of the
+method's workload table (tiny, the bf16 and fp8 decodes, the two 64-head
+prefills) is timed on its own under "configs", with its roofline fraction (HBM
+for the decodes and the tiny call, bf16 MFMA for the prefills) and the fp64
+oracle timed beside it on the host (the tiny call and the decodes in full, the
+prefills on every 64th row, scaled to the whole call). The two decodes are
+timed again with their heads split over two GPUs (32 heads: one GPU's share)
+under "head_share", as two-segment calls (a seeded 128-slot sliding window over
+a second pool with its own scale, next to the same workload's one-segment
+time) under "two_segment", and with the output epilogue (inverse RoPE of the
+last 64 columns and an MXFP8 store) fused into the forward's store, next to
+the plain forward followed by the separate epilogue pass, under "epilogue".
+The headline decode is timed again on a pool that does not fit the MALL (each
+request's top-k from its own 16384-row context of a 1.2 GB pool) under
+"sensitivity". The indexer that produces index rows (fp8 MQA logits over
+[ks, ke) windows, then a per-row top-k) is timed on the shapes of its own
+kernel-time table under "indexer".
 """
 
 from __future__ import annotations
@@ -55,8 +60,10 @@ def attention_kernel(plan, d_qk, fp8):
     if hb == 64 and v != 1:
         if fp8 and v == 0:
             return f"smla::prefill_fp8_kernel<{d_qk}, false>", "prefill_fp8.hip"
+        if fp8 and v == 3:
+            return f"smla::prefill_mx_kernel<{d_qk}, false, false>", "prefill_mx.hip"
         return f"smla::prefill_kernel<{d_qk}, {str(fp8).lower()}, false>", "prefill.hip"
-    return "smla::fwd_kernel (staged tile)", "kernels.hip"
+    return f"smla::fwd_kernel (staged tile, {hb} heads)", "kernels.hip"
 
 
 def parse():
@@ -65,8 +72,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_fp8")
-    ap.add_argument("--prefill", default="prefill_fp8,prefill_glm",
-                    help="comma list of extra workloads to time ('' for none)")
+    ap.add_argument("--configs", default="tiny,decode_bf16,decode_fp8,prefill_fp8,prefill_glm",
+                    help="comma list of the configurations timed on their own, each with its "
+                         "roofline fraction and the oracle beside it ('' for none)")
+    ap.add_argument("--head-share", default="decode_bf16_h32,decode_fp8_h32",
+                    help="decode workloads with 32 heads (one GPU's share of a two-way head "
+                         "split) ('' for none)")
     ap.add_argument("--two-segment", default="decode_bf16,decode_fp8",
                     help="comma list of workloads also timed with a sliding-window second "
                          "segment ('' for none)")
@@ -80,8 +91,6 @@ def parse():
                     help="decode workloads whose pool does not fit the MALL, reported next to "
                          "the headline ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time for the oracle sample")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to calibrate HBM byte counters)")
@@ -122,8 +131,8 @@ def source_digest(src):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_src, workload):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
+def counters_from_profiles(kernel_src, workload):
+    """The committed rocprofv3 --pmc summary of a kernel on a workload, if it
     was taken on the current source of the kernel; else None."""
     stem = kernel_src.rsplit(".", 1)[0]
     path = os.path.join(ROOT, "profiles", f"{stem}_kernel_{workload}_pmc.json")
@@ -134,7 +143,7 @@ def traffic_from_profiles(kernel_src, workload):
             d = json.load(f)
         if d.get("kernel_source_sha256_16") != source_digest(kernel_src):
             return None
-        return d.get("hbm_bytes_per_launch")
+        return d
     except Exception:
         return None
 
@@ -280,10 +289,20 @@ def time_indexer(name, steps, warmup):
             "logits_write_tbs": round(M * N * 4 / (res["logits"] * 1e-6) / 1e12, 2)}
 
 
-def cpu_baseline(inp, target_s):
-    """Time the fp64 oracle as it stands on a bounded sample of rows (random
-    order, cycling through the rows again if one pass takes less than
-    target_s)."""
+def host_cores():
+    """(physical cores, logical CPUs) of the host."""
+    logical = os.cpu_count() or 1
+    try:
+        import psutil
+        return psutil.cpu_count(logical=False) or logical, logical
+    except Exception:
+        return logical, logical
+
+
+def cpu_baseline(inp, stride=1):
+    """Time the fp64 oracle as it stands on the call's rows (every
+    `stride`-th row when stride > 1, the time then scaled by the row count to
+    one whole call)."""
     import numpy as np
     import oracle
     try:
@@ -292,23 +311,43 @@ def cpu_baseline(inp, target_s):
     except Exception:
         threads = os.cpu_count() or 1
     R = inp.q.shape[0]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(R)
-    done, t0 = 0, time.perf_counter()
-    chunk = 8
-    while time.perf_counter() - t0 < target_s:
-        start = done % R
-        rows = np.sort(order[start:start + chunk])
+    rows = np.arange(0, R, stride)
+    t0 = time.perf_counter()
+    for lo in range(0, len(rows), 64):  # chunks bound the gathered rows held at once
         oracle.sparse_mla_fwd_torch(inp.q, inp.pool, inp.kv_scale, inp.indices, inp.sm_scale,
-                                    rows=rows)
-        done += len(rows)
-        chunk = min(2 * chunk, 256)
+                                    rows=rows[lo:lo + 64])
     el = time.perf_counter() - t0
-    us_per_call = el / done * R * 1e6
-    return {"value": round(us_per_call, 1), "unit": "us/call", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} rows of {R} (random order, seed 0, cycling) in {el:.1f} s, "
-                      f"scaled by {R}/{done} to one call; host has {os.cpu_count()} logical CPUs"}
+    cores, logical = host_cores()
+    if stride == 1:
+        sample = f"all {R} rows in {el:.2f} s"
+    else:
+        sample = (f"every {stride}th row ({len(rows)} of {R}) in {el:.2f} s, scaled by "
+                  f"{R}/{len(rows)} to the whole call (rows cost the same: equal top-k)")
+    return {"value": round(el / len(rows) * R * 1e6, 1), "unit": "us/call", "cores": cores,
+            "threads": threads, "logical_cpus": logical, "kind": "oracle", "sample": sample}
+
+
+def config_record(name, r, bound, cpu=None):
+    """One configuration's figures from a time_workload result."""
+    us = statistics.median(r["times"])
+    w = r["inp"].workload
+    alg = r["alg"]
+    tf = alg["flops"] / (us * 1e-6) / 1e12
+    gbs = alg["bytes"] / (us * 1e-6) / 1e9
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    rec = {"workload": name, "description": w.description, "us_per_call": round(us, 2),
+           "us_min": round(min(r["times"]), 2), "warm_us_per_call": round(r["warm_us"], 2),
+           "gathered_kv_tbs": round(alg["kv_bytes"] / (us * 1e-6) / 1e12, 3),
+           "alg_tbs": round(gbs / 1e3, 3), "tflops": round(tf, 2), "roofline": roof,
+           "kernel": attention_kernel(r["plan"], w.d_qk, w.kv_dtype == "fp8")[0], "plan": r["plan"]}
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
+    return rec
 
 
 def main():
@@ -328,16 +367,17 @@ def main():
     _lib.load()  # fails loudly if the HIP library is not built
 
     cold = not args.warm
+    cpu_on = not args.no_cpu_baseline
     head = time_workload(args.workload, args.steps, args.warmup, cold)
     times = head["times"]
     us = statistics.median(times)
     alg = head["alg"]
-    # dominant kernel: the attention kernel (the whole call when splits == 1)
-    kernel_us = us
-    w0 = head["inp"].workload
-    kname, ksrc = attention_kernel(head["plan"], w0.d_qk, w0.kv_dtype == "fp8")
-    achieved = alg["bytes"] / (kernel_us * 1e-6) / 1e9
     w = head["inp"].workload
+    kname, ksrc = attention_kernel(head["plan"], w.d_qk, w.kv_dtype == "fp8")
+    # the plan is one launch of the attention kernel (splits == 1), so the
+    # event time of a call is that kernel's launch duration
+    achieved = alg["bytes"] / (us * 1e-6) / 1e9
+    ctr = counters_from_profiles(ksrc, w.name)
     line = {
         "metric": "sparse MLA us/call; HBM TB/s (decode) and MFMA TFLOP/s (prefill), 1 GPU",
         "value": round(us, 2),
@@ -367,40 +407,56 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles(ksrc, w.name),
+            "traffic": ctr.get("hbm_bytes_per_launch") if ctr else None,
+            "traffic_kind": "L2-to-fabric bytes per launch: FETCH_SIZE x 2 + WRITE_SIZE (factors "
+                            "from a 1 GiB copy); MALL hits included",
+            "dram_destined_read_bytes": ctr.get("dram_destined_read_bytes_per_launch") if ctr else None,
             "bytes_per_launch": alg["bytes"],
             "kernel": kname,
-            "kernel_avg_us": round(kernel_us, 2),
+            "call_event_us": round(us, 2),
         },
     }
+    configs = []
+    for name in [s_ for s_ in args.configs.split(",") if s_]:
+        prefill = name.startswith("prefill")
+        r = head if name == args.workload else time_workload(
+            name, max(3, args.steps // 2) if prefill else args.steps, 2 if prefill else 3, cold)
+        cpu = cpu_baseline(r["inp"], stride=64 if prefill else 1) if cpu_on else None
+        configs.append(config_record(name, r, "mfma" if prefill else "hbm", cpu))
+        if name == args.workload and cpu is not None:
+            line["cpu_baseline"] = cpu
+        if r is not head:
+            del r
+    if configs:
+        line["configs"] = configs
+    if cpu_on and "cpu_baseline" not in line:
+        line["cpu_baseline"] = cpu_baseline(head["inp"], stride=1)
+    share = []
+    for name in [s_ for s_ in args.head_share.split(",") if s_]:
+        r = time_workload(name, args.steps, 3, cold)
+        share.append(config_record(name, r, "hbm"))
+        del r
+    if share:
+        line["head_share"] = share
     sens = []
-    for name in [s for s in args.sensitivity.split(",") if s]:
+    for name in [s_ for s_ in args.sensitivity.split(",") if s_]:
         r = time_workload(name, args.steps, 3, cold)
         sus = statistics.median(r["times"])
-        sens.append({"workload": name, "description": r["inp"].workload.description,
+        ws = r["inp"].workload
+        sc = counters_from_profiles(attention_kernel(r["plan"], ws.d_qk, ws.kv_dtype == "fp8")[1],
+                                    name)
+        sens.append({"workload": name, "description": ws.description,
                      "us_per_call": round(sus, 1), "warm_us_per_call": round(r["warm_us"], 1),
                      "alg_tbs": round(r["alg"]["bytes"] / (sus * 1e-6) / 1e12, 2),
                      "hbm_frac": round(r["alg"]["bytes"] / (sus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "l2_fabric_bytes": sc.get("hbm_bytes_per_launch") if sc else None,
+                     "dram_destined_read_bytes": sc.get("dram_destined_read_bytes_per_launch") if sc else None,
                      "plan": r["plan"]})
         del r
     if sens:
         line["sensitivity"] = sens
-    prefill = []
-    for name in [s for s in args.prefill.split(",") if s]:
-        r = time_workload(name, max(3, args.steps // 2), 2, cold)
-        pus = statistics.median(r["times"])
-        tf = r["alg"]["flops"] / (pus * 1e-6) / 1e12
-        wp = r["inp"].workload
-        prefill.append({"workload": name, "us_per_call": round(pus, 1), "tflops": round(tf, 1),
-                        "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "kernel": attention_kernel(r["plan"], wp.d_qk, wp.kv_dtype == "fp8")[0],
-                        "warm_us_per_call": round(r["warm_us"], 1), "plan": r["plan"],
-                        "gathered_kv_tbs": round(r["alg"]["kv_bytes"] / (pus * 1e-6) / 1e12, 2)})
-        del r
-    if prefill:
-        line["prefill"] = prefill
     two = []
-    for name in [s for s in args.two_segment.split(",") if s]:
+    for name in [s_ for s_ in args.two_segment.split(",") if s_]:
         r = time_workload(name, args.steps, 3, cold, window=args.window)
         one = time_workload(name, args.steps, 3, cold)
         tus = statistics.median(r["times"])
@@ -414,7 +470,7 @@ def main():
     if two:
         line["two_segment"] = two
     epis = []
-    for name in [s for s in args.epilogue.split(",") if s]:
+    for name in [s_ for s_ in args.epilogue.split(",") if s_]:
         res = {m: time_workload(name, args.steps, 3, cold, epi=m)
                for m in ("fused", "unfused", None)}
         us_ = {m: statistics.median(r["times"]) for m, r in res.items()}
@@ -428,11 +484,9 @@ def main():
     if epis:
         line["epilogue"] = epis
     ixs = [time_indexer(name, max(5, args.steps // 2), 2)
-           for name in [s for s in args.indexer.split(",") if s]]
+           for name in [s_ for s_ in args.indexer.split(",") if s_]]
     if ixs:
         line["indexer"] = ixs
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(head["inp"], args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

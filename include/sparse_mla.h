@@ -75,11 +75,17 @@ typedef struct smla_options {
   int32_t head_block;      /* 0 = planner's choice, else 16, 32 or 64 heads per workgroup */
   int32_t splits;          /* 0 = planner's choice, else 1..64 splits of each row's slots */
   int32_t remap;           /* 0 = planner's choice, 1 = XCD-aware order, 2 = grid order */
-  int32_t variant;         /* kernel instance; 0 = default. 1 = the staged-tile kernel
-                              (any head block; also what pools past the 32-bit buffer
-                              range use). 2 = 64 heads only: the 8-wave double-buffered
-                              kernel (the default over bf16 pools; the fp8 default is
-                              the 4-wave kernel) */
+  int32_t variant;         /* kernel instance; 0 = the planner's choice: the 16-head
+                              decode kernel over fp8 pools (H <= 32), the staged-tile
+                              kernel (16 and 32 heads over bf16 pools; 64 heads over
+                              bf16 pools), the 4-wave kernel (64 heads over fp8 pools).
+                              1 = the staged-tile kernel (any head block; also what
+                              pools past the 32-bit buffer range use). 2 = 64 heads
+                              only: the 8-wave double-buffered kernel. 3 = 64 heads
+                              over fp8 pools only: the fp8-dot kernel (both products
+                              on the fp8 matrix cores over two-term e4m3 splits of q
+                              and P); falls back to the default where the pool's row
+                              pitch does not fit its structured buffer */
   void* workspace;         /* optional caller device buffer for split partials */
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
   const void* q_scale;     /* fp32 [1] device pointer: per-tensor scale of a float8_e4m3fn q

@@ -474,6 +474,15 @@ int plan_two(const Checked& c1, const Checked& c2, const smla_options* opt, int 
   tot.topk = c1.pb.topk + c2.pb.topk;
   tot.pool_bytes = std::max(c1.pb.pool_bytes, c2.pb.pool_bytes);
   if ((s = make_plan(tot, opt, num_cus, p1, &perr))) return fail(s, perr);
+  // 64 heads over bf16 pools: unless the caller chose a kernel, the 8-wave
+  // kernel, which walks both segments in one launch (the one-segment
+  // default, the staged-tile kernel, would need two launches and a combine).
+  smla_options o2 = opt ? *opt : smla_options{};
+  if (p1->head_block == 64 && !c1.fp8 && o2.variant == 0) {
+    o2.variant = 2;
+    opt = &o2;
+    if ((s = make_plan(tot, opt, num_cus, p1, &perr))) return fail(s, perr);
+  }
   if (walks_second_segment(p1->head_block, c1.fp8, p1->variant)) {
     if (!uses_decode_kernel(p1->head_block, c1.fp8, p1->variant)) {
       // Tiled walk: the second segment starts at a whole tile.

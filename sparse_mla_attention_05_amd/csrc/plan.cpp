@@ -7,7 +7,15 @@
 // the CUs; XCD remap only for rows of two or more head blocks), re-derived for
 // this kernel:
 //  * head block: 16 heads for H <= 16, 32 for H <= 32, else 64, so one
-//    workgroup gathers and stages each KV tile once for as many heads as fit.
+//    workgroup gathers and stages each KV tile once for as many heads as fit;
+//    except that fp8 pools with H <= 32 take 16-head blocks: the 16-head
+//    decode kernel twice (its two head blocks of a row side by side on one
+//    XCD) measured 260 us against 340 us for the 32-head staged kernel on
+//    the 768-row, top-k 2048 decode at 32 heads.
+//  * kernel: over bf16 pools the 64-head staged-tile kernel (variant 1);
+//    it measured 3-14 % faster than the 8-wave kernel of prefill.hip on
+//    every 64-head bf16 shape tried (96..2048 rows, top-k 512 and 2048;
+//    55.3 against 63.2 us on the 192-row decode), which stays as variant 2.
 //  * splits: when rows x head blocks leave the CUs' workgroup slots
 //    underfilled, each row's slots are split if a makespan model (rounds of
 //    workgroups x (tiles per split + a fixed per-workgroup cost) + the
@@ -49,7 +57,7 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
     }
     hb = opt->head_block;
   } else {
-    hb = pb.heads <= 16 ? 16 : (pb.heads <= 32 ? 32 : 64);
+    hb = pb.heads <= 16 ? 16 : (pb.heads <= 32 ? (pb.kv_fp8 ? 16 : 32) : 64);
   }
   int variant = 0;
   if (opt && opt->variant) {
@@ -59,6 +67,8 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
       return SMLA_ERR_INVALID_ARG;
     }
     variant = opt->variant;
+  } else if (hb == 64 && !pb.kv_fp8) {
+    variant = 1;
   }
   // The decode (16 heads, fp8) and 64-head kernels read the pool through a
   // 32-bit buffer range; a larger pool takes the staged-tile kernel.

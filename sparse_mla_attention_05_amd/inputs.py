@@ -113,6 +113,21 @@ SENSITIVITY_WORKLOADS: dict[str, Workload] = {
 }
 
 
+# The two decode workloads with their heads split over two GPUs (32 heads on
+# each): one GPU's share of a head-parallel deployment, timed on its own.
+HEAD_SHARE_WORKLOADS: dict[str, Workload] = {
+    "decode_bf16_h32": Workload(
+        name="decode_bf16_h32", rows=192, heads=32, d_qk=576, pool_rows=131072, topk=512,
+        kv_dtype="bf16", seed=1, index_mode="request", invalid_per_row=26, rows_per_request=6,
+        ctx_per_request=4096,
+        description="decode_bf16 with 32 heads (one GPU's share of a two-way head split)"),
+    "decode_fp8_h32": Workload(
+        name="decode_fp8_h32", rows=768, heads=32, d_qk=576, pool_rows=262144, topk=2048,
+        kv_dtype="fp8", seed=2, index_mode="uniform",
+        description="decode_fp8 with 32 heads (one GPU's share of a two-way head split)"),
+}
+
+
 @dataclass
 class Inputs:
     q: torch.Tensor          # bf16 [R, H, D]
@@ -215,7 +230,7 @@ def make_inputs(w: Workload | str, rows: int | None = None) -> Inputs:
     byte-identical to the same rows of the full draw.
     """
     if isinstance(w, str):
-        w = WORKLOADS[w] if w in WORKLOADS else SENSITIVITY_WORKLOADS[w]
+        w = {**WORKLOADS, **SENSITIVITY_WORKLOADS, **HEAD_SHARE_WORKLOADS}[w]
     gen = torch.Generator(device="cpu").manual_seed(w.seed)
     q = torch.randn((w.rows, w.heads, w.d_qk), generator=gen, dtype=torch.float32)
     q = q.to(torch.bfloat16)

@@ -140,7 +140,17 @@ def test_plan_is_legal(R, H, D, K):
 
 def test_plan_head_block_choice_and_overrides():
     assert _plan(768, 16)["head_block"] == 16
-    assert _plan(100, 32)["head_block"] == 32
+    # 32 heads: two 16-head decode-kernel blocks over fp8 pools (measured
+    # faster than the 32-head staged kernel), one 32-head block over bf16
+    p = _plan(768, 32)
+    assert (p["head_block"], p["head_blocks"], p["variant"], p["remap"]) == (16, 2, 0, 1)
+    p = _plan(100, 32, dtype=torch.bfloat16)
+    assert (p["head_block"], p["variant"]) == (32, 0)
+    assert _plan(100, 48)["head_block"] == 64
+    # 64 heads over bf16 pools: the staged-tile kernel unless overridden
+    assert _plan(192, 64, K=512, dtype=torch.bfloat16)["variant"] == 1
+    assert _plan(192, 64, K=512, dtype=torch.bfloat16, variant=2)["variant"] == 2
+    assert _plan(8192, 64)["variant"] == 0
     assert _plan(8192, 64)["head_block"] == 64
     assert _plan(8192, 64)["splits"] == 1
     assert _plan(4, 16, K=2048)["splits"] > 1      # a tiny launch gets split
@@ -239,7 +249,10 @@ def test_plan2_workspace_covers_both_segments(H, K1, K2, dtype):
     elif dtype == torch.bfloat16:
         # the 64-head bf16 kernel walks them too, the main top-k padded to tiles
         K1p = (K1 + whole["tile_slots"] - 1) // whole["tile_slots"] * whole["tile_slots"]
-        padded = _lib.sparse_mla_plan(q, pool, torch.zeros(R, K1p + K2, dtype=torch.int32))
+        # (the 8-wave kernel, variant 2: the one-segment default is the staged
+        # kernel, which would need a second launch)
+        padded = _lib.sparse_mla_plan(q, pool, torch.zeros(R, K1p + K2, dtype=torch.int32),
+                                      variant=2)
         assert p1 == padded and p2["grid"] == 0
         S = p1["splits"] if p1["splits"] > 1 else 0
     else:

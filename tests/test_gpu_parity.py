@@ -86,7 +86,8 @@ def _check(inp, **opts):
 
 # ---------------------------------------------------------- the workloads
 
-@pytest.mark.parametrize("name", ["tiny", "decode_bf16", "decode_fp8"])
+@pytest.mark.parametrize("name", ["tiny", "decode_bf16", "decode_fp8", "decode_bf16_h32",
+                                  "decode_fp8_h32"])
 def test_workload_full_parity(name):
     print(f"\n[parity] workload={name}", flush=True)
     inp = make_inputs(name)
@@ -347,7 +348,7 @@ VARIANT_SHAPES = [(v, d, kv, h) for v in (0, 1, 2, 3)
 @pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (17, 1), (1000, 3), (300, 2)])
 def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
     """The 64-head kernels (variant 0: the 4-wave kernel over fp8 pools, the
-    8-wave kernel over bf16 pools; 1: the single-buffered staged-tile kernel;
+    staged-tile kernel over bf16 pools; 1: the single-buffered staged-tile kernel;
     2: the 8-wave kernel; 3: the fp8-dot kernel, fp8 pools only) on ragged
     top-k, odd tile counts, a partial head block, leading invalid tiles and
     an empty row, with and without splits."""
