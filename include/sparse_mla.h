@@ -90,6 +90,11 @@ typedef struct smla_options {
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
   const void* q_scale;     /* fp32 [1] device pointer: per-tensor scale of a float8_e4m3fn q
                               (value = code * q_scale; NULL = 1). Must be NULL for a bf16 q */
+  int32_t workgroups;      /* kernels that walk several work items per workgroup (the
+                              fp8-dot kernel on rows that are not split): 0 = one
+                              workgroup per compute unit of the device, else at most
+                              this many (rounded down to a multiple of 8 when >= 8);
+                              negative is an error. Results do not depend on it */
 } smla_options;
 
 /* What the planner picked for a call (sparse_mla_plan). */

@@ -38,7 +38,7 @@ class SmlaOptions(ctypes.Structure):
     _fields_ = [("head_block", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("remap", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
-                ("q_scale", ctypes.c_void_p)]
+                ("q_scale", ctypes.c_void_p), ("workgroups", ctypes.c_int32)]
 
 
 class SmlaPlan(ctypes.Structure):
@@ -168,9 +168,10 @@ def _check(status: int):
 
 
 def _options(head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None, variant=0,
-             q_scale=None):
+             q_scale=None, workgroups=0):
     o = SmlaOptions()
     o.head_block, o.splits, o.remap, o.variant = head_block, splits, remap, variant
+    o.workgroups = workgroups
     if q_scale is not None:
         o.q_scale = q_scale.data_ptr()
     if workspace is not None:
@@ -191,34 +192,39 @@ def sparse_mla_fwd(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=Non
 
 def sparse_mla_fwd_ex(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None,
                       head_block=0, splits=0, remap=0, workspace=None, workspace_bytes=None,
-                      variant=0, q_scale=None) -> None:
+                      variant=0, q_scale=None,
+                      workgroups=0) -> None:
     """sparse_mla_fwd with planner overrides (head_block 16/32/64, splits,
     remap 1 = XCD-aware / 2 = grid order, kernel variant) and an optional
     caller workspace."""
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, out, lse)]
-    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale,
+                   workgroups)
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd_ex(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), _ptr(ds[3]),
                                  float(sm_scale), _ptr(ds[4]), _ptr(ds[5]), st, ctypes.byref(opt)))
 
 
 def sparse_mla_fwd_noalloc(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None,
-                           head_block=0, splits=0, remap=0, variant=0, q_scale=None) -> None:
+                           head_block=0, splits=0, remap=0, variant=0, q_scale=None,
+                           workgroups=0) -> None:
     """sparse_mla_fwd_ex without any device allocation: split partials go to
     the library's fixed per-device scratch (SMLA_NOALLOC_SCRATCH_BYTES)."""
     _check(status_of_fwd_noalloc(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream,
-                                 head_block, splits, remap, variant, q_scale))
+                                 head_block, splits, remap, variant, q_scale,
+                                 workgroups=workgroups))
 
 
 def status_of_fwd_noalloc(q, kv_pool, kv_scale, indices, sm_scale, out, lse, stream=None,
                           head_block=0, splits=0, remap=0, variant=0, q_scale=None,
-                          workspace=None, workspace_bytes=None) -> int:
+                          workspace=None, workspace_bytes=None, workgroups=0) -> int:
     """Raw status of sparse_mla_fwd_noalloc (a workspace may be passed only to
     test its rejection)."""
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, out, lse)]
-    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale,
+                   workgroups)
     st = _stream_handle(stream, q, out)
     return lib.sparse_mla_fwd_noalloc(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), _ptr(ds[3]),
                                       float(sm_scale), _ptr(ds[4]), _ptr(ds[5]), st,
@@ -255,10 +261,10 @@ def sparse_mla_is_supported(q, kv_pool, indices) -> bool:
 
 
 def sparse_mla_plan(q, kv_pool, indices, head_block=0, splits=0, remap=0, num_cus=0,
-                    variant=0) -> dict:
+                    variant=0, workgroups=0) -> dict:
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, indices)]
-    opt = _options(head_block, splits, remap, variant=variant)
+    opt = _options(head_block, splits, remap, variant=variant, workgroups=workgroups)
     plan = SmlaPlan()
     _check(lib.sparse_mla_plan(_ptr(ds[0]), _ptr(ds[1]), _ptr(ds[2]), ctypes.byref(opt),
                                int(num_cus), ctypes.byref(plan)))
@@ -267,14 +273,16 @@ def sparse_mla_plan(q, kv_pool, indices, head_block=0, splits=0, remap=0, num_cu
 
 def sparse_mla_fwd2(q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale, extra_indices,
                     sm_scale, out, lse, stream=None, head_block=0, splits=0, remap=0,
-                    workspace=None, workspace_bytes=None, variant=0, q_scale=None) -> None:
+                    workspace=None, workspace_bytes=None, variant=0, q_scale=None,
+                    workgroups=0) -> None:
     """Two-segment forward: one softmax over the valid slots of `indices` into
     kv_pool (scale kv_scale) and of `extra_indices` into extra_pool (scale
     extra_kv_scale, or kv_scale when None for fp8 pools)."""
     lib = load()
     ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale,
                                 extra_indices, out, lse)]
-    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale,
+                   workgroups)
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd2(*[_ptr(d) for d in ds[:7]], float(sm_scale), _ptr(ds[7]),
                                _ptr(ds[8]), st, ctypes.byref(opt)))
@@ -335,7 +343,8 @@ def _epilogue(rope_positions=None, rope_cos_sin=None, out_scale=None):
 def sparse_mla_fwd_epi(q, kv_pool, kv_scale, indices, sm_scale, out, lse, rope_positions=None,
                        rope_cos_sin=None, out_scale=None, extra_pool=None, extra_kv_scale=None,
                        extra_indices=None, stream=None, head_block=0, splits=0, remap=0,
-                       workspace=None, workspace_bytes=None, variant=0, q_scale=None) -> None:
+                       workspace=None, workspace_bytes=None, variant=0, q_scale=None,
+                       workgroups=0) -> None:
     """Forward whose final store applies the output epilogue: inverse RoPE of
     columns 448..511 (rope_positions int32 [R], rope_cos_sin fp32 [P, 64]) and,
     with out_scale (float8_e8m0fnu [R, H, 16]), an MXFP8 store of float8_e4m3fn
@@ -344,7 +353,8 @@ def sparse_mla_fwd_epi(q, kv_pool, kv_scale, indices, sm_scale, out, lse, rope_p
     ds = [describe(t) for t in (q, kv_pool, kv_scale, indices, extra_pool, extra_kv_scale,
                                 extra_indices, out, lse)]
     epi, _keep = _epilogue(rope_positions, rope_cos_sin, out_scale)
-    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale)
+    opt = _options(head_block, splits, remap, workspace, workspace_bytes, variant, q_scale,
+                   workgroups)
     st = _stream_handle(stream, q, out)
     _check(lib.sparse_mla_fwd_epi(*[_ptr(d) for d in ds[:7]], float(sm_scale), ctypes.byref(epi),
                                   _ptr(ds[7]), _ptr(ds[8]), st, ctypes.byref(opt)))

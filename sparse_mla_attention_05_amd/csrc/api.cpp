@@ -358,7 +358,8 @@ int validate_epilogue(const smla_epilogue* epi, int64_t R, int64_t H, smla_tenso
 // of the segment, its plan's launch shape.
 FwdParams segment_params(const smla_tensor* q, const smla_tensor* pool, const float* scale,
                          const smla_tensor* idx, const Checked& c, const smla_plan& plan,
-                         float sm_scale, smla_tensor* out, smla_tensor* lse) {
+                         float sm_scale, smla_tensor* out, smla_tensor* lse,
+                         const smla_options* opt) {
   FwdParams p{};
   p.q = static_cast<const uint16_t*>(q->data);
   p.q_rs = q->stride[0];
@@ -396,6 +397,11 @@ FwdParams segment_params(const smla_tensor* q, const smla_tensor* pool, const fl
   p.head_blocks = plan.head_blocks;
   p.remap = plan.remap;
   p.grid = plan.grid;
+  int dev = 0;
+  p.persist_cap = opt && opt->workgroups > 0
+                      ? opt->workgroups
+                      : (hipGetDevice(&dev) == hipSuccess ? device_cus(dev) : 0);
+  p.q_scale = opt ? static_cast<const float*>(opt->q_scale) : nullptr;
   p.sm_log2 = sm_scale * 1.4426950408889634f;
   p.q_fp8 = c.q_fp8 ? 1 : 0;
   return p;
@@ -524,7 +530,7 @@ int fwd_one(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
   if ((s = make_plan(c.pb, opt, device_cus(dev), &plan, &perr))) return fail(s, perr);
 
   FwdParams p = segment_params(q, kv_pool, c.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
-                               indices, c, plan, sm_scale, out, lse);
+                               indices, c, plan, sm_scale, out, lse, opt);
   p.epi = eo;
   p.q_scale = opt ? static_cast<const float*>(opt->q_scale) : nullptr;
   if (plan.splits > 1) {
@@ -588,7 +594,7 @@ int fwd_two(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
     // the plan splits).
     FwdParams p = segment_params(q, kv_pool,
                                  c1.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
-                                 indices, c1, plan1, sm_scale, out, lse);
+                                 indices, c1, plan1, sm_scale, out, lse, opt);
     p.epi = eo;
     p.q_scale = opt ? static_cast<const float*>(opt->q_scale) : nullptr;
     p.pool2 = static_cast<const uint8_t*>(extra_pool->data);
@@ -625,10 +631,11 @@ int fwd_two(const smla_tensor* q, const smla_tensor* kv_pool, const smla_tensor*
   // the combine kernel's LSE-weighted merge is then the softmax over the
   // union of both segments' slots.
   FwdParams p1 = segment_params(q, kv_pool, c1.fp8 ? static_cast<const float*>(kv_scale->data) : nullptr,
-                                indices, c1, plan1, sm_scale, out, lse);
+                                indices, c1, plan1, sm_scale, out, lse, opt);
   p1.part_o = part_o;
   p1.part_lse = part_lse;
-  FwdParams p2 = segment_params(q, extra_pool, scale2, extra_indices, c2, plan2, sm_scale, out, lse);
+  FwdParams p2 = segment_params(q, extra_pool, scale2, extra_indices, c2, plan2, sm_scale, out, lse,
+                                opt);
   p1.q_scale = p2.q_scale = opt ? static_cast<const float*>(opt->q_scale) : nullptr;
   p2.part_o = part_o + int64_t(plan1.splits) * per_split * kDv;
   p2.part_lse = part_lse + int64_t(plan1.splits) * per_split;

@@ -89,6 +89,9 @@ struct FwdParams {
   int32_t page_shift;
   uint32_t page_mask;
   int64_t page_bytes;
+  // CUs of the device: a kernel that keeps one workgroup per CU and streams
+  // its share of the work items launches at most this many workgroups.
+  int32_t persist_cap;
 };
 
 // The output epilogue as a pass of its own over bf16 rows [rows, heads, 512].

@@ -46,8 +46,13 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   static const char* kBadGrid = "launch grid exceeds 2^31 - 1 workgroups";
   static const char* kBadVariant =
       "variant override must be 0, 1, 2 or 3 (2: 64 heads only; 3: 64 heads, fp8 pools only)";
+  static const char* kBadWgs = "workgroups must be >= 0";
   if (num_cus <= 0) num_cus = 256;
   *plan = smla_plan{};
+  if (opt && opt->workgroups < 0) {
+    *err = kBadWgs;
+    return SMLA_ERR_INVALID_ARG;
+  }
 
   int hb = 0;
   if (opt && opt->head_block) {

@@ -234,25 +234,50 @@ prefill_mx_kernel(const FwdParams p) {
   const int hp = wave >> 1, kh = wave & 1;
   const int c32 = lane & 31, h = lane >> 5;
 
-  int64_t work = p.remap ? smla_xcd_work(blockIdx.x, p.grid) : int64_t(blockIdx.x);
-  const int hblk = int(work % p.head_blocks);
-  work /= p.head_blocks;
-  const int split = int(work % p.splits);
-  const int64_t r = work / p.splits;
+  // This workgroup's work items j = blockIdx.x + k G (k < n_items), each a
+  // (row, head block, split). A workgroup walks several items only when the
+  // rows are not split (the launch then has fewer workgroups than items), so
+  // all its items cover the same tiles.
+  const int64_t total = p.grid;
+  const int64_t G = gridDim.x;
+  const int n_items =
+      __builtin_amdgcn_readfirstlane(int((total - int64_t(blockIdx.x) + G - 1) / G));
+  int hblk, split;
+  // Row of item k (and its head block and split); uniform, in scalar
+  // registers. Item numbers are below 2^32 (a grid size).
+  auto item_of = [&](int k, int& hb_o, int& sp_o) -> int64_t {
+    const int64_t j = int64_t(blockIdx.x) + int64_t(k) * G;
+    const uint32_t wk = uint32_t(p.remap ? smla_xcd_work(j, total) : j);
+    const uint32_t hb = uint32_t(p.head_blocks), sp = uint32_t(p.splits);
+    hb_o = __builtin_amdgcn_readfirstlane(int(wk % hb));
+    sp_o = __builtin_amdgcn_readfirstlane(int(wk / hb % sp));
+    return int64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(wk / hb / sp))));
+  };
+  int64_t r = item_of(0, hblk, split);
   float cs_pre = 0.f;
-  if constexpr (EPI) {
-    if (p.epi.pos != nullptr && tid < 64) cs_pre = epi_cs_row(p.epi, r)[tid];
-  }
+  auto load_cs = [&]() {
+    if constexpr (EPI) {
+      if (p.epi.pos != nullptr && tid < 64) cs_pre = epi_cs_row(p.epi, r)[tid];
+    }
+  };
+  load_cs();
 
-  const int head = hblk * 64 + 32 * hp + c32;
-  const bool head_ok = head < p.heads;
+  int head = hblk * 64 + 32 * hp + c32;
+  bool head_ok = head < p.heads;
   const int ntiles = (p.topk + kXTile - 1) / kXTile;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(ntiles, t_begin + p.tiles_per_split);
   const int slot_end = min(p.topk, t_end * kXTile);
 
   // ---- index rows and the tile DMA
-  const i32x4 idx_rsrc = make_rsrc(p.idx + r * p.idx_rs, 0, 4u * uint32_t(slot_end));
+  auto idx_rsrc_of = [&](int64_t row) { return make_rsrc(p.idx + row * p.idx_rs, 0, 4u * uint32_t(slot_end)); };
+  i32x4 idx_rsrc = idx_rsrc_of(r);
+  i32x4 idx_rsrc_next = idx_rsrc;  // the next item's, while the walk streams into it
+  // The next item's q rows (64 heads of a row, contiguous when the heads
+  // are), fetched into the L2 during the walk's last steps: one dword per
+  // 64 bytes. A zero-record resource fetches nothing.
+  const i32x4 null_rsrc = make_rsrc(p.q, 0, 0u);
+  i32x4 q_pf_rsrc = null_rsrc;
   const uint32_t rs = uint32_t(p.pool_rs_bytes);
   const uint32_t records = p.pool_bytes >= uint32_t(DQK) ? (p.pool_bytes - DQK) / rs + 1 : 0u;
   const i32x4 pool_rsrc = make_rsrc(p.pool, rs, records);
@@ -260,11 +285,12 @@ prefill_mx_kernel(const FwdParams p) {
   const uint32_t lds0 = lds_addr(smem);
   const int32_t* const idx_ring = reinterpret_cast<const int32_t*>(smem + C::OFF_IDX);
 
-  // The indices of tile t (64 of them; past slot_end the range check reads
-  // 0) to the index ring; one instruction, issued by wave 0.
-  auto idx_dma = [&](int tt, int t) {
-    if (wave == 0)
-      dma4(idx_rsrc, lds0 + C::OFF_IDX + (tt % kXRing) * kXTile * 4, uint32_t(4 * (t * kXTile + lane)));
+  // The indices of tile t of the row of `rsrc` (64 of them; past slot_end
+  // the range check reads 0) to the index ring at stream position tt; one
+  // instruction. Every wave issues it (the same bytes to the same place), so
+  // that no branch splits the code around it.
+  auto idx_dma = [&](int tt, int t, const i32x4& rsrc) {
+    dma4(rsrc, lds0 + C::OFF_IDX + (tt % kXRing) * kXTile * 4, uint32_t(4 * (t * kXTile + lane)));
   };
   // This lane's slots of a tile (relative to 16 * wave): the DMA slots
   // 8h + k (k < 8; rows 2k + h), the rope slot of rope row lane / 4, the
@@ -272,8 +298,9 @@ prefill_mx_kernel(const FwdParams p) {
   const int rope_slot = 8 * ((lane >> 2) & 1) + ((lane >> 3) & 7);
   int idn[8], idr = -1, idb;
   // The lane's indices of tile t (ring place tt) from the ring; slots past
-  // the split's end read 0 there: mark them invalid; then map slot indices
-  // of a paged pool to rows of page_rows.
+  // the split's end (all of them for a tile past the walk's end) are marked
+  // invalid, with selects rather than a branch; then slot indices of a
+  // paged pool are mapped to rows of page_rows.
   auto read_idx = [&](int tt, int t) {
     const int32_t* ir = idx_ring + (tt % kXRing) * kXTile + 16 * wave;
     const u32x4 a = *reinterpret_cast<const u32x4*>(ir + 8 * h);
@@ -287,7 +314,6 @@ prefill_mx_kernel(const FwdParams p) {
     idb = ir[lane & 15];
     const int base = t * kXTile + 16 * wave;
     if (base + 16 > slot_end) {
-      asm volatile("" ::: "memory");  // a branch, not selects on every tile
 #pragma unroll
       for (int k = 0; k < 8; ++k) idn[k] = base + 8 * h + k < slot_end ? idn[k] : -1;
       if constexpr (ROPE) idr = base + rope_slot < slot_end ? idr : -1;
@@ -304,35 +330,50 @@ prefill_mx_kernel(const FwdParams p) {
     }
   };
   // DMA of the walk's tile tt (indices read) into its ring places, and its
-  // slot flags.
+  // slot flags, in pieces: k < 8 the rows 2k + h of the first 512 columns,
+  // k = 8 the rope columns, k = 9 the flags (every lane writes; lanes
+  // l and l + 16 write the same value to the same place).
   const uint32_t dma_rope = 512u + 16u * uint32_t((lane & 3) ^ ((lane >> 4) & 3));
+  constexpr int kPieces = 10;
+  auto dma_piece = [&](int tt, int k) {
+    if (k < 8) {
+      dma16(pool_rsrc, lds0 + (tt % kXRing) * C::NOPE + 16 * wave * kXRow + 2 * k * kXRow, idn[k],
+            16u * uint32_t((lane & 31) ^ nope_perm(2 * k + h)));
+    } else if (k == 8) {
+      if constexpr (ROPE)
+        dma16(pool_rsrc, lds0 + C::OFF_ROPE + (tt % kXRopeRing) * C::ROPEB + 16 * wave * kXRope,
+              idr, dma_rope);
+    } else {
+      kbias[(tt % kXRing) * kXTile + 16 * wave + (lane & 15)] = idb >= 0 ? 0.f : kNegInf;
+    }
+  };
   auto issue_dma = [&](int tt) {
-    const uint32_t nb = lds0 + (tt % kXRing) * C::NOPE + 16 * wave * kXRow;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      dma16(pool_rsrc, nb + 2 * k * kXRow, idn[k], 16u * uint32_t((lane & 31) ^ nope_perm(2 * k + h)));
-    if constexpr (ROPE)
-      dma16(pool_rsrc, lds0 + C::OFF_ROPE + (tt % kXRopeRing) * C::ROPEB + 16 * wave * kXRope, idr,
-            dma_rope);
-    if (lane < 16) kbias[(tt % kXRing) * kXTile + 16 * wave + lane] = idb >= 0 ? 0.f : kNegInf;
+    for (int k = 0; k < kPieces; ++k) dma_piece(tt, k);
   };
   // A walk's start: the indices of its first four tiles, then (indices
   // landed) the DMAs of the first three. `between` runs after the barrier
   // that lands the indices, before the DMAs.
-  auto start_walk = [&](int nt, auto&& between) {
+  // A walk whose first tiles are already requested (`fresh` false: the
+  // previous item's walk streamed into them) only waits for them.
+  auto start_walk = [&](int nt, bool fresh, auto&& between) {
+    if (fresh) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      if (tt < nt) idx_dma(tt, t_begin + tt);
+      for (int tt = 0; tt < 4; ++tt)
+        if (tt < nt) idx_dma(tt, t_begin + tt, idx_rsrc);
+    }
     sync_tile();
     between();
+    if (fresh) {
 #pragma unroll
-    for (int tt = 0; tt < 3; ++tt) {
-      if (tt < nt) {
-        read_idx(tt, t_begin + tt);
-        issue_dma(tt);  // waits for the read: ring place tt may be refilled after this
+      for (int tt = 0; tt < 3; ++tt) {
+        if (tt < nt) {
+          read_idx(tt, t_begin + tt);
+          issue_dma(tt);  // waits for the read: ring place tt may be refilled after this
+        }
       }
+      if (nt > 4) idx_dma(4, t_begin + 4, idx_rsrc);
     }
-    if (nt > 4) idx_dma(4, t_begin + 4);
   };
 
   // q of this lane's head: k-step st takes columns 64 st + 16h and
@@ -343,8 +384,6 @@ prefill_mx_kernel(const FwdParams p) {
   // compiler's waits for them wait for nothing else.
   i32x8 qhi[NSTEP], qlo[NSTEP];
   int sb_hi = kE8One, sb_lo = kE8One;
-  const int hq = head_ok ? head : p.heads - 1;  // a masked head reads a real one, scaled by 0
-  const int64_t qp = r * p.q_rs + int64_t(hq) * p.q_hs;
   auto q_col = [&](int st, int d) { return 64 * st + 32 * d + 16 * h; };
   auto q_exponent = [&](float amax) {
     amax = fmaxf(amax, __shfl_xor(amax, 32));
@@ -368,7 +407,9 @@ prefill_mx_kernel(const FwdParams p) {
     qhi[st] = pack8(hw);
     qlo[st] = pack8(lw);
   };
-  auto start_first_walk = [&](int nt) {
+  auto start_first_walk = [&](int nt, bool fresh) {
+    const int hq = head_ok ? head : p.heads - 1;  // a masked head reads a real one, scaled by 0
+    const int64_t qp = r * p.q_rs + int64_t(hq) * p.q_hs;
     if (p.q_fp8) {
       u32x4 raw[NSTEP][2];
 #pragma unroll
@@ -378,7 +419,7 @@ prefill_mx_kernel(const FwdParams p) {
           raw[st][d] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + qp +
                                                        q_col(st, d));
       float sc = 0.f;
-      start_walk(nt, [&]() {
+      start_walk(nt, fresh, [&]() {
         float amax = 0.f;
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st)
@@ -419,7 +460,7 @@ prefill_mx_kernel(const FwdParams p) {
           for (int hf = 0; hf < 2; ++hf)
             raw[st][d][hf] = *reinterpret_cast<const u32x4*>(p.q + qp + q_col(st, d) + 8 * hf);
       float sc = 0.f;
-      start_walk(nt, [&]() {
+      start_walk(nt, fresh, [&]() {
         float amax = 0.f;
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st)
@@ -501,18 +542,24 @@ prefill_mx_kernel(const FwdParams p) {
   // kXMaxDrift above the pair's first valid tile's maximum) starts from the
   // first walk's final references, which no later score exceeds by
   // 2^kXLimit.
-  auto walk = [&](bool first) {
+  // Walks carry one stream of tiles through the rings: gbase is the stream
+  // position of a walk's first tile. A streaming walk (`stream`) requests,
+  // in its last steps, the indices and first tiles of the next item's walk
+  // instead of tiles past its end.
+  const int nt = t_end - t_begin;
+  int gbase = 0;
+  auto walk = [&](bool first, bool fresh, bool stream) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] = floatx16{};
     l_run = 0.f;
-    const int nt = t_end - t_begin;
     if (nt <= 0) return;
     // start: the first tiles requested (and, on the first walk, q split
     // while they land)
+    if (fresh) gbase = 0;
     if (first)
-      start_first_walk(nt);
+      start_first_walk(nt, fresh);
     else
-      start_walk(nt, [&]() {});
+      start_walk(nt, true, [&]() {});
     sync_tile();
 
     floatx16 s_cur = floatx16{}, s_next;
@@ -520,7 +567,7 @@ prefill_mx_kernel(const FwdParams p) {
     for (int st = 0; st < NSTEP; ++st) {
       u32x4 kf[2];
 #pragma unroll
-      for (int d = 0; d < 2; ++d) kf[d] = kread(0, st, d);
+      for (int d = 0; d < 2; ++d) kf[d] = kread(gbase, st, d);
       kstep(s_cur, st, kf);
     }
     float nm = m_w == kNegInf ? 0.f : -m_w;
@@ -533,9 +580,10 @@ prefill_mx_kernel(const FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) bn[i / 4][i % 4] = b[i / 4][i % 4] + nm;
     };
-    make_bn(0);
+    make_bn(gbase);
     for (int tt = 0; tt < nt; ++tt) {
-      const int par = tt & 1;
+      const int g = gbase + tt;  // stream position: ring places
+      const int par = g & 1;
       const bool has_next = tt + 1 < nt;
       float xmax, lt;
       uint32_t phi[4], plo[4];
@@ -601,7 +649,7 @@ prefill_mx_kernel(const FwdParams p) {
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int d = 0; d < 2; ++d) kr[st][d] = kread(tt + 1, st, d);
+          for (int d = 0; d < 2; ++d) kr[st][d] = kread(g + 1, st, d);
         // the first two stages while the fragments arrive
         {
           int sst, g;
@@ -619,7 +667,7 @@ prefill_mx_kernel(const FwdParams p) {
           for (int term = 0; term < 2; ++term) {
             s_next = mx32(a, term ? qlo[st] : qhi[st], s_next, term ? sb_lo : sb_hi);
             __builtin_amdgcn_sched_barrier(0);
-            if (st + 2 < NSTEP) kr[(st + 2) % 3][term] = kread(tt + 1, st + 2, term);
+            if (st + 2 < NSTEP) kr[(st + 2) % 3][term] = kread(g + 1, st + 2, term);
             const int di = 2 * st + term;
 #pragma unroll
             for (int j = 2; j < 20; ++j)
@@ -634,6 +682,9 @@ prefill_mx_kernel(const FwdParams p) {
         }
       } else {
         softmax();
+        // the next tile's last k-step below runs on zeros (its result is
+        // not used)
+        kr[(NSTEP - 1) % 3][0] = kr[(NSTEP - 1) % 3][1] = u32x4{};
       }
       // computed here, before the rare-path branch
       asm volatile("" :: "v"(phi[0]), "v"(phi[1]), "v"(phi[2]), "v"(phi[3]), "v"(plo[0]),
@@ -680,27 +731,41 @@ prefill_mx_kernel(const FwdParams p) {
         m_blk = xm[(par * kXWaves + 2 * hp + h) * 32 + c32];           // half h's
         m_other = xm[(par * kXWaves + 2 * hp + (kh ^ 1)) * 32 + c32];  // the partner's
       }
-      if (tt + 3 < nt) read_idx(tt + 3, t_begin + tt + 3);
-      if (has_next) kstep(s_next, NSTEP - 1, kr[(NSTEP - 1) % 3]);
-      if (tt + 3 < nt) issue_dma(tt + 3);
-      if (tt + 5 < nt) idx_dma(tt + 5, t_begin + tt + 5);
+      // The indices of tile tt + 3, or past the walk's end the next item's
+      // first tiles when streaming (else all invalid: the DMAs write zeros
+      // to ring places that are free); tile tt + 5's indices the same way.
+      const int t3 = tt + 3 < nt ? t_begin + tt + 3 : (stream ? t_begin + tt + 3 - nt : t_end);
+      const bool x5 = tt + 5 >= nt;
+      const int t5 = !x5 ? t_begin + tt + 5 : (stream ? t_begin + tt + 5 - nt : t_end);
+      read_idx(g + 3, t3);
+      // the next item's q into the L2: 256 64-byte lines a step over the
+      // five steps before the last. The dwords land in the slot flags of
+      // tile tt's ring place, which were read a step ago and are written
+      // next after the following barrier (tile tt + 4's).
+      const int pf = tt - (nt - 6);
+      const bool pf_on = stream && pf >= 0 && pf < 5;
+      const i32x4 pf_rsrc = pf_on ? q_pf_rsrc : null_rsrc;
+      const uint32_t pf_off = 64u * uint32_t((pf_on ? pf : 0) * 256 + 64 * wave + lane);
 
-      if (m_o == kNegInf) m_o = fmaxf(m_w, m_other);  // the pair's first valid tile
-      float d_blk = 0.f, d_own = 0.f;
-      if (m_o != kNegInf) {
-        redo |= int((m_blk - m_o > kXMaxDrift) || (m_w - m_o > kXMaxDrift));
-        d_blk = fminf(fmaxf(m_blk - m_o, kXMinDrift), kXMaxDrift);
-        d_own = fminf(fmaxf(m_w - m_o, kXMinDrift), kXMaxDrift);
-      }
+      const float m_first = fmaxf(m_w, m_other);
+      m_o = m_o == kNegInf ? m_first : m_o;  // the pair's first valid tile
+      const bool ref = m_o != kNegInf;
+      redo |= int(ref && ((m_blk - m_o > kXMaxDrift) || (m_w - m_o > kXMaxDrift)));
+      const float d_blk = ref ? fminf(fmaxf(m_blk - m_o, kXMinDrift), kXMaxDrift) : 0.f;
+      const float d_own = ref ? fminf(fmaxf(m_w - m_o, kXMinDrift), kXMaxDrift) : 0.f;
       l_run += __builtin_ldexpf(lt, int(d_own));
       const int sb_ph = kE8One + int(d_blk), sb_pl = kE8One - 4 + int(d_blk);
       const i32x8 ph = cat(xh0, xh1), pl = cat(xl0, xl1);
 
-      // ---- O^T += V^T P^T over this wave's 8 column blocks; each value
-      // fragment feeds both terms of P and is read two blocks ahead. The
-      // next step's carried reads go out before the last two blocks.
+      // ---- the next tile's last k-step, then O^T += V^T P^T over this
+      // wave's 8 column blocks; each value fragment feeds both terms of P
+      // and is read two blocks ahead. One piece of tile tt + 3's DMA (then
+      // tile tt + 5's indices) goes out after each of the first dots, so
+      // that the address unit never holds the wave; the next step's slot
+      // flags are read before the last two blocks. No branch in this
+      // stretch: the order below is the order issued.
       {
-        const uint8_t* vb = smem + (tt % kXRing) * C::NOPE + vro;
+        const uint8_t* vb = smem + (g % kXRing) * C::NOPE + vro;
         auto vread = [&](int m, int v) -> u32x2 {
           return lds_read_tr8(vb + 16 * ((2 * m + ve) ^ vperm) +
                               (32 * (v >> 1) + 16 * (v & 1)) * kXRow);
@@ -711,6 +776,9 @@ prefill_mx_kernel(const FwdParams p) {
         for (int m = 0; m < VR - 1; ++m)
 #pragma unroll
           for (int v = 0; v < 4; ++v) vr[m][v] = vread(m, v);
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(s_next, NSTEP - 1, kr[(NSTEP - 1) % 3]);
+        asm volatile("" : "+a"(s_next));  // issued here, ahead of the DMAs
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -726,7 +794,11 @@ prefill_mx_kernel(const FwdParams p) {
               vr[mn % VR][2 * term] = vread(mn, 2 * term);
               vr[mn % VR][2 * term + 1] = vread(mn, 2 * term + 1);
             }
-            if (m == 6 && term == 0 && has_next) make_bn(tt + 1);
+            const int j = 2 * m + term;
+            if (j < kPieces) dma_piece(g + 3, j);
+            if (j == kPieces) idx_dma(g + 5, t5, x5 ? idx_rsrc_next : idx_rsrc);
+            if (j == 11) dma4(pf_rsrc, lds0 + C::OFF_BIAS + (g % kXRing) * kXTile * 4, pf_off);
+            if (j == 12) make_bn(g + 1);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -741,64 +813,118 @@ prefill_mx_kernel(const FwdParams p) {
       for (int st = 0; st < 7; ++st) asm volatile("" : "+a"(qhi[st]), "+a"(qlo[st]));
       s_cur = s_next;
     }
+    gbase += nt;
+    // a walk that does not stream: the DMAs past its end have landed before
+    // the ring is reused or the workgroup ends
+    if (!stream) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-#pragma clang loop unroll(disable)
-  for (int pass = 0; pass < 2; ++pass) {
-    walk(pass == 0);
-    if (pass == 1 || __syncthreads_or(redo) == 0) break;
-    // the second walk starts from the pair's final weight references
-    const int par = (t_end - t_begin - 1) & 1;
-    m_o = fmaxf(m_w, xm[(par * kXWaves + (wave ^ 1)) * 32 + c32]);
-    __syncthreads();  // every wave has read them before the walk reuses the area
-  }
-
-  // ---- epilogue: the head's row sum over both lane halves and both waves
-  // of the pair; normalise; store.
-  const float l_lane = l_run + __shfl_xor(l_run, 32);
-  xl[wave * 32 + c32] = l_lane;
-  if constexpr (EPI) {
-    if (tid < 64) epi_cs[tid] = cs_pre;
-  }
-  __syncthreads();
-  const float lt_tot = l_lane + xl[(wave ^ 1) * 32 + c32];
-  if (!head_ok) return;
-  const float inv = lt_tot > 0.f ? kv_scale / lt_tot : 0.f;
-  const bool split_mode = p.part_o != nullptr;
-  const int colh = 256 * kh + 4 * h;  // column of register 0 of block 0
-  if (EPI && !split_mode) {
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      float v[4][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[j][u] = o[m][4 * j + u] * inv;
-      epi_store_c32x4(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, r, head, colh + 32 * m, v);
+  // Streaming needs the next item's indices within the walk's last five
+  // steps, so a walk of fewer tiles starts every item afresh.
+  const bool can_stream = nt >= 5;
+  bool prefetched = false;  // this item's first tiles are in the ring
+  for (int k = 0; k < n_items; ++k) {
+    if (k > 0) {
+      r = item_of(k, hblk, split);
+      head = hblk * 64 + 32 * hp + c32;
+      head_ok = head < p.heads;
+      idx_rsrc = idx_rsrc_of(r);
+      load_cs();
     }
-  } else {
+    const bool more = can_stream && k + 1 < n_items;
+    if (more) {
+      int hb1, sp1;
+      const int64_t r1 = item_of(k + 1, hb1, sp1);
+      idx_rsrc_next = idx_rsrc_of(r1);
+      const int64_t es = p.q_fp8 ? 1 : 2;
+      const int64_t nh1 = min(64, p.heads - 64 * hb1);
+      const int64_t span = min(nh1 * p.q_hs * es, int64_t(2 * 64 * DQK) * es);
+      q_pf_rsrc = make_rsrc(reinterpret_cast<const uint8_t*>(p.q) + (r1 * p.q_rs + 64 * hb1 * p.q_hs) * es,
+                            0, uint32_t(span));
+    }
+    m_o = kNegInf;
+    m_w = kNegInf;
+    redo = 0;
+    bool streamed = false;
+#pragma clang loop unroll(disable)
+    for (int pass = 0; pass < 2; ++pass) {
+      walk(pass == 0, pass == 1 || !prefetched, pass == 0 && more);
+      streamed = pass == 0 && more;
+      if (pass == 1 || __syncthreads_or(redo) == 0) break;
+      // the second walk starts from the pair's final weight references,
+      // after the stream into the next item has drained (its tiles are
+      // requested again)
+      const int par = (gbase - 1) & 1;
+      m_o = fmaxf(m_w, xm[(par * kXWaves + (wave ^ 1)) * 32 + c32]);
+      sync_tile();  // every wave has read them before the walk reuses the area
+    }
+    prefetched = streamed;
+
+    // ---- the item's end: the head's row sum over both lane halves and
+    // both waves of the pair; normalise; store.
+    const float l_lane = l_run + __shfl_xor(l_run, 32);
+    xl[wave * 32 + c32] = l_lane;
+    if constexpr (EPI) {
+      if (tid < 64) epi_cs[tid] = cs_pre;
+    }
+    // the LDS traffic only: the stream's DMAs stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const float lt_tot = l_lane + xl[(wave ^ 1) * 32 + c32];
+    const int64_t r_st = r;
+    const int head_st = head, split_st = split;
+    if (head_ok) {
+      const float inv = lt_tot > 0.f ? kv_scale / lt_tot : 0.f;
+      const bool split_mode = p.part_o != nullptr;
+      const int colh = 256 * kh + 4 * h;  // column of register 0 of block 0
+      if (EPI && !split_mode) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 8; ++m) {
+          float v[4][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = colh + 32 * m + 8 * j;
-        const float a0 = o[m][4 * j] * inv, a1 = o[m][4 * j + 1] * inv;
-        const float a2 = o[m][4 * j + 2] * inv, a3 = o[m][4 * j + 3] * inv;
-        if (!split_mode) {
-          *reinterpret_cast<u32x2*>(p.out + r * p.out_rs + int64_t(head) * p.out_hs + col) =
-              u32x2{pack_bf16(a0, a1), pack_bf16(a2, a3)};
-        } else {
-          *reinterpret_cast<floatx4*>(
-              p.part_o + ((int64_t(split) * p.rows + r) * p.heads + head) * kDv + col) =
-              floatx4{a0, a1, a2, a3};
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[j][u] = o[m][4 * j + u] * inv;
+          epi_store_c32x4(p.epi, p.epi.pos != nullptr ? epi_cs : nullptr, r_st, head_st, colh + 32 * m,
+                          v);
         }
+      } else if (!split_mode) {
+        // bf16 rows, 16 contiguous columns per store: lane h and its
+        // partner lane (h flipped) trade half of each 32-column block, so
+        // that h = 0 holds columns 0..15 of the block and h = 1 columns
+        // 16..31.
+        uint16_t* const orow = p.out + r_st * p.out_rs + int64_t(head_st) * p.out_hs + 256 * kh + 16 * h;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          uint32_t w[8];  // columns 8j + 4h + (0..3) of the block, as bf16 pairs
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = pack_bf16(o[m][2 * i] * inv, o[m][2 * i + 1] * inv);
+          uint32_t x[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = __shfl_xor(h ? w[i] : w[4 + i], 32);
+          const u32x4 lo = h ? u32x4{x[0], x[1], w[4], w[5]} : u32x4{w[0], w[1], x[0], x[1]};
+          const u32x4 hi = h ? u32x4{x[2], x[3], w[6], w[7]} : u32x4{w[2], w[3], x[2], x[3]};
+          *reinterpret_cast<u32x4*>(orow + 32 * m) = lo;
+          *reinterpret_cast<u32x4*>(orow + 32 * m + 8) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int col = colh + 32 * m + 8 * j;
+            *reinterpret_cast<floatx4*>(
+                p.part_o + ((int64_t(split_st) * p.rows + r_st) * p.heads + head_st) * kDv + col) =
+                floatx4{o[m][4 * j] * inv, o[m][4 * j + 1] * inv, o[m][4 * j + 2] * inv,
+                        o[m][4 * j + 3] * inv};
+          }
       }
-  }
-  if (kh == 0 && h == 0) {
-    const float lse = lt_tot > 0.f ? (m_o + __log2f(lt_tot)) * kLn2 : kNegInf;
-    if (!split_mode)
-      p.lse[r * p.lse_rs + int64_t(head) * p.lse_hs] = lse;
-    else
-      p.part_lse[(int64_t(split) * p.rows + r) * p.heads + head] = lse;
+      if (kh == 0 && h == 0) {
+        const float lse = lt_tot > 0.f ? (m_o + __log2f(lt_tot)) * kLn2 : kNegInf;
+        if (!split_mode)
+          p.lse[r_st * p.lse_rs + int64_t(head_st) * p.lse_hs] = lse;
+        else
+          p.part_lse[(int64_t(split_st) * p.rows + r_st) * p.heads + head_st] = lse;
+      }
+    }
   }
 }
 
@@ -829,7 +955,14 @@ int launch_prefill_mx(const FwdParams& p, int dqk, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool epi = epi_active(p.epi) && p.part_o == nullptr;
   const bool paged = p.page_shift != 31;
-  const dim3 grid(uint32_t(p.grid)), block(kXWaves * 64);
+  // Rows not split: one workgroup per CU (rounded down to whole rounds of
+  // the 8 XCDs, so a workgroup's items stay on its XCD) walks its share of
+  // the work items as one stream of tiles. Split rows: one workgroup per
+  // item.
+  int64_t wgs = p.grid;
+  if (p.splits == 1 && p.persist_cap > 0 && p.grid > p.persist_cap)
+    wgs = p.persist_cap >= 8 ? p.persist_cap / 8 * 8 : p.persist_cap;
+  const dim3 grid{uint32_t(wgs)}, block{uint32_t(kXWaves * 64)};
   if (dqk == 576)
     paged ? launch_mx<576, true>(p, epi, grid, block, st) : launch_mx<576, false>(p, epi, grid, block, st);
   else if (dqk == 512)

@@ -472,6 +472,15 @@ def test_plan_rejects_unknown_variants():
     assert _plan(64, 16, variant=1)["variant"] == 1
 
 
+def test_plan_rejects_negative_workgroups():
+    """The workgroup cap of kernels that walk several items per workgroup:
+    0 = one per compute unit, positive = at most that many, negative is an
+    error (the plan itself does not depend on it)."""
+    with pytest.raises(_lib.SparseMLAError):
+        _plan(8192, 64, variant=3, workgroups=-1)
+    assert _plan(8192, 64, variant=3, workgroups=3) == _plan(8192, 64, variant=3)
+
+
 def test_plan_fp8_dot_kernel_eligibility():
     """Variant 3 (the fp8-dot 64-head kernel) addresses pool rows through a
     structured buffer: 64-head blocks over fp8 pools only, row pitch under
