@@ -264,8 +264,15 @@ def time_indexer(name, steps, warmup):
     }
     res = {}
     for key, call in calls.items():
-        for _ in range(warmup):
+        # warm until the device clock has settled: at least `warmup` calls
+        # and 25 ms of back-to-back work
+        t0 = time.perf_counter()
+        n = 0
+        while n < warmup or time.perf_counter() - t0 < 0.025:
             call()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
         times = []
         for _ in range(steps):
             flush.fill_(1.0)

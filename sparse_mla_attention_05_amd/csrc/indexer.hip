@@ -14,16 +14,18 @@
 // 16 heads x 16 keys over all 128 dims (A = Q rows, B = K rows, the same
 // lane->k mapping on both sides). A lane's accumulator holds heads 4g..4g+3 of one key; relu
 // and the head weight are applied there, the four lanes g of a key are summed
-// by two xor shuffles arranged as a butterfly over the wave's four rows
+// by lane-row swaps arranged as a transpose over the wave's four rows
 // (afterwards lane g owns row g), and the key's scale is applied after the
 // head sum. Tiles outside every row's window are not computed; with `clean`
 // the kernel writes -inf there itself.
 //
-// Top-k kernel. One workgroup per row: a three-level radix select (11, 11
-// and 10 bits) on the order-preserving integer image of the fp32 logits
-// finds the k-th largest value T; a last pass writes, in ascending index
-// order, every key above T and the lowest-index keys equal to T (block-wide
-// prefix sums of two ballots per 1024 keys). Only the window is read.
+// Top-k kernel. One workgroup per row: a radix select (12, 10 and 10 bits)
+// on the order-preserving integer image of the fp32 logits finds the k-th
+// largest value T, and the output holds, in ascending index order, every
+// key above T and the lowest-index keys equal to T. The first level reads
+// the window; the keys in and above its chosen bin are then compacted into
+// LDS by a second read when they fit, and the other levels and the output
+// work there. Only the window is read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -199,12 +201,20 @@ ix_logits_kernel(const IxParams p) {
         }
         part[j] = a + b;
       }
-      // Butterfly over the lane groups g (bits 4, 5): afterwards lane g holds
-      // row g's sum over all 32 heads for key `key`.
-      const bool b0s = (g & 1) != 0, b1s = (g & 2) != 0;
-      const float qa0 = (b0s ? part[1] : part[0]) + __shfl_xor(b0s ? part[0] : part[1], 16);
-      const float qb0 = (b0s ? part[3] : part[2]) + __shfl_xor(b0s ? part[2] : part[3], 16);
-      const float tot = (b1s ? qb0 : qa0) + __shfl_xor(b1s ? qa0 : qb0, 32);
+      // Transposing sums over the lane groups g (bits 4, 5), by row swaps
+      // between register pairs: the 16-lane swap leaves group g rows
+      // (g & 1) and 2 + (g & 1) summed over the group pair {g & 2, (g & 2) + 1},
+      // the 32-lane swap then adds the other pair, so that lane g holds row
+      // g's sum over all 32 heads for key `key`.
+      const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]),
+                                                        __float_as_uint(part[1]), false, false);
+      const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[2]),
+                                                        __float_as_uint(part[3]), false, false);
+      const float q01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+      const float q23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+      const auto s4 = __builtin_amdgcn_permlane32_swap(__float_as_uint(q01), __float_as_uint(q23),
+                                                       false, false);
+      const float tot = __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
       const int n = n0 + key;
       const bool inside = n >= my_lo && n < my_hi;
       const bool write = n < t_stop && (inside || p.clean != 0);
@@ -241,7 +251,11 @@ ix_logits_kernel(const IxParams p) {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kTkUnroll = 8;  // keys per thread in flight in a histogram pass
+constexpr int kTkPer = 8;                       // contiguous keys per thread in a round
+constexpr int kTkRound = kTkThreads * kTkPer;   // keys per round
+constexpr int kTkBits0 = 12;                    // bits of the first radix level
+constexpr int kTkShift0 = 32 - kTkBits0;
+constexpr int kTkCap = 8192;                    // candidates kept in LDS
 
 // Order-preserving integer image of an fp32 value (-0 taken as +0, so the two
 // zeros tie as they do as numbers).
@@ -251,31 +265,67 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive count of the items after this thread's in thread order (a
-// suffix sum), over the whole block; sh holds kTkWaves words.
-__device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, uint32_t* sh) {
+// Exclusive prefix sum of v over the block in thread order, and the block's
+// total; sh holds kTkWaves words. Every thread of the block calls it.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;  // inclusive suffix within the wave
+  uint32_t x = v;  // inclusive prefix within the wave
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_down(x, d);
-    if (lane + d < 64) x += y;
+    const uint32_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  if (lane == 0) sh[wave] = x;
+  if (lane == 63) sh[wave] = x;
   __syncthreads();
-  uint32_t above = 0;
-  for (int w = wave + 1; w < kTkWaves; ++w) above += sh[w];
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const uint32_t t = sh[w];
+    before += w < wave ? t : 0u;
+    total += t;
+  }
   __syncthreads();
-  return x - v + above;
+  return x - v + before;
 }
 
-__global__ void __launch_bounds__(kTkThreads) topk_kernel(const TopkParams p) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t scan[kTkWaves];
-  __shared__ uint32_t pick[2];  // bin, count above it
-  __shared__ uint32_t cnt[2][2][kTkWaves];
+// Bin of a radix level holding the `need`-th largest key: `h` are this
+// thread's `per` consecutive bins starting at per * tid (of `bins`); writes
+// (bin, count in the bins above it) to pick.
+__device__ __forceinline__ void pick_bin(const uint32_t* h, int per, uint32_t need, uint32_t* sh,
+                                         uint32_t* pick) {
+  uint32_t mine = 0;
+  for (int i = 0; i < per; ++i) mine += h[i];
+  uint32_t total;
+  const uint32_t before = block_excl_scan(mine, sh, total);
+  // keys in bins above this thread's: total - before - mine
+  uint32_t above = total - before - mine;
+  for (int i = per - 1; i >= 0; --i) {
+    if (above < need && above + h[i] >= need) {
+      pick[0] = uint32_t(per * threadIdx.x + i);
+      pick[1] = above;
+    }
+    above += h[i];
+  }
+  __syncthreads();
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One workgroup per row. A 12-bit histogram of the order keys over the
+// window (one read) fixes the bin of the k-th largest key; when that bin and
+// the ones above hold at most kTkCap keys (the usual case: logits are
+// continuous), a second read compacts them into LDS in index order and the
+// rest (two 10-bit levels and the output) runs on those. Otherwise two more
+// full-window levels and an output read finish the select. Keys above the
+// k-th largest value T are written, then the lowest-index keys equal to T,
+// in ascending index order. Only the window is read.
+__global__ void __launch_bounds__(kTkThreads) topk_kernel(const TopkParams p) {
+  __shared__ uint32_t cand_u[kTkCap];  // the first level's histogram, then candidate keys
+  __shared__ int32_t cand_n[kTkCap];   // candidate indices
+  __shared__ uint32_t hist[1024];      // the 10-bit levels
+  __shared__ uint32_t scan[kTkWaves];
+  __shared__ uint32_t pick[2];         // bin, count above it
+
+  const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
   const float* row = p.logits + r * p.l_rs;
   int32_t* out = p.out + r * p.o_rs;
@@ -287,87 +337,168 @@ __global__ void __launch_bounds__(kTkThreads) topk_kernel(const TopkParams p) {
     for (int i = tid; i < p.k; i += kTkThreads) out[i] = i < len ? lo + i : -1;
     return;
   }
+  // Keys n0 .. n0 + 7 of a round (n0 a multiple of 8: two 16-byte loads),
+  // through a buffer resource that ends at the window's end (keys past it
+  // read 0); keys outside [lo, hi) are masked where they are used.
+  const __amdgpu_buffer_rsrc_t rr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, uint32_t(4 * hi), kIxBufferWord3);
+  auto load8 = [&](int n0, uint32_t (&u)[kTkPer]) {
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, 4u * uint32_t(n0), 0, 0));
+    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, 4u * uint32_t(n0) + 16u, 0, 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u[j] = order_key(__uint_as_float(a[j]));
+      u[4 + j] = order_key(__uint_as_float(b[j]));
+    }
+  };
+  const int lo8 = lo & ~(kTkPer - 1);  // rounds start 32-byte aligned
+  auto in = [&](int n) { return n >= lo && n < hi; };
 
-  // ---- radix select: three levels of 11, 11 and 10 bits.
-  uint32_t prefix = 0;     // selected high bits so far
-  uint32_t need = p.k;     // how many of the candidates still to take
-  constexpr int kShift[3] = {21, 10, 0};
-  constexpr int kBins[3] = {2048, 2048, 1024};
+  // ---- level 0: 12-bit histogram over the window
+  uint32_t* const hist0 = cand_u;
+  for (int i = tid; i < (1 << kTkBits0); i += kTkThreads) hist0[i] = 0u;
+  __syncthreads();
+  for (int base = lo8; base < hi; base += kTkRound) {
+    const int n0 = base + kTkPer * tid;
+    uint32_t u[kTkPer];
+    load8(n0, u);
 #pragma unroll
-  for (int lv = 0; lv < 3; ++lv) {
-    const int sh = kShift[lv];
-    const int bins = kBins[lv];
-    for (int i = tid; i < 2048; i += kTkThreads) hist[i] = 0u;
+    for (int j = 0; j < kTkPer; ++j)
+      if (in(n0 + j)) atomicAdd(&hist0[u[j] >> kTkShift0], 1u);
+  }
+  __syncthreads();
+  constexpr int kPer0 = (1 << kTkBits0) / kTkThreads;
+  uint32_t h0[kPer0];
+#pragma unroll
+  for (int i = 0; i < kPer0; ++i) h0[i] = hist0[kPer0 * tid + i];
+  pick_bin(h0, kPer0, uint32_t(p.k), scan, pick);
+  const uint32_t b0 = pick[0];
+  uint32_t need = uint32_t(p.k) - pick[1];        // keys of bin b0 still to take
+  const uint32_t ncand = pick[1] + hist0[b0];     // keys in bins >= b0
+  __syncthreads();
+
+  uint32_t prefix = b0;
+  if (ncand <= uint32_t(kTkCap)) {
+    // ---- candidates: the keys in bins >= b0, compacted in index order
+    uint32_t pos = 0;
+    for (int base = lo8; base < hi; base += kTkRound) {
+      const int n0 = base + kTkPer * tid;
+      uint32_t u[kTkPer];
+      load8(n0, u);
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < kTkPer; ++j) c += (in(n0 + j) && (u[j] >> kTkShift0) >= b0) ? 1u : 0u;
+      uint32_t total;
+      uint32_t at = pos + block_excl_scan(c, scan, total);
+#pragma unroll
+      for (int j = 0; j < kTkPer; ++j)
+        if (in(n0 + j) && (u[j] >> kTkShift0) >= b0) {
+          cand_u[at] = u[j];
+          cand_n[at] = n0 + j;
+          ++at;
+        }
+      pos += total;
+    }
     __syncthreads();
-    const int hs = lv == 0 ? 32 : kShift[lv - 1];  // candidates match `prefix` above bit hs
-    // kTkUnroll keys per thread in flight: the loads are unconditional (the
-    // key index is clamped into the window) and masked where they are used;
-    // one key per iteration would wait on each load in turn.
-    for (int64_t n0 = lo + tid; n0 < hi; n0 += kTkUnroll * kTkThreads) {
-      uint32_t u[kTkUnroll];
+    // ---- two 10-bit levels over the candidates of bin b0
 #pragma unroll
-      for (int j = 0; j < kTkUnroll; ++j)
-        u[j] = order_key(row[min(n0 + int64_t(j) * kTkThreads, int64_t(hi) - 1)]);
-#pragma unroll
-      for (int j = 0; j < kTkUnroll; ++j) {
-        const bool in = n0 + int64_t(j) * kTkThreads < hi;
-        if (in && (lv == 0 || (u[j] >> hs) == prefix))
-          atomicAdd(&hist[(u[j] >> sh) & uint32_t(bins - 1)], 1u);
+    for (int lv = 0; lv < 2; ++lv) {
+      const int sh = lv == 0 ? 10 : 0;
+      hist[tid] = 0u;
+      __syncthreads();
+      for (int i = tid; i < int(ncand); i += kTkThreads) {
+        const uint32_t u = cand_u[i];
+        if ((u >> (sh + 10)) == prefix) atomicAdd(&hist[(u >> sh) & 1023u], 1u);
       }
+      __syncthreads();
+      uint32_t h1[1] = {hist[tid]};
+      pick_bin(h1, 1, need, scan, pick);
+      prefix = (prefix << 10) | pick[0];
+      need -= pick[1];
+      __syncthreads();
+    }
+    const uint32_t T = prefix;
+    // ---- output: candidates above T, then the first `need` equal to it,
+    // in index order (thread t takes candidates 8t .. 8t + 7)
+    uint32_t u[kTkPer];
+    int32_t nn[kTkPer];
+    uint32_t ce = 0;
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) {
+      const int i = kTkPer * tid + j;
+      u[j] = i < int(ncand) ? cand_u[i] : 0u;
+      nn[j] = i < int(ncand) ? cand_n[i] : 0;
+      ce += (i < int(ncand) && u[j] == T) ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t eq_before = block_excl_scan(ce, scan, tot);
+    bool sel[kTkPer];
+    uint32_t cs = 0;
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) {
+      const int i = kTkPer * tid + j;
+      const bool eq = i < int(ncand) && u[j] == T;
+      sel[j] = i < int(ncand) && (u[j] > T || (eq && eq_before < need));
+      eq_before += eq ? 1u : 0u;
+      cs += sel[j] ? 1u : 0u;
+    }
+    uint32_t at = block_excl_scan(cs, scan, tot);
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j)
+      if (sel[j]) out[at++] = nn[j];
+    return;
+  }
+
+  // ---- many keys in and above the k-th key's bin: two more levels over the
+  // whole window, then the output read
+#pragma unroll
+  for (int lv = 0; lv < 2; ++lv) {
+    const int sh = lv == 0 ? 10 : 0;
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int base = lo8; base < hi; base += kTkRound) {
+      const int n0 = base + kTkPer * tid;
+      uint32_t u[kTkPer];
+      load8(n0, u);
+#pragma unroll
+      for (int j = 0; j < kTkPer; ++j)
+        if (in(n0 + j) && (u[j] >> (sh + 10)) == prefix) atomicAdd(&hist[(u[j] >> sh) & 1023u], 1u);
     }
     __syncthreads();
-    // thread t owns bins 2t (lower) and 2t + 1
-    const uint32_t h0 = 2 * tid < bins ? hist[2 * tid] : 0u;
-    const uint32_t h1 = 2 * tid + 1 < bins ? hist[2 * tid + 1] : 0u;
-    const uint32_t above1 = block_suffix_excl(h0 + h1, scan);  // count in bins > 2t + 1
-    if (above1 < need && above1 + h1 >= need) {
-      pick[0] = 2 * tid + 1;
-      pick[1] = above1;
-    } else if (above1 + h1 < need && above1 + h1 + h0 >= need) {
-      pick[0] = 2 * tid;
-      pick[1] = above1 + h1;
-    }
-    __syncthreads();
-    prefix = (prefix << (lv == 0 ? 11 : (lv == 1 ? 11 : 10))) | pick[0];
+    uint32_t h1[1] = {hist[tid]};
+    pick_bin(h1, 1, need, scan, pick);
+    prefix = (prefix << 10) | pick[0];
     need -= pick[1];
     __syncthreads();
   }
-  const uint32_t T = prefix;  // the k-th largest key; `need` keys equal to it are taken
-
-  // ---- output in ascending index order: 1024 keys per round.
+  const uint32_t T = prefix;
   uint32_t eq_base = 0, sel_base = 0;
-  // Each round's keys are loaded one round ahead (clamped into the window).
-  float cur = row[min(lo + tid, hi - 1)];
-  for (int base = lo, round = 0; base < hi; base += kTkThreads, ++round) {
-    const int n = base + tid;
-    const float nxt = row[min(int64_t(n) + kTkThreads, int64_t(hi) - 1)];
-    const uint32_t u = n < hi ? order_key(cur) : 0u;
-    cur = nxt;
-    const bool eq = n < hi && u == T;
-    const uint64_t eqm = __ballot(eq);
-    const uint32_t eq_in_wave = __popcll(eqm & ((uint64_t(1) << lane) - 1));
-    uint32_t (*c)[kTkWaves] = cnt[round & 1];
-    if (lane == 0) c[0][wave] = __popcll(eqm);
-    __syncthreads();
-    uint32_t eq_before = eq_base, eq_round = 0;
-    for (int w = 0; w < kTkWaves; ++w) {
-      const uint32_t x = c[0][w];
-      if (w < wave) eq_before += x;
-      eq_round += x;
+  for (int base = lo8; base < hi; base += kTkRound) {
+    const int n0 = base + kTkPer * tid;
+    uint32_t u[kTkPer];
+    load8(n0, u);
+    uint32_t ce = 0;
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) ce += (in(n0 + j) && u[j] == T) ? 1u : 0u;
+    uint32_t tot_e;
+    uint32_t eq_before = eq_base + block_excl_scan(ce, scan, tot_e);
+    bool sel[kTkPer];
+    uint32_t cs = 0;
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) {
+      const bool inw = in(n0 + j);
+      const bool eq = inw && u[j] == T;
+      sel[j] = inw && (u[j] > T || (eq && eq_before < need));
+      eq_before += eq ? 1u : 0u;
+      cs += sel[j] ? 1u : 0u;
     }
-    const bool sel = n < hi && (u > T || (eq && eq_before + eq_in_wave < need));
-    const uint64_t selm = __ballot(sel);
-    if (lane == 0) c[1][wave] = __popcll(selm);
-    __syncthreads();
-    uint32_t sel_before = sel_base, sel_round = 0;
-    for (int w = 0; w < kTkWaves; ++w) {
-      const uint32_t x = c[1][w];
-      if (w < wave) sel_before += x;
-      sel_round += x;
-    }
-    if (sel) out[sel_before + __popcll(selm & ((uint64_t(1) << lane) - 1))] = n;
-    eq_base += eq_round;
-    sel_base += sel_round;
+    uint32_t tot_s;
+    uint32_t at = sel_base + block_excl_scan(cs, scan, tot_s);
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j)
+      if (sel[j]) out[at++] = n0 + j;
+    eq_base += tot_e;
+    sel_base += tot_s;
   }
 }
 

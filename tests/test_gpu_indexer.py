@@ -100,7 +100,7 @@ def test_logits_workloads_sampled_rows(name):
 
 
 @pytest.mark.parametrize("R,N,k", [(30, 500, 64), (12, 5000, 2048), (6, 70000, 2048), (20, 40000, 2048),
-                                   (18, 3000, 512)])
+                                   (18, 3000, 512), (6, 131072, 2048), (12, 30000, 9000)])
 def test_topk_equals_oracle(R, N, k):
     print(f"\n[indexer topk] R={R} N={N} k={k}", flush=True)
     x, ks, ke = make_topk_logits(R, N, seed=R + N, k=k)
