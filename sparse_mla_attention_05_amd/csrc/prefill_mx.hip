@@ -493,13 +493,15 @@ prefill_mx_kernel(const FwdParams p) {
   const int rro = krow * kXRope;
   const int rperm = rope_perm(krow);
   // values: read v (0..3) of column block m covers tile rows
-  // 32(v/2) + 16(v%2) + 8h .. +7; the lane pair (2t, 2t+1) of a 16-lane group
+  // 32((v/2) ^ kh) + 16(v%2) + 8h .. +7 (the wave's own key half first, as
+  // its P^T bytes are); the lane pair (2t, 2t+1) of a 16-lane group
   // points at row 8h + 2(t & 3) + t/2 of that group of 16, bytes 8(lane & 1)
   // of chunk 16kh + 2m + (lane bit 4).
   const int vt = (lane & 15) >> 1;
   const int vplow = 8 * h + 2 * (vt & 3) + (vt >> 2);
   const int vperm = nope_perm(vplow);
   const int vro = vplow * kXRow + 256 * kh + 8 * (lane & 1);
+  const int vro_own = vro + 32 * kh * kXRow, vro_oth = vro + 32 * (kh ^ 1) * kXRow;
   const int ve = (lane >> 4) & 1;
 
   floatx16 o[8];
@@ -584,6 +586,15 @@ prefill_mx_kernel(const FwdParams p) {
     for (int tt = 0; tt < nt; ++tt) {
       const int g = gbase + tt;  // stream position: ring places
       const int par = g & 1;
+      // The indices of tile tt + 3 (their ring place landed a step ago), or
+      // past the walk's end the next item's first tiles when streaming (else
+      // all invalid: the DMAs write zeros to ring places that are free);
+      // tile tt + 5's indices the same way. Read here, off the stretch after
+      // the barrier.
+      const int t3 = tt + 3 < nt ? t_begin + tt + 3 : (stream ? t_begin + tt + 3 - nt : t_end);
+      const bool x5 = tt + 5 >= nt;
+      const int t5 = !x5 ? t_begin + tt + 5 : (stream ? t_begin + tt + 5 - nt : t_end);
+      read_idx(g + 3, t3);
       const bool has_next = tt + 1 < nt;
       float xmax, lt;
       uint32_t phi[4], plo[4];
@@ -716,28 +727,36 @@ prefill_mx_kernel(const FwdParams p) {
         *reinterpret_cast<u32x4*>(xp + 16) = u32x4{plo[0], plo[1], plo[2], plo[3]};
         xm[(par * kXWaves + wave) * 32 + c32] = m_w;
       }
+      // The values of the first two column blocks (tile tt has been in the
+      // ring since the last barrier): read before this one, so that only
+      // the partner's P is read after it.
+      const uint8_t* const vb = smem + (g % kXRing) * C::NOPE;
+      // Value fragment (block m, read v): keys of this wave's own half for
+      // v < 2, the partner's for v >= 2, the order of the P^T bytes below.
+      auto vread = [&](int m, int v) -> u32x2 {
+        return lds_read_tr8(vb + (v < 2 ? vro_own : vro_oth) + 16 * ((2 * m + ve) ^ vperm) +
+                            16 * (v & 1) * kXRow);
+      };
+      constexpr int VR = 3;
+      u32x2 vr[VR][4];
+#pragma unroll
+      for (int m = 0; m < VR - 1; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) vr[m][v] = vread(m, v);
       sync_tile();  // P and references visible; tile tt + 2 landed; tile tt - 1 free
 
-      // ---- both halves' P^T and references (their latency covered by the
-      // next tile's last k-step and the DMA issue)
-      u32x4 xh0, xl0, xh1, xl1;
-      float m_blk, m_other;
+      // ---- the partner's P^T and reference (the own half stays in
+      // registers: the dots take the own keys first). The scale of k-block
+      // h is the reference of its half: own for h = 0, the partner's for 1.
+      u32x4 xho, xlo;
+      float m_other;
       {
-        const uint8_t* xp = smem + C::OFF_XP + par * C::XPB + (2 * hp * 64 + lane) * 32;
-        xh0 = *reinterpret_cast<const u32x4*>(xp);
-        xl0 = *reinterpret_cast<const u32x4*>(xp + 16);
-        xh1 = *reinterpret_cast<const u32x4*>(xp + 64 * 32);
-        xl1 = *reinterpret_cast<const u32x4*>(xp + 64 * 32 + 16);
-        m_blk = xm[(par * kXWaves + 2 * hp + h) * 32 + c32];           // half h's
-        m_other = xm[(par * kXWaves + 2 * hp + (kh ^ 1)) * 32 + c32];  // the partner's
+        const uint8_t* xp = smem + C::OFF_XP + par * C::XPB + ((wave ^ 1) * 64 + lane) * 32;
+        xho = *reinterpret_cast<const u32x4*>(xp);
+        xlo = *reinterpret_cast<const u32x4*>(xp + 16);
+        m_other = xm[(par * kXWaves + (wave ^ 1)) * 32 + c32];
       }
-      // The indices of tile tt + 3, or past the walk's end the next item's
-      // first tiles when streaming (else all invalid: the DMAs write zeros
-      // to ring places that are free); tile tt + 5's indices the same way.
-      const int t3 = tt + 3 < nt ? t_begin + tt + 3 : (stream ? t_begin + tt + 3 - nt : t_end);
-      const bool x5 = tt + 5 >= nt;
-      const int t5 = !x5 ? t_begin + tt + 5 : (stream ? t_begin + tt + 5 - nt : t_end);
-      read_idx(g + 3, t3);
+      const float m_blk = h ? m_other : m_w;
       // the next item's q into the L2: 256 64-byte lines a step over the
       // five steps before the last. The dwords land in the slot flags of
       // tile tt's ring place, which were read a step ago and are written
@@ -755,7 +774,8 @@ prefill_mx_kernel(const FwdParams p) {
       const float d_own = ref ? fminf(fmaxf(m_w - m_o, kXMinDrift), kXMaxDrift) : 0.f;
       l_run += __builtin_ldexpf(lt, int(d_own));
       const int sb_ph = kE8One + int(d_blk), sb_pl = kE8One - 4 + int(d_blk);
-      const i32x8 ph = cat(xh0, xh1), pl = cat(xl0, xl1);
+      const i32x8 ph = cat(u32x4{phi[0], phi[1], phi[2], phi[3]}, xho);
+      const i32x8 pl = cat(u32x4{plo[0], plo[1], plo[2], plo[3]}, xlo);
 
       // ---- the next tile's last k-step, then O^T += V^T P^T over this
       // wave's 8 column blocks; each value fragment feeds both terms of P
@@ -765,17 +785,6 @@ prefill_mx_kernel(const FwdParams p) {
       // flags are read before the last two blocks. No branch in this
       // stretch: the order below is the order issued.
       {
-        const uint8_t* vb = smem + (g % kXRing) * C::NOPE + vro;
-        auto vread = [&](int m, int v) -> u32x2 {
-          return lds_read_tr8(vb + 16 * ((2 * m + ve) ^ vperm) +
-                              (32 * (v >> 1) + 16 * (v & 1)) * kXRow);
-        };
-        constexpr int VR = 3;
-        u32x2 vr[VR][4];
-#pragma unroll
-        for (int m = 0; m < VR - 1; ++m)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) vr[m][v] = vread(m, v);
         __builtin_amdgcn_sched_barrier(0);
         kstep(s_next, NSTEP - 1, kr[(NSTEP - 1) % 3]);
         asm volatile("" : "+a"(s_next));  // issued here, ahead of the DMAs
