@@ -398,21 +398,24 @@ prefill_fp8_kernel(const FwdParams p) {
 
   // One walk over tiles [t0, t_end) with the references in m_ref, or, with
   // fix_ref, with the references fixed by the walk's first tile.
-  auto walk = [&](int t0, bool fix_ref) {
+  // The first walk gets the indices of its first three tiles already
+  // loaded (ids[0..1] masked, ids[2] raw), so its start waits for one
+  // gather after the other and no index load between them.
+  auto walk = [&](int t0, bool fix_ref, const int (&ids)[3]) {
 #pragma unroll
     for (int d = 0; d < NDW; ++d) o[d][0] = o[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) nmu[hb] = m_ref[hb] == kNegInf ? 0.f : -m_ref[hb];
     l_part[0] = l_part[1] = 0.f;
     if (t0 >= t_end) return;
-    int id_a = load_idx(t0);
+    const int id_a = fix_ref ? ids[0] : load_idx(t0);
+    int id_b = fix_ref ? ids[1] : load_idx(t0 + 1);
+    int raw_n = fix_ref ? ids[2] : idx_raw(t0 + 2);  // masked where it is used
     gather(id_a);
     if (fix_ref) load_q();  // the first walk; a second one reuses Q
 #pragma unroll
     for (int i = 0; i < LPT; ++i) stage_chunk(i, tile0);
     if (gq == 0) kbias[gk] = id_a >= 0 ? 0.f : kNegInf;
-    int id_b = load_idx(t0 + 1);
-    int raw_n = idx_raw(t0 + 2);  // masked where it is used
     gather(id_b);
     __syncthreads();
     // One tile: QK of tile t from `cur` with tile t+1 (zeros past the end:
@@ -498,7 +501,15 @@ prefill_fp8_kernel(const FwdParams p) {
   // The first tile with a valid slot (uniform over the workgroup); tiles
   // before it add nothing.
   int t0 = t_begin;
-  while (t0 < t_end && __syncthreads_or(load_idx(t0) >= 0) == 0) ++t0;
+  int ids[3];  // the first walk's indices of tiles t0, t0 + 1 (masked) and t0 + 2 (raw)
+  ids[0] = -1;
+  while (t0 < t_end) {
+    ids[0] = load_idx(t0);
+    ids[1] = load_idx(t0 + 1);  // in flight with the test
+    ids[2] = idx_raw(t0 + 2);
+    if (__syncthreads_or(ids[0] >= 0) != 0) break;
+    ++t0;
+  }
   // Walk once with the first valid tile's max as the reference. Every
   // weight of a lane is at most its partial row sum, so if no lane's sum
   // passed kXSumLimit no weight did, and the bf16 weights and fp32 sums
@@ -507,7 +518,7 @@ prefill_fp8_kernel(const FwdParams p) {
 #pragma clang loop unroll(disable)
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) max_pass(t0, t_end);
-    walk(t0, pass == 0);
+    walk(t0, pass == 0, ids);
     if (pass == 1) break;
     if (tid == 0) redo[0] = 0u;
     __syncthreads();
