@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_fp8")
+    ap.add_argument("--variant", type=int, default=0,
+                    help="kernel instance for the --workload timing (0: the planner's choice); "
+                         "used to profile an opt-in kernel")
     ap.add_argument("--configs", default="tiny,decode_bf16,decode_fp8,prefill_fp8,prefill_glm",
                     help="comma list of the configurations timed on their own, each with its "
                          "roofline fraction and the oracle beside it ('' for none)")
@@ -148,12 +151,13 @@ def counters_from_profiles(kernel_src, workload):
         return None
 
 
-def time_workload(name, steps, warmup, cold, window=0, epi=None):
+def time_workload(name, steps, warmup, cold, window=0, epi=None, variant=0):
     """Time one workload; with `window` > 0 as a two-segment call whose second
     segment is a seeded sliding window of that many slots over its own pool;
     with epi = "fused" the forward's store applies the inverse RoPE and the
     MXFP8 store, with epi = "unfused" the plain forward is followed by the
-    separate epilogue pass."""
+    separate epilogue pass. A nonzero `variant` asks the planner for that
+    kernel instance (plain calls only)."""
     import torch
     from sparse_mla_attention_05_amd import _lib
     from sparse_mla_attention_05_amd.inputs import (make_epilogue_inputs, make_extra_segment,
@@ -195,14 +199,28 @@ def time_workload(name, steps, warmup, cold, window=0, epi=None):
                 _lib.sparse_mla_fwd(q, pool, scale, idx, inp.sm_scale, out, lse, stream=stream)
                 _lib.sparse_mla_out_epilogue(out, codes, rope_positions=pos, rope_cos_sin=cs,
                                              out_scale=scales, stream=stream)
+    elif variant:
+        plan = _lib.sparse_mla_plan(q, pool, idx, variant=variant)
+
+        def call():
+            _lib.sparse_mla_fwd_ex(q, pool, scale, idx, inp.sm_scale, out, lse, stream=stream,
+                                   variant=variant)
     else:
         plan = _lib.sparse_mla_plan(q, pool, idx)
 
         def call():
             _lib.sparse_mla_fwd(q, pool, scale, idx, inp.sm_scale, out, lse, stream=stream)
 
-    for _ in range(warmup):
+    # Warm until the device clock has settled: at least `warmup` calls and
+    # WARM_SECONDS of back-to-back work (the clock ramps over tens of ms:
+    # successive calls of a cold device run up to ~15 % slower).
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < WARM_SECONDS:
         call()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     times = []
     t0 = time.perf_counter()
@@ -239,6 +257,7 @@ def time_workload(name, steps, warmup, cold, window=0, epi=None):
 
 
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, TFLOP/s
+WARM_SECONDS = 0.15  # back-to-back work before a timing starts
 
 
 def time_indexer(name, steps, warmup):
@@ -264,11 +283,10 @@ def time_indexer(name, steps, warmup):
     }
     res = {}
     for key, call in calls.items():
-        # warm until the device clock has settled: at least `warmup` calls
-        # and 25 ms of back-to-back work
+        # warm until the device clock has settled (as time_workload does)
         t0 = time.perf_counter()
         n = 0
-        while n < warmup or time.perf_counter() - t0 < 0.025:
+        while n < warmup or time.perf_counter() - t0 < WARM_SECONDS:
             call()
             n += 1
             if n % 4 == 0:
@@ -375,7 +393,7 @@ def main():
 
     cold = not args.warm
     cpu_on = not args.no_cpu_baseline
-    head = time_workload(args.workload, args.steps, args.warmup, cold)
+    head = time_workload(args.workload, args.steps, args.warmup, cold, variant=args.variant)
     times = head["times"]
     us = statistics.median(times)
     alg = head["alg"]
