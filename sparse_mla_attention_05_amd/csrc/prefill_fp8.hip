@@ -177,13 +177,14 @@ prefill_fp8_kernel(const FwdParams p) {
   // issued a tile before it is used: applying the mask right after the load
   // would make the wave wait for every gather issued before it.
   // The row's indices up to last_slot through a buffer resource: a load past
-  // it reads 0, which the mask then marks invalid.
+  // it reads 0, which the mask then marks invalid. The loads run up to three
+  // tiles past the row's end (past the tensor's end on its last row) and the
+  // hardware range check covers the vector and immediate offsets but not the
+  // scalar one, so the whole byte offset goes in the vector offset.
   const __amdgpu_buffer_rsrc_t idx_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(idx_row), 0, 4 * (last_slot + 1), kXBufferWord3);
-  // The per-lane part of the slot number stays gk (tile offsets are uniform),
-  // so no per-lane counter is carried through the tile loop.
   auto idx_raw = [&](int t) -> int {
-    return __builtin_amdgcn_raw_buffer_load_b32(idx_rsrc, uint32_t(4 * gk), 4 * t * TK, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(idx_rsrc, uint32_t(4 * (gk + t * TK)), 0, 0);
   };
   auto idx_mask = [&](int t) -> int { return -int(!(t < t_end && gk <= last_slot - t * TK)); };
   auto load_idx = [&](int t) -> int { return idx_raw(t) | idx_mask(t); };
