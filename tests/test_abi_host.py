@@ -500,3 +500,46 @@ def test_plan_fp8_dot_kernel_eligibility():
     assert _lib.sparse_mla_plan(q, paged_ok, idx, variant=3)["variant"] == 3
     assert _lib.sparse_mla_plan(q, paged_odd, idx, variant=3)["variant"] == 0
     assert _lib.sparse_mla_plan(q, wide, idx, variant=3)["variant"] == 0
+
+
+def _call_args(src, start):
+    """Top-level comma-separated arguments of the call whose '(' is at start."""
+    depth, args, cur = 0, [], ""
+    for ch in src[start:]:
+        if ch == "(":
+            depth += 1
+            if depth == 1:
+                continue
+        elif ch == ")":
+            depth -= 1
+            if depth == 0:
+                args.append(cur.strip())
+                return args
+        if ch == "," and depth == 1:
+            args.append(cur.strip())
+            cur = ""
+        else:
+            cur += ch
+    raise AssertionError("unbalanced call")
+
+
+def test_buffer_loads_keep_offsets_range_checked():
+    """Every buffer load or store in the kernels passes its offset in the
+    vector (or immediate) operand and 0 as the scalar offset: the hardware
+    range check that turns out-of-range slots into zeros does not cover the
+    scalar offset, so an offset there can read past a tensor's end."""
+    csrc = os.path.join(os.path.dirname(_lib.__file__), "csrc")
+    n = 0
+    for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h")):
+            continue
+        src = open(os.path.join(csrc, name)).read()
+        for m in re.finditer(r"__builtin_amdgcn_raw_buffer_(load|store)_\w+\s*\(", src):
+            args = _call_args(src, m.end() - 1)
+            soff = args[2] if m.group(1) == "load" else args[3]
+            assert soff in ("0", "0u"), f"{name}: scalar offset {soff!r} in {m.group(0)}"
+            n += 1
+        for m in re.finditer(r"buffer_(load|store)_dword\w*\s+%\d+,\s*%\d+,\s*(\S+)", src):
+            assert m.group(2) == "0", f"{name}: scalar offset {m.group(2)!r} in inline asm"
+            n += 1
+    assert n > 10
