@@ -78,14 +78,17 @@ typedef struct smla_options {
   int32_t variant;         /* kernel instance; 0 = the planner's choice: the 16-head
                               decode kernel over fp8 pools (H <= 32), the staged-tile
                               kernel (16 and 32 heads over bf16 pools; 64 heads over
-                              bf16 pools), the 4-wave kernel (64 heads over fp8 pools).
+                              bf16 pools), for 64 heads over fp8 pools the 4-wave
+                              kernel (576-wide rows) or the fp8-dot kernel (512-wide).
                               1 = the staged-tile kernel (any head block; also what
                               pools past the 32-bit buffer range use). 2 = 64 heads
                               only: the 8-wave double-buffered kernel. 3 = 64 heads
                               over fp8 pools only: the fp8-dot kernel (both products
                               on the fp8 matrix cores over two-term e4m3 splits of q
-                              and P); falls back to the default where the pool's row
-                              pitch does not fit its structured buffer */
+                              and P); falls back to the 4-wave kernel where the pool's
+                              row pitch does not fit its structured buffer. 4 = 64
+                              heads over fp8 pools only: the 4-wave kernel (bf16 dots
+                              on widened tiles), reported by the plan as variant 0 */
   void* workspace;         /* optional caller device buffer for split partials */
   int64_t workspace_bytes; /* its size; must be >= smla_plan.workspace_bytes when given */
   const void* q_scale;     /* fp32 [1] device pointer: per-tensor scale of a float8_e4m3fn q

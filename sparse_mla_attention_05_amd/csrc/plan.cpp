@@ -16,6 +16,8 @@
 //    it measured 3-14 % faster than the 8-wave kernel of prefill.hip on
 //    every 64-head bf16 shape tried (96..2048 rows, top-k 512 and 2048;
 //    55.3 against 63.2 us on the 192-row decode), which stays as variant 2.
+//    Over fp8 pools 64-head blocks of 512-wide rows take the fp8-dot kernel
+//    (variant 3), 576-wide rows the 4-wave kernel (variant 0).
 //  * splits: when rows x head blocks leave the CUs' workgroup slots
 //    underfilled, each row's slots are split if a makespan model (rounds of
 //    workgroups x (tiles per split + a fixed per-workgroup cost) + the
@@ -45,7 +47,7 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   static const char* kBadRemap = "remap override must be 0, 1 or 2";
   static const char* kBadGrid = "launch grid exceeds 2^31 - 1 workgroups";
   static const char* kBadVariant =
-      "variant override must be 0, 1, 2 or 3 (2: 64 heads only; 3: 64 heads, fp8 pools only)";
+      "variant override must be 0..4 (2: 64 heads only; 3, 4: 64 heads, fp8 pools only)";
   static const char* kBadWgs = "workgroups must be >= 0";
   if (num_cus <= 0) num_cus = 256;
   *plan = smla_plan{};
@@ -66,14 +68,20 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
   }
   int variant = 0;
   if (opt && opt->variant) {
-    if (opt->variant < 1 || opt->variant > 3 || (opt->variant == 2 && hb != 64) ||
-        (opt->variant == 3 && !(hb == 64 && pb.kv_fp8))) {
+    if (opt->variant < 1 || opt->variant > 4 || (opt->variant == 2 && hb != 64) ||
+        (opt->variant >= 3 && !(hb == 64 && pb.kv_fp8))) {
       *err = kBadVariant;
       return SMLA_ERR_INVALID_ARG;
     }
-    variant = opt->variant;
+    // 4 asks for the 4-wave fp8 kernel, which the plan reports as variant 0.
+    variant = opt->variant == 4 ? 0 : opt->variant;
   } else if (hb == 64 && !pb.kv_fp8) {
     variant = 1;
+  } else if (hb == 64 && pb.dqk == 512) {
+    // 512-wide fp8 rows: the fp8-dot kernel, measured 1.5-4.4 % faster than
+    // the 4-wave kernel on the 8192-row, top-k 2048 prefill across boxes
+    // (576-wide rows: within 1 % either way, so the 4-wave kernel stays).
+    variant = 3;
   }
   // The decode (16 heads, fp8) and 64-head kernels read the pool through a
   // 32-bit buffer range; a larger pool takes the staged-tile kernel.

@@ -150,7 +150,11 @@ def test_plan_head_block_choice_and_overrides():
     # 64 heads over bf16 pools: the staged-tile kernel unless overridden
     assert _plan(192, 64, K=512, dtype=torch.bfloat16)["variant"] == 1
     assert _plan(192, 64, K=512, dtype=torch.bfloat16, variant=2)["variant"] == 2
+    # 64 heads over fp8 pools: the 4-wave kernel for 576-wide rows, the
+    # fp8-dot kernel for 512-wide rows; 4 forces the 4-wave kernel
     assert _plan(8192, 64)["variant"] == 0
+    assert _plan(8192, 64, D=512)["variant"] == 3
+    assert _plan(8192, 64, D=512, variant=4)["variant"] == 0
     assert _plan(8192, 64)["head_block"] == 64
     assert _plan(8192, 64)["splits"] == 1
     assert _plan(4, 16, K=2048)["splits"] > 1      # a tiny launch gets split
@@ -465,9 +469,14 @@ def test_workspace_query_without_a_gpu():
 
 def test_plan_rejects_unknown_variants():
     with pytest.raises(_lib.SparseMLAError):
-        _plan(64, 64, variant=4)
+        _plan(64, 64, variant=5)
     with pytest.raises(_lib.SparseMLAError):
         _plan(64, 16, variant=2)                   # 2 is a 64-head kernel
+    with pytest.raises(_lib.SparseMLAError):
+        _plan(64, 16, variant=4)                   # 4 is a 64-head fp8 kernel
+    with pytest.raises(_lib.SparseMLAError):
+        _plan(64, 64, dtype=torch.bfloat16, variant=4)
+    assert _plan(64, 64, variant=4)["variant"] == 0
     assert _plan(64, 64, variant=2)["variant"] == 2
     assert _plan(64, 16, variant=1)["variant"] == 1
 

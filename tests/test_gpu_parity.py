@@ -95,12 +95,12 @@ def test_workload_full_parity(name):
     print(f"[parity] {name}: {stats}", flush=True)
 
 
-@pytest.mark.parametrize("variant", [0, 3])
+@pytest.mark.parametrize("variant", [0, 3, 4])
 @pytest.mark.parametrize("name", ["prefill_fp8", "prefill_glm"])
 def test_prefill_parity_on_sampled_rows(name, variant):
-    """The whole workload runs in the launch the benchmark times; the oracle
-    checks every 64th row plus the last one (variant 3: the fp8-dot 64-head
-    kernel)."""
+    """The whole workload runs in the launch the benchmark times (variant 0,
+    the planner's choice); the oracle checks every 64th row plus the last
+    one. Variants 3 and 4 force the fp8-dot and the 4-wave 64-head kernels."""
     print(f"\n[parity] workload={name} variant={variant} (sampled rows)", flush=True)
     inp = make_inputs(name)
     out, lse = run_gpu(inp, **({"variant": variant} if variant else {}))
@@ -339,17 +339,17 @@ def test_decode_index_chunks(topk, splits, heads, d_qk):
     _check(inp, variant=0, splits=splits)
 
 
-VARIANT_SHAPES = [(v, d, kv, h) for v in (0, 1, 2, 3)
+VARIANT_SHAPES = [(v, d, kv, h) for v in (0, 1, 2, 3, 4)
                   for d, kv, h in [(576, "fp8", 64), (512, "fp8", 80), (576, "bf16", 64)]
-                  if not (v == 3 and kv == "bf16")]
+                  if not (v >= 3 and kv == "bf16")]
 
 
 @pytest.mark.parametrize("variant,d_qk,kv,heads", VARIANT_SHAPES)
 @pytest.mark.parametrize("topk,splits", [(2048, 1), (1000, 1), (17, 1), (1000, 3), (300, 2)])
 def test_64head_variants(variant, d_qk, kv, heads, topk, splits):
-    """The 64-head kernels (variant 0: the 4-wave kernel over fp8 pools, the
-    staged-tile kernel over bf16 pools; 1: the single-buffered staged-tile kernel;
-    2: the 8-wave kernel; 3: the fp8-dot kernel, fp8 pools only) on ragged
+    """The 64-head kernels (variant 0: the planner's choice; 1: the
+    single-buffered staged-tile kernel; 2: the 8-wave kernel; 3: the fp8-dot
+    kernel and 4: the 4-wave kernel, fp8 pools only) on ragged
     top-k, odd tile counts, a partial head block, leading invalid tiles and
     an empty row, with and without splits."""
     inp = _case(rows=5, heads=heads, d_qk=d_qk, topk=topk, pool_rows=8192, kv_dtype=kv,
