@@ -15,13 +15,16 @@
 // matrix cores and keeps bf16-class accuracy by splitting the bf16/fp32
 // operands into two e4m3 terms:
 //  * q (bf16, 8 significant bits) times a power of two 2^e that puts the
-//    head's largest |q| in [128, 256) is q' = hi + lo/16 with hi = e4m3(q')
-//    and lo = e4m3((q' - hi) * 16). The residual q' - hi is a multiple of
-//    q's last bit no larger than half of hi's, so it has at most 4
-//    significant bits and lo holds it exactly: the split is exact except for
-//    elements below 2^-14 of the largest, where it errs by 2^-22 of it.
-//    The MFMA's E8M0 block scales apply 2^-e and 2^-(e+4), so S = K.q comes
-//    out exactly as with bf16 dots, up to fp32 accumulation order.
+//    largest |q| of its 32-column block (one k-block of a dot) in [128, 256)
+//    is q' = hi + lo/16 with hi = e4m3(q') and lo = e4m3((q' - hi) * 16).
+//    The residual q' - hi is a multiple of q's last bit no larger than half
+//    of hi's, so it has at most 4 significant bits and lo holds it exactly:
+//    the split is exact except for elements below 2^-14 of their block's
+//    largest, where it errs by 2^-22 of it. The MFMA's E8M0 block scales
+//    (one per column and 32-deep k-block) apply 2^-e and 2^-(e+4), so
+//    S = K.q comes out exactly as with bf16 dots, up to fp32 accumulation
+//    order. A block's scale depends on its own 32 values only, so each
+//    k-step of q is split as soon as it has landed.
 //  * P = 2^(s - m) <= 2^8 (see below) splits the same way into two e4m3
 //    terms, 8 significant bits in all, the precision of the pages' bf16 P.
 //  * The fp8 keys and values are used as stored (exact), so tiles stay fp8
@@ -188,10 +191,28 @@ __device__ __forceinline__ void dma4(const i32x4& rsrc, uint32_t lds, uint32_t v
 }
 #pragma clang diagnostic pop
 
-// D += A B on the fp8 matrix cores; A's block scale 1, B's 2^(sb - 127)
-// (lane j gives the scale of column j % 32, k-block j / 32).
+// D += A B on the fp8 matrix cores; A's block scale 1, B's 2^(code - 127)
+// with code byte SEL of sb (lane j gives the scale of column j % 32,
+// k-block j / 32).
+template <int SEL = 0>
 __device__ __forceinline__ floatx16 mx32(const i32x8& a, const i32x8& b, floatx16 c, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8One, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8One, SEL, sb);
+}
+__device__ __forceinline__ floatx16 mx32_byte(const i32x8& a, const i32x8& b, floatx16 c, int sb,
+                                              int sel) {
+  switch (sel & 3) {
+    case 0: return mx32<0>(a, b, c, sb);
+    case 1: return mx32<1>(a, b, c, sb);
+    case 2: return mx32<2>(a, b, c, sb);
+    default: return mx32<3>(a, b, c, sb);
+  }
+}
+
+// Exponent e that puts a bf16 magnitude pattern m (|x| as 15 bits) in
+// [128, 256) once scaled by 2^e; 0 for m = 0 (an all-zero block).
+__device__ __forceinline__ int block_exp(uint32_t m) {
+  const int e = 134 - int(m >> 7);  // m = 1.f x 2^(E - 127): e = 7 - (E - 127)
+  return m == 0u ? 0 : min(max(e, -100), 100);
 }
 
 __device__ __forceinline__ i32x8 cat(const u32x4& a, const u32x4& b) {
@@ -352,18 +373,16 @@ prefill_mx_kernel(const FwdParams p) {
     for (int k = 0; k < kPieces; ++k) dma_piece(tt, k);
   };
   // A walk's start: the indices of its first four tiles, then (indices
-  // landed) the DMAs of the first three. `between` runs after the barrier
-  // that lands the indices, before the DMAs.
+  // landed) the DMAs of the first three.
   // A walk whose first tiles are already requested (`fresh` false: the
   // previous item's walk streamed into them) only waits for them.
-  auto start_walk = [&](int nt, bool fresh, auto&& between) {
+  auto start_walk = [&](int nt, bool fresh) __attribute__((always_inline)) {
     if (fresh) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
         if (tt < nt) idx_dma(tt, t_begin + tt, idx_rsrc);
     }
     sync_tile();
-    between();
     if (fresh) {
 #pragma unroll
       for (int tt = 0; tt < 3; ++tt) {
@@ -377,21 +396,46 @@ prefill_mx_kernel(const FwdParams p) {
   };
 
   // q of this lane's head: k-step st takes columns 64 st + 16h and
-  // 64 st + 32 + 16h (16 each), split into hi and lo e4m3 terms under the
-  // head's power of two (2^e puts its largest |q| in [128, 256)). The loads
-  // are issued before the walk's first barrier and all consumed (the
-  // largest magnitude) right after it, before any DMA is in flight, so the
-  // compiler's waits for them wait for nothing else.
+  // 64 st + 32 + 16h (16 each, one in each k-block), split into hi and lo
+  // e4m3 terms under each k-block's power of two (2^e puts the block's
+  // largest |q| in [128, 256)). The loads are issued before the walk's
+  // first barrier, whose wait covers them, so the split after it waits for
+  // nothing (in particular not for the tile DMAs issued in between).
   i32x8 qhi[NSTEP], qlo[NSTEP];
-  int sb_hi = kE8One, sb_lo = kE8One;
+  // E8M0 codes of the q terms' block scales, byte st % 4 of word st / 4:
+  // this lane gives k-block h's (hi: 127 - e, lo: 127 - e - 4).
+  constexpr int NSB = (NSTEP + 3) / 4;
+  int sbh[NSB], sbl[NSB];
+#pragma unroll
+  for (int i = 0; i < NSB; ++i) sbh[i] = sbl[i] = 0x7F7F7F7F;
   auto q_col = [&](int st, int d) { return 64 * st + 32 * d + 16 * h; };
-  auto q_exponent = [&](float amax) {
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const int e = 8 - __builtin_amdgcn_frexp_expf(amax);
-    return amax > 0.f && head_ok ? min(max(e, -100), 100) : 0;
-  };
-  // q given as 8 bf16 bit patterns per u32x4 pair: (hi, lo) terms of k-step st
-  auto split_q = [&](int st, const u32x4 (&raw)[2][2], float sc) {
+  // q of k-step st given as 8 bf16 bit patterns per u32x4 ([block d][half]):
+  // each k-block's largest magnitude (this lane's 16 values and the partner
+  // lane's, l ^ 32), its exponent, and the (hi, lo) terms under 2^e.
+  auto split_q = [&](int st, const u32x4 (&raw)[2][2]) __attribute__((always_inline)) {
+    uint32_t mb[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t w = raw[d][hf][k] & 0x7FFF7FFFu;
+          m = max(m, max(w & 0xFFFFu, w >> 16));
+        }
+      mb[d] = m;
+    }
+    const uint32_t both = mb[0] | (mb[1] << 16);
+    const uint32_t other = uint32_t(__shfl_xor(int(both), 32));
+    const int e0 = block_exp(max(mb[0], other & 0xFFFFu));
+    const int e1 = block_exp(max(mb[1], other >> 16));
+    const float sc0 = head_ok ? __builtin_ldexpf(1.0f, e0) : 0.f;
+    const float sc1 = head_ok ? __builtin_ldexpf(1.0f, e1) : 0.f;
+    const int eh = h ? e1 : e0;
+    const int sh = 8 * (st & 3);
+    sbh[st / 4] = (sbh[st / 4] & ~(0xFF << sh)) | ((kE8One - eh) << sh);
+    sbl[st / 4] = (sbl[st / 4] & ~(0xFF << sh)) | ((kE8One - 4 - eh) << sh);
     uint32_t hw[8], lw[8];
 #pragma unroll
     for (int d = 0; d < 2; ++d)
@@ -399,6 +443,7 @@ prefill_mx_kernel(const FwdParams p) {
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
+          const float sc = d ? sc1 : sc0;
           const uint32_t w0 = raw[d][hf][2 * k], w1 = raw[d][hf][2 * k + 1];
           split4(__uint_as_float(w0 << 16) * sc, __uint_as_float(w0 & 0xFFFF0000u) * sc,
                  __uint_as_float(w1 << 16) * sc, __uint_as_float(w1 & 0xFFFF0000u) * sc,
@@ -407,7 +452,7 @@ prefill_mx_kernel(const FwdParams p) {
     qhi[st] = pack8(hw);
     qlo[st] = pack8(lw);
   };
-  auto start_first_walk = [&](int nt, bool fresh) {
+  auto start_first_walk = [&](int nt, bool fresh) __attribute__((always_inline)) {
     const int hq = head_ok ? head : p.heads - 1;  // a masked head reads a real one, scaled by 0
     const int64_t qp = r * p.q_rs + int64_t(hq) * p.q_hs;
     if (p.q_fp8) {
@@ -418,26 +463,7 @@ prefill_mx_kernel(const FwdParams p) {
         for (int d = 0; d < 2; ++d)
           raw[st][d] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + qp +
                                                        q_col(st, d));
-      float sc = 0.f;
-      start_walk(nt, fresh, [&]() {
-        float amax = 0.f;
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st)
-#pragma unroll
-          for (int d = 0; d < 2; ++d)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const u32x2 w = widen_fp8x4(raw[st][d][k]);
-              amax = fmaxf(amax, fmaxf(fmaxf(fabsf(__uint_as_float(w.x << 16)),
-                                             fabsf(__uint_as_float(w.x & 0xFFFF0000u))),
-                                       fmaxf(fabsf(__uint_as_float(w.y << 16)),
-                                             fabsf(__uint_as_float(w.y & 0xFFFF0000u)))));
-            }
-        const int e = q_exponent(amax);
-        sc = head_ok ? __builtin_ldexpf(1.0f, e) : 0.f;
-        sb_hi = kE8One - e;
-        sb_lo = kE8One - e - 4;
-      });
+      start_walk(nt, fresh);
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) {
         u32x4 bf[2][2];
@@ -448,7 +474,7 @@ prefill_mx_kernel(const FwdParams p) {
           bf[d][0] = u32x4{a.x, a.y, b.x, b.y};
           bf[d][1] = u32x4{c.x, c.y, e.x, e.y};
         }
-        split_q(st, bf, sc);
+        split_q(st, bf);
       }
     } else {
       u32x4 raw[NSTEP][2][2];
@@ -459,26 +485,9 @@ prefill_mx_kernel(const FwdParams p) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf)
             raw[st][d][hf] = *reinterpret_cast<const u32x4*>(p.q + qp + q_col(st, d) + 8 * hf);
-      float sc = 0.f;
-      start_walk(nt, fresh, [&]() {
-        float amax = 0.f;
+      start_walk(nt, fresh);
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st)
-#pragma unroll
-          for (int d = 0; d < 2; ++d)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-              for (int k = 0; k < 4; ++k)
-                amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[st][d][hf][k] << 16)),
-                                         fabsf(__uint_as_float(raw[st][d][hf][k] & 0xFFFF0000u))));
-        const int e = q_exponent(amax);
-        sc = head_ok ? __builtin_ldexpf(1.0f, e) : 0.f;
-        sb_hi = kE8One - e;
-        sb_lo = kE8One - e - 4;
-      });
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) split_q(st, raw[st], sc);
+      for (int st = 0; st < NSTEP; ++st) split_q(st, raw[st]);
     }
   };
   const float kv_scale = *p.kv_scale;
@@ -523,8 +532,8 @@ prefill_mx_kernel(const FwdParams p) {
   // One k-step of S^T: both terms of q against one key fragment.
   auto kstep = [&](floatx16& s, int st, const u32x4 (&kf)[2]) {
     const i32x8 a = cat(kf[0], kf[1]);
-    s = mx32(a, qhi[st], s, sb_hi);
-    s = mx32(a, qlo[st], s, sb_lo);
+    s = mx32_byte(a, qhi[st], s, sbh[st / 4], st);
+    s = mx32_byte(a, qlo[st], s, sbl[st / 4], st);
   };
   // Slot flags (0 or -inf) of this lane's 16 slots of the walk's tile tt.
   auto read_bias = [&](int tt, floatx4 (&b)[4]) {
@@ -561,7 +570,7 @@ prefill_mx_kernel(const FwdParams p) {
     if (first)
       start_first_walk(nt, fresh);
     else
-      start_walk(nt, true, [&]() {});
+      start_walk(nt, true);
     sync_tile();
 
     floatx16 s_cur = floatx16{}, s_next;
@@ -676,7 +685,7 @@ prefill_mx_kernel(const FwdParams p) {
           const i32x8 a = cat(kr[st % 3][0], kr[st % 3][1]);
 #pragma unroll
           for (int term = 0; term < 2; ++term) {
-            s_next = mx32(a, term ? qlo[st] : qhi[st], s_next, term ? sb_lo : sb_hi);
+            s_next = mx32_byte(a, term ? qlo[st] : qhi[st], s_next, term ? sbl[st / 4] : sbh[st / 4], st);
             __builtin_amdgcn_sched_barrier(0);
             if (st + 2 < NSTEP) kr[(st + 2) % 3][term] = kread(g + 1, st + 2, term);
             const int di = 2 * st + term;
