@@ -142,23 +142,57 @@ prefill_fp8_kernel(const FwdParams p) {
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(ntiles, t_begin + p.tiles_per_split);
 
-  // Q^T operands: head h0 + 16hb + l16, columns 8g + 32s .. +7. Loaded by
-  // the walk right after the gathers of its first tile, so the two loads'
-  // latencies overlap.
+  // Q^T operands: head h0 + 16hb + l16, columns 8g + 32s .. +7 (zero for a
+  // head past the last). Loaded by each walk right after the gathers of its
+  // first tile, so the two loads' latencies overlap.
   bf16x8 qf[2][KSTEPS];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-  auto load_q = [&]() {
+  // The two waves of a pair hold the same Q^T: each loads the k-steps
+  // s = kh (mod 2), puts them in the pair's region of the second tile
+  // buffer (free until the walk's first step stages into it), and reads all
+  // k-steps back from there, which halves the workgroup's Q requests.
+  // Region of pair hp: [hb][s][lane], 16 bytes. (Register indices stay
+  // compile-time: the parity only moves addresses. An array indexed by a
+  // run-time value, or written differently on the two sides of a branch on
+  // the parity, would live in scratch memory.)
+  bf16x8 qh[2][KSTEPS / 2];
+  auto load_q_half = [&]() {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int i = 0; i < KSTEPS / 2; ++i) qh[hb][i] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
       const int h = h0 + 16 * hb + l16;
       if (h < p.heads) {
-        const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g;
-        load_q_frags(p.q, p.q_fp8, qp, 32, qf[hb]);
+        const int64_t qp = r * p.q_rs + int64_t(h) * p.q_hs + 8 * g + 32 * kh;
+        if (p.q_fp8) {
+          u32x2 c[KSTEPS / 2];
+#pragma unroll
+          for (int i = 0; i < KSTEPS / 2; ++i)
+            c[i] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(p.q) + qp + 64 * i);
+#pragma unroll
+          for (int i = 0; i < KSTEPS / 2; ++i) qh[hb][i] = widen_fp8x8(c[i].x, c[i].y);
+        } else {
+#pragma unroll
+          for (int i = 0; i < KSTEPS / 2; ++i)
+            qh[hb][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p.q + qp + 64 * i));
+        }
       }
     }
+  };
+  auto q_slot = [&](uint8_t* buf, int hb, int s) -> u32x4* {
+    return reinterpret_cast<u32x4*>(buf + (((hp * 2 + hb) * KSTEPS + s) * 64 + lane) * 16);
+  };
+  auto put_q_half = [&](uint8_t* buf) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int i = 0; i < KSTEPS / 2; ++i)
+        *q_slot(buf, hb, 2 * i + kh) = __builtin_bit_cast(u32x4, qh[hb][i]);
+  };
+  auto get_q = [&](uint8_t* buf) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[hb][s] = __builtin_bit_cast(bf16x8, *q_slot(buf, hb, s));
     // Keep Q^T in VGPRs: left to itself the allocator parks it in AGPRs (the
     // dots can read it there) and then has no AGPRs left for O^T and S^T.
 #pragma unroll
@@ -413,12 +447,15 @@ prefill_fp8_kernel(const FwdParams p) {
     int id_b = fix_ref ? ids[1] : load_idx(t0 + 1);
     int raw_n = fix_ref ? ids[2] : idx_raw(t0 + 2);  // masked where it is used
     gather(id_a);
-    if (fix_ref) load_q();  // the first walk; a second one reuses Q
+    load_q_half();  // (a second walk loads it again: Q^T is then not live across walks)
 #pragma unroll
     for (int i = 0; i < LPT; ++i) stage_chunk(i, tile0);
     if (gq == 0) kbias[gk] = id_a >= 0 ? 0.f : kNegInf;
     gather(id_b);
+    put_q_half(tile1);
     __syncthreads();
+    get_q(tile1);
+    __syncthreads();  // every wave has its Q^T before the first step stages into tile1
     // One tile: QK of tile t from `cur` with tile t+1 (zeros past the end:
     // harmless, never read) staged into `nxt`, the buffer tile t-1 used,
     // which every wave finished before the last barrier; softmax; P swap;
