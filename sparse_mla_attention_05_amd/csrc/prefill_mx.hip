@@ -402,6 +402,9 @@ prefill_mx_kernel(const FwdParams p) {
   // first barrier, whose wait covers them, so the split after it waits for
   // nothing (in particular not for the tile DMAs issued in between).
   i32x8 qhi[NSTEP], qlo[NSTEP];
+  // Walks carry one stream of tiles through the rings: gbase is the stream
+  // position of a walk's first tile.
+  int gbase = 0;
   // E8M0 codes of the q terms' block scales, byte st % 4 of word st / 4:
   // this lane gives k-block h's (hi: 127 - e, lo: 127 - e - 4).
   constexpr int NSB = (NSTEP + 3) / 4;
@@ -409,10 +412,12 @@ prefill_mx_kernel(const FwdParams p) {
 #pragma unroll
   for (int i = 0; i < NSB; ++i) sbh[i] = sbl[i] = 0x7F7F7F7F;
   auto q_col = [&](int st, int d) { return 64 * st + 32 * d + 16 * h; };
-  // q of k-step st given as 8 bf16 bit patterns per u32x4 ([block d][half]):
+  // q of one k-step given as 8 bf16 bit patterns per u32x4 ([block d][half]):
   // each k-block's largest magnitude (this lane's 16 values and the partner
-  // lane's, l ^ 32), its exponent, and the (hi, lo) terms under 2^e.
-  auto split_q = [&](int st, const u32x4 (&raw)[2][2]) __attribute__((always_inline)) {
+  // lane's, l ^ 32), its exponent, and the (hi, lo) terms under 2^e. Returns
+  // the E8M0 code of this lane's k-block h (hi term: 127 - e).
+  auto split_terms = [&](const u32x4 (&raw)[2][2], uint32_t (&hw)[8], uint32_t (&lw)[8])
+      __attribute__((always_inline)) -> int {
     uint32_t mb[2];
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
@@ -432,11 +437,6 @@ prefill_mx_kernel(const FwdParams p) {
     const int e1 = block_exp(max(mb[1], other >> 16));
     const float sc0 = head_ok ? __builtin_ldexpf(1.0f, e0) : 0.f;
     const float sc1 = head_ok ? __builtin_ldexpf(1.0f, e1) : 0.f;
-    const int eh = h ? e1 : e0;
-    const int sh = 8 * (st & 3);
-    sbh[st / 4] = (sbh[st / 4] & ~(0xFF << sh)) | ((kE8One - eh) << sh);
-    sbl[st / 4] = (sbl[st / 4] & ~(0xFF << sh)) | ((kE8One - 4 - eh) << sh);
-    uint32_t hw[8], lw[8];
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
@@ -449,46 +449,103 @@ prefill_mx_kernel(const FwdParams p) {
                  __uint_as_float(w1 << 16) * sc, __uint_as_float(w1 & 0xFFFF0000u) * sc,
                  hw[4 * d + 2 * hf + k], lw[4 * d + 2 * hf + k]);
         }
-    qhi[st] = pack8(hw);
-    qlo[st] = pack8(lw);
+    return kE8One - (h ? e1 : e0);
+  };
+  // k-step st's terms and block scale codes into place
+  auto set_q = [&](int st, const u32x4 (&t)[4], int code) __attribute__((always_inline)) {
+    qhi[st] = cat(t[0], t[1]);
+    qlo[st] = cat(t[2], t[3]);
+    const int sh = 8 * (st & 3);
+    sbh[st / 4] = (sbh[st / 4] & ~(0xFF << sh)) | (code << sh);
+    sbl[st / 4] = (sbl[st / 4] & ~(0xFF << sh)) | ((code - 4) << sh);
+  };
+  // The two waves of a pair need the same q terms: wave kh loads and splits
+  // the k-steps st = 2i + kh (for an odd count, wave 1's last one is a
+  // placeholder), and the pair swaps them through LDS that is free while a
+  // walk starts: the ring place of the walk's fourth tile (k-steps 0..7,
+  // 4 KB each: this lane's 64 bytes) and the P-exchange area (k-step 8, the
+  // placeholder and the scale codes). The area holds one pair's terms, so
+  // the pairs take turns. A wave reads back all k-steps (its own too), which
+  // keeps every register index compile-time.
+  constexpr int NH = (NSTEP + 1) / 2;
+  auto xq_terms = [&](int st) -> u32x4* {
+    uint8_t* const base = st < 8 ? smem + ((gbase + 3) % kXRing) * C::NOPE + st * 4096
+                                 : smem + C::OFF_XP + (st - 8) * 4096;
+    return reinterpret_cast<u32x4*>(base + lane * 64);
+  };
+  auto xq_code = [&](int st) -> int* {
+    return reinterpret_cast<int*>(smem + C::OFF_XP + 2 * 4096 + (st * 64 + lane) * 4);
+  };
+  auto swap_q = [&](const uint32_t (&hw)[NH][8], const uint32_t (&lw)[NH][8], const int (&code)[NH])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp) {
+      if (hp == rp) {
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+          u32x4* const t = xq_terms(2 * i + kh);
+          t[0] = u32x4{hw[i][0], hw[i][1], hw[i][2], hw[i][3]};
+          t[1] = u32x4{hw[i][4], hw[i][5], hw[i][6], hw[i][7]};
+          t[2] = u32x4{lw[i][0], lw[i][1], lw[i][2], lw[i][3]};
+          t[3] = u32x4{lw[i][4], lw[i][5], lw[i][6], lw[i][7]};
+          *xq_code(2 * i + kh) = code[i];
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (hp == rp) {
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+          const u32x4* const t = xq_terms(st);
+          const u32x4 tt[4] = {t[0], t[1], t[2], t[3]};
+          set_q(st, tt, *xq_code(st));
+        }
+      }
+      // the other pair overwrites the area next; after the second turn the
+      // walk's first barrier follows
+      if (rp == 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
   };
   auto start_first_walk = [&](int nt, bool fresh) __attribute__((always_inline)) {
     const int hq = head_ok ? head : p.heads - 1;  // a masked head reads a real one, scaled by 0
     const int64_t qp = r * p.q_rs + int64_t(hq) * p.q_hs;
+    uint32_t hw[NH][8], lw[NH][8];
+    int code[NH];
     if (p.q_fp8) {
-      u32x4 raw[NSTEP][2];
+      u32x4 raw[NH][2];
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st)
+      for (int i = 0; i < NH; ++i)
 #pragma unroll
         for (int d = 0; d < 2; ++d)
-          raw[st][d] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + qp +
-                                                       q_col(st, d));
+          raw[i][d] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + qp +
+                                                      q_col(min(2 * i + kh, NSTEP - 1), d));
       start_walk(nt, fresh);
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
+      for (int i = 0; i < NH; ++i) {
         u32x4 bf[2][2];
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
-          const u32x2 a = widen_fp8x4(raw[st][d][0]), b = widen_fp8x4(raw[st][d][1]);
-          const u32x2 c = widen_fp8x4(raw[st][d][2]), e = widen_fp8x4(raw[st][d][3]);
+          const u32x2 a = widen_fp8x4(raw[i][d][0]), b = widen_fp8x4(raw[i][d][1]);
+          const u32x2 c = widen_fp8x4(raw[i][d][2]), e = widen_fp8x4(raw[i][d][3]);
           bf[d][0] = u32x4{a.x, a.y, b.x, b.y};
           bf[d][1] = u32x4{c.x, c.y, e.x, e.y};
         }
-        split_q(st, bf);
+        code[i] = split_terms(bf, hw[i], lw[i]);
       }
     } else {
-      u32x4 raw[NSTEP][2][2];
+      u32x4 raw[NH][2][2];
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st)
+      for (int i = 0; i < NH; ++i)
 #pragma unroll
         for (int d = 0; d < 2; ++d)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf)
-            raw[st][d][hf] = *reinterpret_cast<const u32x4*>(p.q + qp + q_col(st, d) + 8 * hf);
+            raw[i][d][hf] = *reinterpret_cast<const u32x4*>(
+                p.q + qp + q_col(min(2 * i + kh, NSTEP - 1), d) + 8 * hf);
       start_walk(nt, fresh);
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) split_q(st, raw[st]);
+      for (int i = 0; i < NH; ++i) code[i] = split_terms(raw[i], hw[i], lw[i]);
     }
+    swap_q(hw, lw, code);
   };
   const float kv_scale = *p.kv_scale;
   const float cscale = p.sm_log2 * q_scale_of(p.q_scale) * kv_scale;
@@ -553,12 +610,9 @@ prefill_mx_kernel(const FwdParams p) {
   // kXMaxDrift above the pair's first valid tile's maximum) starts from the
   // first walk's final references, which no later score exceeds by
   // 2^kXLimit.
-  // Walks carry one stream of tiles through the rings: gbase is the stream
-  // position of a walk's first tile. A streaming walk (`stream`) requests,
-  // in its last steps, the indices and first tiles of the next item's walk
-  // instead of tiles past its end.
+  // A streaming walk (`stream`) requests, in its last steps, the indices and
+  // first tiles of the next item's walk instead of tiles past its end.
   const int nt = t_end - t_begin;
-  int gbase = 0;
   auto walk = [&](bool first, bool fresh, bool stream) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] = floatx16{};
