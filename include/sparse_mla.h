@@ -78,8 +78,9 @@ typedef struct smla_options {
   int32_t variant;         /* kernel instance; 0 = the planner's choice: the 16-head
                               decode kernel over fp8 pools (H <= 32), the staged-tile
                               kernel (16 and 32 heads over bf16 pools; 64 heads over
-                              bf16 pools), for 64 heads over fp8 pools the 4-wave
-                              kernel (576-wide rows) or the fp8-dot kernel (512-wide).
+                              bf16 pools), for 64 heads over fp8 pools the fp8-dot
+                              kernel (the 4-wave kernel where it cannot address the
+                              pool).
                               1 = the staged-tile kernel (any head block; also what
                               pools past the 32-bit buffer range use). 2 = 64 heads
                               only: the 8-wave double-buffered kernel. 3 = 64 heads

@@ -16,8 +16,9 @@
 //    it measured 3-14 % faster than the 8-wave kernel of prefill.hip on
 //    every 64-head bf16 shape tried (96..2048 rows, top-k 512 and 2048;
 //    55.3 against 63.2 us on the 192-row decode), which stays as variant 2.
-//    Over fp8 pools 64-head blocks of 512-wide rows take the fp8-dot kernel
-//    (variant 3), 576-wide rows the 4-wave kernel (variant 0).
+//    Over fp8 pools 64-head blocks take the fp8-dot kernel (variant 3)
+//    where its structured buffer can address the pool, else the 4-wave
+//    kernel (variant 0; variant 4 forces it).
 //  * splits: when rows x head blocks leave the CUs' workgroup slots
 //    underfilled, each row's slots are split if a makespan model (rounds of
 //    workgroups x (tiles per split + a fixed per-workgroup cost) + the
@@ -77,10 +78,10 @@ int make_plan(const Problem& pb, const smla_options* opt, int num_cus, smla_plan
     variant = opt->variant == 4 ? 0 : opt->variant;
   } else if (hb == 64 && !pb.kv_fp8) {
     variant = 1;
-  } else if (hb == 64 && pb.dqk == 512) {
-    // 512-wide fp8 rows: the fp8-dot kernel, measured 1.5-4.4 % faster than
-    // the 4-wave kernel on the 8192-row, top-k 2048 prefill across boxes
-    // (576-wide rows: within 1 % either way, so the 4-wave kernel stays).
+  } else if (hb == 64) {
+    // 64-head blocks over fp8 pools: the fp8-dot kernel, measured faster
+    // than the 4-wave kernel on both prefill shapes in same-box runs (6 %
+    // on the 16384-row 512-wide one, 1.2 % on the 8192-row 576-wide one).
     variant = 3;
   }
   // The decode (16 heads, fp8) and 64-head kernels read the pool through a

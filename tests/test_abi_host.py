@@ -150,9 +150,9 @@ def test_plan_head_block_choice_and_overrides():
     # 64 heads over bf16 pools: the staged-tile kernel unless overridden
     assert _plan(192, 64, K=512, dtype=torch.bfloat16)["variant"] == 1
     assert _plan(192, 64, K=512, dtype=torch.bfloat16, variant=2)["variant"] == 2
-    # 64 heads over fp8 pools: the 4-wave kernel for 576-wide rows, the
-    # fp8-dot kernel for 512-wide rows; 4 forces the 4-wave kernel
-    assert _plan(8192, 64)["variant"] == 0
+    # 64 heads over fp8 pools: the fp8-dot kernel (variant 3) for both row
+    # widths; 4 forces the 4-wave kernel (reported as variant 0)
+    assert _plan(8192, 64)["variant"] == 3
     assert _plan(8192, 64, D=512)["variant"] == 3
     assert _plan(8192, 64, D=512, variant=4)["variant"] == 0
     assert _plan(8192, 64)["head_block"] == 64

@@ -209,8 +209,9 @@ PATHS = [
     ("fp8", 576, 16, 512, {}),                                  # decode kernel
     ("fp8", 512, 16, 300, dict(head_block=16, splits=3)),       # decode, split-K: combine
     ("fp8", 576, 20, 256, {}),                                  # 16-head blocks, one partial
-    ("fp8", 576, 64, 512, {}),                                  # 64-head fp8 kernel
-    ("fp8", 512, 64, 300, {}),
+    ("fp8", 576, 64, 512, {}),                                  # 64-head fp8 default (fp8-dot)
+    ("fp8", 512, 64, 300, dict(variant=4)),                     # 4-wave 64-head fp8 kernel
+    ("fp8", 576, 64, 512, dict(variant=4)),
     ("fp8", 576, 64, 512, dict(variant=2)),                     # 8-wave kernel over fp8
     ("fp8", 576, 64, 512, dict(variant=3)),                     # fp8-dot kernel
     ("fp8", 512, 64, 300, dict(variant=3, head_block=64, splits=2)),  # fp8-dot, combine
