@@ -463,15 +463,17 @@ prefill_mx_kernel(const FwdParams p) {
   // the k-steps st = 2i + kh (for an odd count, wave 1's last one is a
   // placeholder), and the pair swaps them through LDS that is free while a
   // walk starts: the ring place of the walk's fourth tile (k-steps 0..7,
-  // 4 KB each: this lane's 64 bytes) and the P-exchange area (k-step 8, the
-  // placeholder and the scale codes). The area holds one pair's terms, so
-  // the pairs take turns. A wave reads back all k-steps (its own too), which
-  // keeps every register index compile-time.
+  // 4 KB each as four 1 KB quarters [quarter][lane] of 16 bytes, so that
+  // every access is contiguous and free of bank conflicts) and the
+  // P-exchange area (k-step 8, the placeholder and the scale codes). The
+  // area holds one pair's terms, so the pairs take turns. A wave reads back
+  // all k-steps (its own too), which keeps every register index
+  // compile-time.
   constexpr int NH = (NSTEP + 1) / 2;
   auto xq_terms = [&](int st) -> u32x4* {
     uint8_t* const base = st < 8 ? smem + ((gbase + 3) % kXRing) * C::NOPE + st * 4096
                                  : smem + C::OFF_XP + (st - 8) * 4096;
-    return reinterpret_cast<u32x4*>(base + lane * 64);
+    return reinterpret_cast<u32x4*>(base) + lane;  // quarter k at [64 k]
   };
   auto xq_code = [&](int st) -> int* {
     return reinterpret_cast<int*>(smem + C::OFF_XP + 2 * 4096 + (st * 64 + lane) * 4);
@@ -485,9 +487,9 @@ prefill_mx_kernel(const FwdParams p) {
         for (int i = 0; i < NH; ++i) {
           u32x4* const t = xq_terms(2 * i + kh);
           t[0] = u32x4{hw[i][0], hw[i][1], hw[i][2], hw[i][3]};
-          t[1] = u32x4{hw[i][4], hw[i][5], hw[i][6], hw[i][7]};
-          t[2] = u32x4{lw[i][0], lw[i][1], lw[i][2], lw[i][3]};
-          t[3] = u32x4{lw[i][4], lw[i][5], lw[i][6], lw[i][7]};
+          t[64] = u32x4{hw[i][4], hw[i][5], hw[i][6], hw[i][7]};
+          t[128] = u32x4{lw[i][0], lw[i][1], lw[i][2], lw[i][3]};
+          t[192] = u32x4{lw[i][4], lw[i][5], lw[i][6], lw[i][7]};
           *xq_code(2 * i + kh) = code[i];
         }
       }
@@ -496,7 +498,7 @@ prefill_mx_kernel(const FwdParams p) {
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
           const u32x4* const t = xq_terms(st);
-          const u32x4 tt[4] = {t[0], t[1], t[2], t[3]};
+          const u32x4 tt[4] = {t[0], t[64], t[128], t[192]};
           set_q(st, tt, *xq_code(st));
         }
       }
