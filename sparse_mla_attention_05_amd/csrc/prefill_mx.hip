@@ -126,6 +126,11 @@ struct XCfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
+// Ring places of stream position t >= 0 (unsigned: one mask for the
+// power-of-two ring, no sign fix-up).
+__device__ __forceinline__ int ring(int t) { return int(uint32_t(t) % uint32_t(kXRing)); }
+__device__ __forceinline__ int rope_ring(int t) { return int(uint32_t(t) % uint32_t(kXRopeRing)); }
+
 // Tile row of slot s (within each group of 16 rows, row 2k + e holds slot
 // 8e + k).
 __device__ __forceinline__ int row_of_slot(int s) {
@@ -311,7 +316,7 @@ prefill_mx_kernel(const FwdParams p) {
   // instruction. Every wave issues it (the same bytes to the same place), so
   // that no branch splits the code around it.
   auto idx_dma = [&](int tt, int t, const i32x4& rsrc) {
-    dma4(rsrc, lds0 + C::OFF_IDX + (tt % kXRing) * kXTile * 4, uint32_t(4 * (t * kXTile + lane)));
+    dma4(rsrc, lds0 + C::OFF_IDX + ring(tt) * kXTile * 4, uint32_t(4 * (t * kXTile + lane)));
   };
   // This lane's slots of a tile (relative to 16 * wave): the DMA slots
   // 8h + k (k < 8; rows 2k + h), the rope slot of rope row lane / 4, the
@@ -323,7 +328,7 @@ prefill_mx_kernel(const FwdParams p) {
   // invalid, with selects rather than a branch; then slot indices of a
   // paged pool are mapped to rows of page_rows.
   auto read_idx = [&](int tt, int t) {
-    const int32_t* ir = idx_ring + (tt % kXRing) * kXTile + 16 * wave;
+    const int32_t* ir = idx_ring + ring(tt) * kXTile + 16 * wave;
     const u32x4 a = *reinterpret_cast<const u32x4*>(ir + 8 * h);
     const u32x4 b = *reinterpret_cast<const u32x4*>(ir + 8 * h + 4);
 #pragma unroll
@@ -358,14 +363,14 @@ prefill_mx_kernel(const FwdParams p) {
   constexpr int kPieces = 10;
   auto dma_piece = [&](int tt, int k) {
     if (k < 8) {
-      dma16(pool_rsrc, lds0 + (tt % kXRing) * C::NOPE + 16 * wave * kXRow + 2 * k * kXRow, idn[k],
+      dma16(pool_rsrc, lds0 + ring(tt) * C::NOPE + 16 * wave * kXRow + 2 * k * kXRow, idn[k],
             16u * uint32_t((lane & 31) ^ nope_perm(2 * k + h)));
     } else if (k == 8) {
       if constexpr (ROPE)
-        dma16(pool_rsrc, lds0 + C::OFF_ROPE + (tt % kXRopeRing) * C::ROPEB + 16 * wave * kXRope,
+        dma16(pool_rsrc, lds0 + C::OFF_ROPE + rope_ring(tt) * C::ROPEB + 16 * wave * kXRope,
               idr, dma_rope);
     } else {
-      kbias[(tt % kXRing) * kXTile + 16 * wave + (lane & 15)] = idb >= 0 ? 0.f : kNegInf;
+      kbias[ring(tt) * kXTile + 16 * wave + (lane & 15)] = idb >= 0 ? 0.f : kNegInf;
     }
   };
   auto issue_dma = [&](int tt) {
@@ -471,7 +476,7 @@ prefill_mx_kernel(const FwdParams p) {
   // compile-time.
   constexpr int NH = (NSTEP + 1) / 2;
   auto xq_terms = [&](int st) -> u32x4* {
-    uint8_t* const base = st < 8 ? smem + ((gbase + 3) % kXRing) * C::NOPE + st * 4096
+    uint8_t* const base = st < 8 ? smem + ring(gbase + 3) * C::NOPE + st * 4096
                                  : smem + C::OFF_XP + (st - 8) * 4096;
     return reinterpret_cast<u32x4*>(base) + lane;  // quarter k at [64 k]
   };
@@ -583,9 +588,9 @@ prefill_mx_kernel(const FwdParams p) {
   int kro_i = kro, kperm_i = kperm, rro_i = rro, rperm_i = rperm;  // refreshed per tile
   auto kread = [&](int tt, int st, int d) -> u32x4 {
     if (ROPE && st == NNOPE)
-      return *reinterpret_cast<const u32x4*>(smem + C::OFF_ROPE + (tt % kXRopeRing) * C::ROPEB +
+      return *reinterpret_cast<const u32x4*>(smem + C::OFF_ROPE + rope_ring(tt) * C::ROPEB +
                                              rro_i + 16 * ((2 * d + h) ^ rperm_i));
-    return *reinterpret_cast<const u32x4*>(smem + (tt % kXRing) * C::NOPE + kro_i +
+    return *reinterpret_cast<const u32x4*>(smem + ring(tt) * C::NOPE + kro_i +
                                            16 * ((4 * st + 2 * d + h) ^ kperm_i));
   };
   // One k-step of S^T: both terms of q against one key fragment.
@@ -596,7 +601,7 @@ prefill_mx_kernel(const FwdParams p) {
   };
   // Slot flags (0 or -inf) of this lane's 16 slots of the walk's tile tt.
   auto read_bias = [&](int tt, floatx4 (&b)[4]) {
-    const float* kb = kbias + (tt % kXRing) * kXTile + 32 * kh + 4 * h;
+    const float* kb = kbias + ring(tt) * kXTile + 32 * kh + 4 * h;
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const floatx4*>(kb + 8 * j);
   };
@@ -795,7 +800,7 @@ prefill_mx_kernel(const FwdParams p) {
       // The values of the first two column blocks (tile tt has been in the
       // ring since the last barrier): read before this one, so that only
       // the partner's P is read after it.
-      const uint8_t* const vb = smem + (g % kXRing) * C::NOPE;
+      const uint8_t* const vb = smem + ring(g) * C::NOPE;
       // Value fragment (block m, read v): keys of this wave's own half for
       // v < 2, the partner's for v >= 2, the order of the P^T bytes below.
       auto vread = [&](int m, int v) -> u32x2 {
@@ -871,7 +876,7 @@ prefill_mx_kernel(const FwdParams p) {
             const int j = 2 * m + term;
             if (j < kPieces) dma_piece(g + 3, j);
             if (j == kPieces) idx_dma(g + 5, t5, x5 ? idx_rsrc_next : idx_rsrc);
-            if (j == 11) dma4(pf_rsrc, lds0 + C::OFF_BIAS + (g % kXRing) * kXTile * 4, pf_off);
+            if (j == 11) dma4(pf_rsrc, lds0 + C::OFF_BIAS + ring(g) * kXTile * 4, pf_off);
             if (j == 12) make_bn(g + 1);
             __builtin_amdgcn_sched_barrier(0);
           }
