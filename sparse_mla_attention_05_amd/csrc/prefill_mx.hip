@@ -465,23 +465,22 @@ prefill_mx_kernel(const FwdParams p) {
     sbl[st / 4] = (sbl[st / 4] & ~(0xFF << sh)) | ((code - 4) << sh);
   };
   // The two waves of a pair need the same q terms: wave kh loads and splits
-  // the k-steps st = 2i + kh (for an odd count, wave 1's last one is a
-  // placeholder), and the pair swaps them through LDS that is free while a
-  // walk starts: the ring place of the walk's fourth tile (k-steps 0..7,
-  // 4 KB each as four 1 KB quarters [quarter][lane] of 16 bytes, so that
-  // every access is contiguous and free of bank conflicts) and the
-  // P-exchange area (k-step 8, the placeholder and the scale codes). The
-  // area holds one pair's terms, so the pairs take turns. A wave reads back
-  // all k-steps (its own too), which keeps every register index
-  // compile-time.
-  constexpr int NH = (NSTEP + 1) / 2;
+  // the k-steps st = 2i + kh, and the pair swaps them through LDS that is
+  // free while a walk starts: the ring place of the walk's fourth tile
+  // (k-steps 0..7, 4 KB each as four 1 KB quarters [quarter][lane] of 16
+  // bytes, so that every access is contiguous and free of bank conflicts)
+  // and the P-exchange area (the scale codes). The area holds one pair's
+  // terms, so the pairs take turns. A wave reads back all swapped k-steps
+  // (its own too), which keeps every register index compile-time. An odd
+  // last k-step (the rope columns of a 576-wide row) is loaded and split by
+  // both waves and set from registers, outside the swap.
+  constexpr int NH = (NSTEP + 1) / 2;  // k-steps a wave loads and splits
+  constexpr int NX = NSTEP / 2;        // of them, swapped
   auto xq_terms = [&](int st) -> u32x4* {
-    uint8_t* const base = st < 8 ? smem + ring(gbase + 3) * C::NOPE + st * 4096
-                                 : smem + C::OFF_XP + (st - 8) * 4096;
-    return reinterpret_cast<u32x4*>(base) + lane;  // quarter k at [64 k]
+    return reinterpret_cast<u32x4*>(smem + ring(gbase + 3) * C::NOPE + st * 4096) + lane;  // quarter k at [64 k]
   };
   auto xq_code = [&](int st) -> int* {
-    return reinterpret_cast<int*>(smem + C::OFF_XP + 2 * 4096 + (st * 64 + lane) * 4);
+    return reinterpret_cast<int*>(smem + C::OFF_XP + (st * 64 + lane) * 4);
   };
   auto swap_q = [&](const uint32_t (&hw)[NH][8], const uint32_t (&lw)[NH][8], const int (&code)[NH])
       __attribute__((always_inline)) {
@@ -489,7 +488,7 @@ prefill_mx_kernel(const FwdParams p) {
     for (int rp = 0; rp < 2; ++rp) {
       if (hp == rp) {
 #pragma unroll
-        for (int i = 0; i < NH; ++i) {
+        for (int i = 0; i < NX; ++i) {
           u32x4* const t = xq_terms(2 * i + kh);
           t[0] = u32x4{hw[i][0], hw[i][1], hw[i][2], hw[i][3]};
           t[64] = u32x4{hw[i][4], hw[i][5], hw[i][6], hw[i][7]};
@@ -501,7 +500,7 @@ prefill_mx_kernel(const FwdParams p) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (hp == rp) {
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
+        for (int st = 0; st < 2 * NX; ++st) {
           const u32x4* const t = xq_terms(st);
           const u32x4 tt[4] = {t[0], t[64], t[128], t[192]};
           set_q(st, tt, *xq_code(st));
@@ -553,6 +552,13 @@ prefill_mx_kernel(const FwdParams p) {
       for (int i = 0; i < NH; ++i) code[i] = split_terms(raw[i], hw[i], lw[i]);
     }
     swap_q(hw, lw, code);
+    if constexpr (NH > NX) {
+      const u32x4 t[4] = {u32x4{hw[NX][0], hw[NX][1], hw[NX][2], hw[NX][3]},
+                          u32x4{hw[NX][4], hw[NX][5], hw[NX][6], hw[NX][7]},
+                          u32x4{lw[NX][0], lw[NX][1], lw[NX][2], lw[NX][3]},
+                          u32x4{lw[NX][4], lw[NX][5], lw[NX][6], lw[NX][7]}};
+      set_q(NSTEP - 1, t, code[NX]);
+    }
   };
   const float kv_scale = *p.kv_scale;
   const float cscale = p.sm_log2 * q_scale_of(p.q_scale) * kv_scale;
