@@ -22,7 +22,8 @@ prefills on every 64th row, scaled to the whole call). The two decodes are
 timed again with their heads split over two GPUs (32 heads: one GPU's share)
 under "head_share", as two-segment calls (a seeded 128-slot sliding window over
 a second pool with its own scale, next to the same workload's one-segment
-time) under "two_segment", and with the output epilogue (inverse RoPE of the
+time; the fp8 prefill too, whose 64-head kernel composes the two segments
+through the combine kernel) under "two_segment", and with the output epilogue (inverse RoPE of the
 last 64 columns and an MXFP8 store) fused into the forward's store, next to
 the plain forward followed by the separate epilogue pass, under "epilogue".
 The headline decode is timed again on a pool that does not fit the MALL (each
@@ -61,7 +62,7 @@ def attention_kernel(plan, d_qk, fp8):
         if fp8 and v == 0:
             return f"smla::prefill_fp8_kernel<{d_qk}, false>", "prefill_fp8.hip"
         if fp8 and v == 3:
-            return f"smla::prefill_mx_kernel<{d_qk}, false, false>", "prefill_mx.hip"
+            return f"smla::prefill_mx_kernel<{d_qk}, false, false, false>", "prefill_mx.hip"
         return f"smla::prefill_kernel<{d_qk}, {str(fp8).lower()}, false>", "prefill.hip"
     return f"smla::fwd_kernel (staged tile, {hb} heads)", "kernels.hip"
 
@@ -81,7 +82,7 @@ def parse():
     ap.add_argument("--head-share", default="decode_bf16_h32,decode_fp8_h32",
                     help="decode workloads with 32 heads (one GPU's share of a two-way head "
                          "split) ('' for none)")
-    ap.add_argument("--two-segment", default="decode_bf16,decode_fp8",
+    ap.add_argument("--two-segment", default="decode_bf16,decode_fp8,prefill_fp8",
                     help="comma list of workloads also timed with a sliding-window second "
                          "segment ('' for none)")
     ap.add_argument("--window", type=int, default=128, help="slots of that second segment")
@@ -482,15 +483,21 @@ def main():
         line["sensitivity"] = sens
     two = []
     for name in [s_ for s_ in args.two_segment.split(",") if s_]:
-        r = time_workload(name, args.steps, 3, cold, window=args.window)
-        one = time_workload(name, args.steps, 3, cold)
+        prefill = name.startswith("prefill")
+        k = max(3, args.steps // 2) if prefill else args.steps
+        r = time_workload(name, k, 3, cold, window=args.window)
+        one = time_workload(name, k, 3, cold)
         tus = statistics.median(r["times"])
         ous = statistics.median(one["times"])
-        two.append({"workload": name, "window": args.window, "us_per_call": round(tus, 1),
-                    "one_segment_us_per_call": round(ous, 1),
-                    "gathered_kv_tbs": round(r["alg"]["kv_bytes"] / (tus * 1e-6) / 1e12, 2),
-                    "hbm_frac": round(r["alg"]["bytes"] / (tus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                    "warm_us_per_call": round(r["warm_us"], 1), "plan": r["plan"]})
+        rec = {"workload": name, "window": args.window, "us_per_call": round(tus, 1),
+               "one_segment_us_per_call": round(ous, 1),
+               "gathered_kv_tbs": round(r["alg"]["kv_bytes"] / (tus * 1e-6) / 1e12, 2)}
+        if prefill:
+            rec["mfma_frac"] = round(r["alg"]["flops"] / (tus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        else:
+            rec["hbm_frac"] = round(r["alg"]["bytes"] / (tus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        rec.update({"warm_us_per_call": round(r["warm_us"], 1), "plan": r["plan"]})
+        two.append(rec)
         del r, one
     if two:
         line["two_segment"] = two

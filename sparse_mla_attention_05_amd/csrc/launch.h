@@ -203,7 +203,8 @@ inline bool uses_decode_kernel(int head_block, bool fp8, int variant) {
 // prefill.hip over bf16 pools (the main segment padded to whole tiles).
 inline bool walks_second_segment(int head_block, bool fp8, int variant) {
   return uses_decode_kernel(head_block, fp8, variant) ||
-         (head_block == 64 && !fp8 && (variant == 0 || variant == 2));
+         (head_block == 64 && !fp8 && (variant == 0 || variant == 2)) ||
+         (head_block == 64 && fp8 && variant == 3);
 }
 
 inline bool uses_buffer_range(int head_block, bool fp8, int variant) {

@@ -128,6 +128,9 @@ struct XCfg {
 
 // Ring places of stream position t >= 0 (unsigned: one mask for the
 // power-of-two ring, no sign fix-up).
+// One of two buffer descriptors by value (a select of the values, not of
+// their addresses, which would keep them in memory).
+__device__ __forceinline__ i32x4 sel4(bool c, i32x4 a, i32x4 b) { return c ? a : b; }
 __device__ __forceinline__ int ring(int t) { return int(uint32_t(t) % uint32_t(kXRing)); }
 __device__ __forceinline__ int rope_ring(int t) { return int(uint32_t(t) % uint32_t(kXRopeRing)); }
 
@@ -239,8 +242,10 @@ __device__ __forceinline__ void sync_tile() {
 }
 
 // PAGED: slot indices of a paged pool are mapped to rows (a separate
-// instance, so the plain pool's walk carries none of it).
-template <int DQK, bool EPI, bool PAGED>
+// instance, so the plain pool's walk carries none of it). TWO: the walk
+// continues over a second segment (its own 2-D pool, scale and index rows)
+// after the main top-k, as one list of tiles (a separate instance too).
+template <int DQK, bool EPI, bool PAGED, bool TWO>
 __global__ void __launch_bounds__(kXWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 prefill_mx_kernel(const FwdParams p) {
   using C = XCfg<DQK>;
@@ -290,15 +295,25 @@ prefill_mx_kernel(const FwdParams p) {
 
   int head = hblk * 64 + 32 * hp + c32;
   bool head_ok = head < p.heads;
-  const int ntiles = (p.topk + kXTile - 1) / kXTile;
+  // Tiles [0, T1) hold the main top-k (its last one padded with invalid
+  // slots), tiles [T1, ntiles) the second segment when one is walked; the
+  // splits partition that list.
+  const int T1 = (p.topk + kXTile - 1) / kXTile;
+  const int ntiles = TWO ? T1 + (p.topk2 + kXTile - 1) / kXTile : T1;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(ntiles, t_begin + p.tiles_per_split);
   const int slot_end = min(p.topk, t_end * kXTile);
+  const int slot_end2 = TWO ? max(0, min(p.topk2, (t_end - T1) * kXTile)) : 0;
+  auto in_second = [&](int t) { return TWO && t >= T1; };  // tile t of the second segment
 
   // ---- index rows and the tile DMA
   auto idx_rsrc_of = [&](int64_t row) { return make_rsrc(p.idx + row * p.idx_rs, 0, 4u * uint32_t(slot_end)); };
-  i32x4 idx_rsrc = idx_rsrc_of(r);
-  i32x4 idx_rsrc_next = idx_rsrc;  // the next item's, while the walk streams into it
+  auto idx2_rsrc_of = [&](int64_t row) {
+    return TWO ? make_rsrc(p.idx2 + row * p.idx2_rs, 0, 4u * uint32_t(slot_end2)) : make_rsrc(p.idx, 0, 0u);
+  };
+  i32x4 idx_rsrc = idx_rsrc_of(r), idx2_rsrc = idx2_rsrc_of(r);
+  // the next item's, while the walk streams into it
+  i32x4 idx_rsrc_next = idx_rsrc, idx2_rsrc_next = idx2_rsrc;
   // The next item's q rows (64 heads of a row, contiguous when the heads
   // are), fetched into the L2 during the walk's last steps: one dword per
   // 64 bytes. A zero-record resource fetches nothing.
@@ -307,22 +322,30 @@ prefill_mx_kernel(const FwdParams p) {
   const uint32_t rs = uint32_t(p.pool_rs_bytes);
   const uint32_t records = p.pool_bytes >= uint32_t(DQK) ? (p.pool_bytes - DQK) / rs + 1 : 0u;
   const i32x4 pool_rsrc = make_rsrc(p.pool, rs, records);
+  const uint32_t rs2 = TWO ? uint32_t(p.pool2_rs_bytes) : rs;
+  const uint32_t records2 =
+      TWO ? (p.pool2_bytes >= uint32_t(DQK) ? (p.pool2_bytes - DQK) / rs2 + 1 : 0u) : records;
+  const i32x4 pool2_rsrc = TWO ? make_rsrc(p.pool2, rs2, records2) : pool_rsrc;
   const uint32_t page_rows = PAGED ? uint32_t(p.page_bytes / p.pool_rs_bytes) : 0u;
   const uint32_t lds0 = lds_addr(smem);
   const int32_t* const idx_ring = reinterpret_cast<const int32_t*>(smem + C::OFF_IDX);
 
-  // The indices of tile t of the row of `rsrc` (64 of them; past slot_end
-  // the range check reads 0) to the index ring at stream position tt; one
-  // instruction. Every wave issues it (the same bytes to the same place), so
-  // that no branch splits the code around it.
-  auto idx_dma = [&](int tt, int t, const i32x4& rsrc) {
-    dma4(rsrc, lds0 + C::OFF_IDX + ring(tt) * kXTile * 4, uint32_t(4 * (t * kXTile + lane)));
+  // The indices of tile t of the row of `rm` (main segment) or `rx` (second
+  // segment) (64 of them; past the segment's slot end the range check reads
+  // 0) to the index ring at stream position tt; one instruction. Every wave
+  // issues it (the same bytes to the same place), so that no branch splits
+  // the code around it.
+  auto idx_dma = [&](int tt, int t, i32x4 rm, i32x4 rx) {
+    const bool x = in_second(t);
+    const i32x4 rsrc = sel4(x, rx, rm);
+    dma4(rsrc, lds0 + C::OFF_IDX + ring(tt) * kXTile * 4, uint32_t(4 * ((x ? t - T1 : t) * kXTile + lane)));
   };
   // This lane's slots of a tile (relative to 16 * wave): the DMA slots
   // 8h + k (k < 8; rows 2k + h), the rope slot of rope row lane / 4, the
   // flag slot lane % 16.
   const int rope_slot = 8 * ((lane >> 2) & 1) + ((lane >> 3) & 7);
   int idn[8], idr = -1, idb;
+  bool idn_x = false;  // the indices in idn are the second segment's
   // The lane's indices of tile t (ring place tt) from the ring; slots past
   // the split's end (all of them for a tile past the walk's end) are marked
   // invalid, with selects rather than a branch; then slot indices of a
@@ -338,12 +361,15 @@ prefill_mx_kernel(const FwdParams p) {
     }
     if constexpr (ROPE) idr = ir[rope_slot];
     idb = ir[lane & 15];
-    const int base = t * kXTile + 16 * wave;
-    if (base + 16 > slot_end) {
+    const bool x = in_second(t);
+    if constexpr (TWO) idn_x = x;
+    const int base = (x ? t - T1 : t) * kXTile + 16 * wave;
+    const int se = x ? slot_end2 : slot_end;
+    if (base + 16 > se) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) idn[k] = base + 8 * h + k < slot_end ? idn[k] : -1;
-      if constexpr (ROPE) idr = base + rope_slot < slot_end ? idr : -1;
-      idb = base + (lane & 15) < slot_end ? idb : -1;
+      for (int k = 0; k < 8; ++k) idn[k] = base + 8 * h + k < se ? idn[k] : -1;
+      if constexpr (ROPE) idr = base + rope_slot < se ? idr : -1;
+      idb = base + (lane & 15) < se ? idb : -1;
     }
     if constexpr (PAGED) {
       auto map = [&](int i) -> int {
@@ -362,12 +388,13 @@ prefill_mx_kernel(const FwdParams p) {
   const uint32_t dma_rope = 512u + 16u * uint32_t((lane & 3) ^ ((lane >> 4) & 3));
   constexpr int kPieces = 10;
   auto dma_piece = [&](int tt, int k) {
+    const i32x4 prs = sel4(TWO && idn_x, pool2_rsrc, pool_rsrc);
     if (k < 8) {
-      dma16(pool_rsrc, lds0 + ring(tt) * C::NOPE + 16 * wave * kXRow + 2 * k * kXRow, idn[k],
+      dma16(prs, lds0 + ring(tt) * C::NOPE + 16 * wave * kXRow + 2 * k * kXRow, idn[k],
             16u * uint32_t((lane & 31) ^ nope_perm(2 * k + h)));
     } else if (k == 8) {
       if constexpr (ROPE)
-        dma16(pool_rsrc, lds0 + C::OFF_ROPE + rope_ring(tt) * C::ROPEB + 16 * wave * kXRope,
+        dma16(prs, lds0 + C::OFF_ROPE + rope_ring(tt) * C::ROPEB + 16 * wave * kXRope,
               idr, dma_rope);
     } else {
       kbias[ring(tt) * kXTile + 16 * wave + (lane & 15)] = idb >= 0 ? 0.f : kNegInf;
@@ -385,7 +412,7 @@ prefill_mx_kernel(const FwdParams p) {
     if (fresh) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
-        if (tt < nt) idx_dma(tt, t_begin + tt, idx_rsrc);
+        if (tt < nt) idx_dma(tt, t_begin + tt, idx_rsrc, idx2_rsrc);
     }
     sync_tile();
     if (fresh) {
@@ -396,7 +423,7 @@ prefill_mx_kernel(const FwdParams p) {
           issue_dma(tt);  // waits for the read: ring place tt may be refilled after this
         }
       }
-      if (nt > 4) idx_dma(4, t_begin + 4, idx_rsrc);
+      if (nt > 4) idx_dma(4, t_begin + 4, idx_rsrc, idx2_rsrc);
     }
   };
 
@@ -562,6 +589,19 @@ prefill_mx_kernel(const FwdParams p) {
   };
   const float kv_scale = *p.kv_scale;
   const float cscale = p.sm_log2 * q_scale_of(p.q_scale) * kv_scale;
+  // The second segment's scale (its own, else the main one). With two
+  // segments O is kept in units of the larger scale s_ref: a tile's weights
+  // (the numerator's P) are taken times its segment's scale / s_ref, as
+  // 2^(x + lr) with lr = log2 of that ratio (at least -100, so that a zero
+  // scale gives weights of 2^-100 rather than 0), and its row sum times
+  // 2^-lr, so that the denominator and the LSE see the plain weights.
+  // Scales are dequantisation scales: nonnegative.
+  const float kv_scale2 = TWO && p.kv_scale2 != nullptr ? *p.kv_scale2 : kv_scale;
+  const float cscale2 = p.sm_log2 * q_scale_of(p.q_scale) * kv_scale2;
+  const float s_ref = TWO ? fmaxf(kv_scale, kv_scale2) : kv_scale;
+  auto lr_of = [&](float sc) { return s_ref > 0.f ? fmaxf(__log2f(sc / s_ref), -100.f) : 0.f; };
+  const float lr1 = TWO ? lr_of(kv_scale) : 0.f, lr2 = TWO ? lr_of(kv_scale2) : 0.f;
+  const float lq1 = TWO ? __builtin_amdgcn_exp2f(-lr1) : 1.f, lq2 = TWO ? __builtin_amdgcn_exp2f(-lr2) : 1.f;
 
   // ---- per-lane LDS offsets (without the tile's base)
   // keys: this lane's score row is slot 32kh + c32; k-step st, half d reads
@@ -652,13 +692,16 @@ prefill_mx_kernel(const FwdParams p) {
     // carried from one step to the next: slot flag - m_w of the next tile's
     // 16 slots of this lane
     float bn[4][4];
-    auto make_bn = [&](int tt) {
+    // (tt: the tile's ring position, t: its tile number)
+    auto make_bn = [&](int tt, int t) {
       floatx4 b[4];
       read_bias(tt, b);
+      float a = nm;
+      if constexpr (TWO) a += in_second(t) ? lr2 : lr1;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) bn[i / 4][i % 4] = b[i / 4][i % 4] + nm;
+      for (int i = 0; i < 16; ++i) bn[i / 4][i % 4] = b[i / 4][i % 4] + a;
     };
-    make_bn(gbase);
+    make_bn(gbase, t_begin);
     for (int tt = 0; tt < nt; ++tt) {
       const int g = gbase + tt;  // stream position: ring places
       const int par = g & 1;
@@ -681,10 +724,12 @@ prefill_mx_kernel(const FwdParams p) {
       // codes. A stage depends only on earlier stages of its group.
       float x[16], w[16], m4[4], l4[4], ra[4][4];
       uint32_t hw[4];
+      const bool second = in_second(t_begin + tt);
+      const float cs_t = second ? cscale2 : cscale;
       auto stage = [&](int st, int g) {
         if (st == 0) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) x[4 * g + u] = __builtin_fmaf(s_cur[4 * g + u], cscale, bn[g][u]);
+          for (int u = 0; u < 4; ++u) x[4 * g + u] = __builtin_fmaf(s_cur[4 * g + u], cs_t, bn[g][u]);
         } else if (st == 1) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) w[4 * g + u] = __builtin_amdgcn_exp2f(x[4 * g + u]);
@@ -848,7 +893,7 @@ prefill_mx_kernel(const FwdParams p) {
       redo |= int(ref && ((m_blk - m_o > kXMaxDrift) || (m_w - m_o > kXMaxDrift)));
       const float d_blk = ref ? fminf(fmaxf(m_blk - m_o, kXMinDrift), kXMaxDrift) : 0.f;
       const float d_own = ref ? fminf(fmaxf(m_w - m_o, kXMinDrift), kXMaxDrift) : 0.f;
-      l_run += __builtin_ldexpf(lt, int(d_own));
+      l_run += __builtin_ldexpf(TWO ? lt * (second ? lq2 : lq1) : lt, int(d_own));
       const int sb_ph = kE8One + int(d_blk), sb_pl = kE8One - 4 + int(d_blk);
       const i32x8 ph = cat(u32x4{phi[0], phi[1], phi[2], phi[3]}, xho);
       const i32x8 pl = cat(u32x4{plo[0], plo[1], plo[2], plo[3]}, xlo);
@@ -881,9 +926,10 @@ prefill_mx_kernel(const FwdParams p) {
             }
             const int j = 2 * m + term;
             if (j < kPieces) dma_piece(g + 3, j);
-            if (j == kPieces) idx_dma(g + 5, t5, x5 ? idx_rsrc_next : idx_rsrc);
+            if (j == kPieces)
+              idx_dma(g + 5, t5, sel4(x5, idx_rsrc_next, idx_rsrc), sel4(x5, idx2_rsrc_next, idx2_rsrc));
             if (j == 11) dma4(pf_rsrc, lds0 + C::OFF_BIAS + ring(g) * kXTile * 4, pf_off);
-            if (j == 12) make_bn(g + 1);
+            if (j == 12) make_bn(g + 1, t_begin + tt + 1);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -913,6 +959,7 @@ prefill_mx_kernel(const FwdParams p) {
       head = hblk * 64 + 32 * hp + c32;
       head_ok = head < p.heads;
       idx_rsrc = idx_rsrc_of(r);
+      idx2_rsrc = idx2_rsrc_of(r);
       load_cs();
     }
     const bool more = can_stream && k + 1 < n_items;
@@ -920,6 +967,7 @@ prefill_mx_kernel(const FwdParams p) {
       int hb1, sp1;
       const int64_t r1 = item_of(k + 1, hb1, sp1);
       idx_rsrc_next = idx_rsrc_of(r1);
+      idx2_rsrc_next = idx2_rsrc_of(r1);
       const int64_t es = p.q_fp8 ? 1 : 2;
       const int64_t nh1 = min(64, p.heads - 64 * hb1);
       const int64_t span = min(nh1 * p.q_hs * es, int64_t(2 * 64 * DQK) * es);
@@ -957,7 +1005,7 @@ prefill_mx_kernel(const FwdParams p) {
     const int64_t r_st = r;
     const int head_st = head, split_st = split;
     if (head_ok) {
-      const float inv = lt_tot > 0.f ? kv_scale / lt_tot : 0.f;
+      const float inv = lt_tot > 0.f ? s_ref / lt_tot : 0.f;
       const bool split_mode = p.part_o != nullptr;
       const int colh = 256 * kh + 4 * h;  // column of register 0 of block 0
       if (EPI && !split_mode) {
@@ -1028,12 +1076,12 @@ KernelShape prefill_mx_shape(int dqk) {
   return k;
 }
 
-template <int DQK, bool PAGED>
+template <int DQK, bool PAGED, bool TWO>
 void launch_mx(const FwdParams& p, bool epi, dim3 grid, dim3 block, hipStream_t st) {
   if (epi)
-    hipLaunchKernelGGL((prefill_mx_kernel<DQK, true, PAGED>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((prefill_mx_kernel<DQK, true, PAGED, TWO>), grid, block, 0, st, p);
   else
-    hipLaunchKernelGGL((prefill_mx_kernel<DQK, false, PAGED>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((prefill_mx_kernel<DQK, false, PAGED, TWO>), grid, block, 0, st, p);
 }
 
 int launch_prefill_mx(const FwdParams& p, int dqk, void* stream) {
@@ -1048,12 +1096,25 @@ int launch_prefill_mx(const FwdParams& p, int dqk, void* stream) {
   if (p.splits == 1 && p.persist_cap > 0 && p.grid > p.persist_cap)
     wgs = p.persist_cap >= 8 ? p.persist_cap / 8 * 8 : p.persist_cap;
   const dim3 grid{uint32_t(wgs)}, block{uint32_t(kXWaves * 64)};
-  if (dqk == 576)
-    paged ? launch_mx<576, true>(p, epi, grid, block, st) : launch_mx<576, false>(p, epi, grid, block, st);
-  else if (dqk == 512)
-    paged ? launch_mx<512, true>(p, epi, grid, block, st) : launch_mx<512, false>(p, epi, grid, block, st);
-  else
+  // A second segment is walked over 2-D pools only (the planner composes
+  // the other cases from two launches).
+  const bool two = p.idx2 != nullptr;
+  if (two && (paged || !mx_pool_ok(p.pool2_rs_bytes, 0))) return int(hipErrorInvalidValue);
+  if (dqk == 576) {
+    if (two)
+      launch_mx<576, false, true>(p, epi, grid, block, st);
+    else
+      paged ? launch_mx<576, true, false>(p, epi, grid, block, st)
+            : launch_mx<576, false, false>(p, epi, grid, block, st);
+  } else if (dqk == 512) {
+    if (two)
+      launch_mx<512, false, true>(p, epi, grid, block, st);
+    else
+      paged ? launch_mx<512, true, false>(p, epi, grid, block, st)
+            : launch_mx<512, false, false>(p, epi, grid, block, st);
+  } else {
     return int(hipErrorInvalidValue);
+  }
   return int(hipGetLastError());
 }
 

@@ -250,14 +250,16 @@ def test_plan2_workspace_covers_both_segments(H, K1, K2, dtype):
         assert whole["head_block"] == 16 and whole["variant"] == 0
         assert p1 == whole and p2["grid"] == 0
         S = p1["splits"] if p1["splits"] > 1 else 0
-    elif dtype == torch.bfloat16:
-        # the 64-head bf16 kernel walks them too, the main top-k padded to tiles
+    elif dtype == torch.bfloat16 or H == 64:
+        # the 64-head bf16 kernel and the 64-head fp8-dot kernel walk them
+        # too, the main top-k padded to tiles
         K1p = (K1 + whole["tile_slots"] - 1) // whole["tile_slots"] * whole["tile_slots"]
-        # (the 8-wave kernel, variant 2: the one-segment default is the staged
-        # kernel, which would need a second launch)
+        # (bf16: the 8-wave kernel, variant 2: the one-segment default is the
+        # staged kernel, which would need a second launch)
         padded = _lib.sparse_mla_plan(q, pool, torch.zeros(R, K1p + K2, dtype=torch.int32),
-                                      variant=2)
+                                      variant=2 if dtype == torch.bfloat16 else 0)
         assert p1 == padded and p2["grid"] == 0
+        assert dtype == torch.bfloat16 or p1["variant"] == 3
         S = p1["splits"] if p1["splits"] > 1 else 0
     else:
         assert p1 == _lib.sparse_mla_plan(q, pool, i1)
@@ -265,6 +267,23 @@ def test_plan2_workspace_covers_both_segments(H, K1, K2, dtype):
         S = p1["splits"] + p2["splits"]
     o_bytes = S * R * H * 512 * 4
     assert ws == ((o_bytes + 255) // 256 * 256 + S * R * H * 4 if S else 0)
+
+
+def test_plan2_fp8dot_composes_when_the_extra_pitch_is_out_of_reach():
+    """The fp8-dot kernel addresses the second segment's pool through a
+    structured buffer whose stride field holds 14 bits: an extra pool with a
+    16 KB row pitch takes the two-launch composition."""
+    R, H = 192, 64
+    q = torch.zeros(R, H, 576, dtype=torch.bfloat16)
+    pool = torch.zeros(1024, 576, dtype=torch.float8_e4m3fn)
+    wide = torch.zeros(64, 16384, dtype=torch.float8_e4m3fn)[:, :576]
+    i1 = torch.zeros(R, 2048, dtype=torch.int32)
+    i2 = torch.zeros(R, 128, dtype=torch.int32)
+    p1, p2, ws = _lib.sparse_mla_plan2(q, pool, i1, wide, i2)
+    assert p1 == _lib.sparse_mla_plan(q, pool, i1) and p1["variant"] == 3
+    assert p2 == _lib.sparse_mla_plan(q, wide, i2) and p2["grid"] > 0
+    S = p1["splits"] + p2["splits"]
+    assert ws == (S * R * H * 512 * 4 + 255) // 256 * 256 + S * R * H * 4
 
 
 # ------------------------------------------------------------ output epilogue

@@ -253,11 +253,14 @@ def test_fused_store(kv, d_qk, heads, topk, opts, mx, rope):
 
 
 @pytest.mark.parametrize("kv,heads,opts", [("fp8", 16, {}), ("fp8", 64, {}), ("bf16", 64, {}),
-                                           ("fp8", 16, dict(variant=1))])
+                                           ("fp8", 16, dict(variant=1)), ("fp8", 64, dict(splits=1)),
+                                           ("fp8", 64, dict(variant=4))])
 def test_fused_store_two_segments(kv, heads, opts):
     """Both two-segment routes: one launch walking both segments (16-head fp8
-    decode kernel, 64-head bf16 kernel) and the composition (each segment's
-    partials, then the combine kernel's store)."""
+    decode kernel, 64-head bf16 kernel, 64-head fp8-dot kernel; with one
+    split the store of that launch applies the epilogue) and the composition
+    (each segment's partials, then the combine kernel's store; the 4-wave
+    64-head fp8 kernel)."""
     print(f"\n[epilogue two-segment] kv={kv} H={heads} {opts}", flush=True)
     inp = _workload(kv, 576, heads, 512)
     ex = make_extra_segment(inp, 128, seed=71, value_std=0.7, invalid_per_row=3)

@@ -80,6 +80,12 @@ CASES = [
     ("bf16", 576, 64, 300, 100, "causal", {}),
     ("bf16", 512, 64, 1000, 128, "uniform", dict(head_block=64, splits=3)),
     ("bf16", 576, 64, 512, 128, "request", dict(variant=1)),
+    # 64-head fp8-dot kernel walking both segments: ragged last tiles in both,
+    # splits that straddle the segment boundary; the 4-wave kernel composes
+    # the two segments through the combine kernel
+    ("fp8", 576, 64, 300, 100, "causal", {}),
+    ("fp8", 512, 64, 300, 100, "uniform", dict(head_block=64, splits=3)),
+    ("fp8", 576, 64, 1000, 128, "request", dict(variant=4)),
 ]
 
 
@@ -145,3 +151,39 @@ def test_two_segment_on_decode_workloads(name, window, every):
     ref_out, ref_lse = run_oracle2(inp, ex, rows=rows)
     stats = assert_parity(out, lse, ref_out, ref_lse, _both(inp, ex), rows=torch.from_numpy(rows))
     print(f"[two-segment] {name}: {stats}", flush=True)
+
+
+def test_fp8dot_two_segments_streaming_on_sampled_rows():
+    """600 rows of 64 heads in one split: the fp8-dot kernel's workgroups walk
+    several rows each as one stream of tiles (3 main tiles, then 2 of the
+    second segment, so the next row's first tiles, fetched ahead, include
+    second-segment ones). The oracle checks every 16th row plus the last."""
+    print("\n[two-segment] fp8-dot streaming, 600 rows, K=192, W=128", flush=True)
+    inp = _workload("fp8", 576, 64, 192, "causal", rows=600, seed=43)
+    ex = make_extra_segment(inp, 128, seed=78, value_std=0.7, invalid_per_row=3)
+    p1, p2, _ = _lib.sparse_mla_plan2(inp.q, inp.pool, inp.indices, ex.pool, ex.indices, splits=1)
+    assert p1["variant"] == 3 and p1["splits"] == 1 and p2["grid"] == 0
+    out, lse = run_gpu2(inp, ex, splits=1)
+    R = inp.q.shape[0]
+    rows = np.unique(np.r_[np.arange(0, R, 16), R - 1])
+    ref_out, ref_lse = run_oracle2(inp, ex, rows=rows)
+    stats = assert_parity(out, lse, ref_out, ref_lse, _both(inp, ex), rows=torch.from_numpy(rows))
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    print(f"[two-segment] {stats}", flush=True)
+
+
+@pytest.mark.parametrize("ratio", [16.0, 1.0 / 16.0])
+def test_fp8dot_two_segments_scale_ratio(ratio):
+    """A second-segment scale about 16 times (or 1/16 of) the main one, with
+    its codes divided by the same factor (clamped to the e4m3 range), so
+    that keys and values keep their magnitudes (and the absolute bounds
+    their meaning) while the fp8-dot kernel's one launch weighs the two
+    segments' codes by scales far apart."""
+    inp = _workload("fp8", 576, 64, 512, "causal", seed=44)
+    ex = make_extra_segment(inp, 128, seed=79, value_std=0.7, invalid_per_row=3)
+    ex.pool = (ex.pool.float() / ratio).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    s2 = (ex.kv_scale.float() * ratio).reshape(1)
+    out, lse = run_gpu2(inp, ex, extra_scale=s2)
+    ref_out, ref_lse = run_oracle2(inp, ex, extra_scale=s2)
+    print(f"\n[two-segment] ratio {ratio}: {assert_parity(out, lse, ref_out, ref_lse, _both(inp, ex))}",
+          flush=True)
