@@ -215,9 +215,14 @@ SMLA_API int sparse_mla_fwd_noalloc(const smla_tensor* q, const smla_tensor* kv_
  * extra ones, rebasing its accumulator from kv_scale onto extra_kv_scale
  * between them (acc *= kv_scale / extra_kv_scale, as the pages do); the
  * 64-head kernel over bf16 pools likewise walks the extra slots after the
- * main ones (no scale to rebase). Otherwise
+ * main ones (no scale to rebase). The 64-head fp8-dot kernel (variant 3)
+ * does so too when kv_pool is 2-D and both pools' row pitches are below
+ * 16 KB: it keeps its accumulator in units of the larger scale and weighs
+ * each segment's slots by its scale over that one (kv_scale and
+ * extra_kv_scale must then be nonnegative, as dequantisation scales are).
+ * Otherwise
  * each segment's kernel writes normalised partials with its own scale and the
- * split-combine kernel merges them. Both are exact in real arithmetic. Every
+ * split-combine kernel merges them. All are exact in real arithmetic. Every
  * other rule is sparse_mla_fwd's; out and lse must not alias any input.
  */
 SMLA_API int sparse_mla_fwd2(const smla_tensor* q, const smla_tensor* kv_pool,
