@@ -469,8 +469,8 @@ int validate_extra(const smla_tensor* q, const smla_tensor* kv_pool, const smla_
 // Plans of a two-segment call and their workspace. When the plan of the
 // combined problem (both segments' slots, the larger pool range) launches a
 // kernel that walks a second segment (the 16-head fp8 decode kernel, the
-// 64-head bf16 kernel, the 64-head fp8-dot kernel over 2-D pools whose row
-// pitches its structured buffers address), that kernel walks both segments
+// 64-head bf16 kernel, the 64-head fp8-dot kernel when the second pool's
+// row pitch fits its structured buffer), that kernel walks both segments
 // in one launch: *p1 is that plan and *p2 has grid 0. Otherwise each segment
 // gets its own plan and the workspace holds both segments' partials for the
 // combine kernel.
@@ -492,8 +492,7 @@ int plan_two(const Checked& c1, const Checked& c2, const smla_options* opt, int 
     if ((s = make_plan(tot, opt, num_cus, p1, &perr))) return fail(s, perr);
   }
   bool one = walks_second_segment(p1->head_block, c1.fp8, p1->variant);
-  if (one && p1->variant == 3)
-    one = c1.pb.page_bytes == 0 && mx_pool_ok(c2.pb.pool_rs_bytes, 0);
+  if (one && p1->variant == 3) one = mx_pool_ok(c2.pb.pool_rs_bytes, 0);
   if (one) {
     if (!uses_decode_kernel(p1->head_block, c1.fp8, p1->variant)) {
       // Tiled walk: the second segment starts at a whole tile.

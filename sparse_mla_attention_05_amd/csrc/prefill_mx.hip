@@ -372,6 +372,7 @@ prefill_mx_kernel(const FwdParams p) {
       idb = base + (lane & 15) < se ? idb : -1;
     }
     if constexpr (PAGED) {
+      if (x) return;  // the second segment's pool is 2-D
       auto map = [&](int i) -> int {
         return i < 0 ? -1
                      : int((uint32_t(i) >> p.page_shift) * page_rows + (uint32_t(i) & p.page_mask));
@@ -1096,19 +1097,21 @@ int launch_prefill_mx(const FwdParams& p, int dqk, void* stream) {
   if (p.splits == 1 && p.persist_cap > 0 && p.grid > p.persist_cap)
     wgs = p.persist_cap >= 8 ? p.persist_cap / 8 * 8 : p.persist_cap;
   const dim3 grid{uint32_t(wgs)}, block{uint32_t(kXWaves * 64)};
-  // A second segment is walked over 2-D pools only (the planner composes
-  // the other cases from two launches).
+  // A second segment's pool is 2-D, with a row pitch the structured buffer
+  // addresses (the planner composes the other cases from two launches).
   const bool two = p.idx2 != nullptr;
-  if (two && (paged || !mx_pool_ok(p.pool2_rs_bytes, 0))) return int(hipErrorInvalidValue);
+  if (two && !mx_pool_ok(p.pool2_rs_bytes, 0)) return int(hipErrorInvalidValue);
   if (dqk == 576) {
     if (two)
-      launch_mx<576, false, true>(p, epi, grid, block, st);
+      paged ? launch_mx<576, true, true>(p, epi, grid, block, st)
+            : launch_mx<576, false, true>(p, epi, grid, block, st);
     else
       paged ? launch_mx<576, true, false>(p, epi, grid, block, st)
             : launch_mx<576, false, false>(p, epi, grid, block, st);
   } else if (dqk == 512) {
     if (two)
-      launch_mx<512, false, true>(p, epi, grid, block, st);
+      paged ? launch_mx<512, true, true>(p, epi, grid, block, st)
+            : launch_mx<512, false, true>(p, epi, grid, block, st);
     else
       paged ? launch_mx<512, true, false>(p, epi, grid, block, st)
             : launch_mx<512, false, false>(p, epi, grid, block, st);

@@ -34,8 +34,9 @@ def _workload(kv, d_qk, heads, topk, mode, rows=12, seed=41):
     return make_inputs(w)
 
 
-def run_gpu2(inp, ex, extra_scale="own", **opts):
-    q, pool, idx = inp.q.cuda(), inp.pool.cuda(), inp.indices.cuda()
+def run_gpu2(inp, ex, extra_scale="own", pool=None, **opts):
+    q, idx = inp.q.cuda(), inp.indices.cuda()
+    pool = inp.pool.cuda() if pool is None else pool
     s1 = inp.kv_scale.cuda() if inp.kv_scale is not None else None
     es = ex.kv_scale if extra_scale == "own" else extra_scale
     s2 = es.cuda() if es is not None else None
@@ -186,4 +187,24 @@ def test_fp8dot_two_segments_scale_ratio(ratio):
     out, lse = run_gpu2(inp, ex, extra_scale=s2)
     ref_out, ref_lse = run_oracle2(inp, ex, extra_scale=s2)
     print(f"\n[two-segment] ratio {ratio}: {assert_parity(out, lse, ref_out, ref_lse, _both(inp, ex))}",
+          flush=True)
+
+
+@pytest.mark.parametrize("d_qk,page_rows,pad", [(576, 64, 576), (512, 32, 512)])
+def test_fp8dot_two_segments_paged_main_pool(d_qk, page_rows, pad):
+    """A paged main pool (pages a whole number of rows apart) in the fp8-dot
+    kernel's two-segment launch gives the flat pool's result bit for bit (same
+    plan, only the main rows' addresses differ), and so the oracle's."""
+    from test_gpu_variants import paged_pool
+
+    inp = _workload("fp8", d_qk, 64, 300, "causal", seed=45)
+    ex = make_extra_segment(inp, 100, seed=80, value_std=0.7, invalid_per_row=3)
+    flat_out, flat_lse = run_gpu2(inp, ex)
+    _keep, paged = paged_pool(inp.pool, page_rows, pad)
+    p1, p2, _ = _lib.sparse_mla_plan2(inp.q, paged, inp.indices, ex.pool, ex.indices)
+    assert p1["variant"] == 3 and p2["grid"] == 0
+    out, lse = run_gpu2(inp, ex, pool=paged)
+    assert torch.equal(out, flat_out) and torch.equal(lse, flat_lse)
+    ref_out, ref_lse = run_oracle2(inp, ex)
+    print(f"\n[two-segment paged] {assert_parity(out, lse, ref_out, ref_lse, _both(inp, ex))}",
           flush=True)
