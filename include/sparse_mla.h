@@ -216,8 +216,8 @@ SMLA_API int sparse_mla_fwd_noalloc(const smla_tensor* q, const smla_tensor* kv_
  * between them (acc *= kv_scale / extra_kv_scale, as the pages do); the
  * 64-head kernel over bf16 pools likewise walks the extra slots after the
  * main ones (no scale to rebase). The 64-head fp8-dot kernel (variant 3)
- * does so too when kv_pool is 2-D and both pools' row pitches are below
- * 16 KB: it keeps its accumulator in units of the larger scale and weighs
+ * does so too when extra_pool's row pitch is below 16 KB (kv_pool may be
+ * paged): it keeps its accumulator in units of the larger scale and weighs
  * each segment's slots by its scale over that one (kv_scale and
  * extra_kv_scale must then be nonnegative, as dequantisation scales are).
  * Otherwise
