@@ -22,9 +22,12 @@
 //    the split is exact except for elements below 2^-14 of their block's
 //    largest, where it errs by 2^-22 of it. The MFMA's E8M0 block scales
 //    (one per column and 32-deep k-block) apply 2^-e and 2^-(e+4), so
-//    S = K.q comes out exactly as with bf16 dots, up to fp32 accumulation
-//    order. A block's scale depends on its own 32 values only, so each
-//    k-step of q is split as soon as it has landed.
+//    S = K.q comes out as with bf16 dots up to the fp8 matrix core's
+//    accumulation, which is coarser than fp32 (measured: products summed in
+//    groups of 8 aligned to each group's largest with a window under 17
+//    bits, so a dot errs by about 2^-16 of its largest product; the LSE of a
+//    sharply peaked row shows it). A block's scale depends on its own 32
+//    values only, so each k-step of q is split as soon as it has landed.
 //  * P = 2^(s - m) <= 2^8 (see below) splits the same way into two e4m3
 //    terms, 8 significant bits in all, the precision of the pages' bf16 P.
 //  * The fp8 keys and values are used as stored (exact), so tiles stay fp8
