@@ -286,6 +286,22 @@ def test_plan2_fp8dot_composes_when_the_extra_pitch_is_out_of_reach():
     assert ws == (S * R * H * 512 * 4 + 255) // 256 * 256 + S * R * H * 4
 
 
+def test_plan2_fp8dot_walks_both_segments_over_a_paged_main_pool():
+    """A paged main pool (pages a whole number of rows apart) keeps the
+    fp8-dot kernel's one-launch walk; the second pool is 2-D."""
+    R, H, rows_per_page = 192, 64, 64
+    q = torch.zeros(R, H, 576, dtype=torch.bfloat16)
+    flat = torch.zeros(16 * rows_per_page * 576, dtype=torch.float8_e4m3fn)
+    paged = flat.as_strided((16, rows_per_page, 576), (rows_per_page * 576, 576, 1))
+    extra = torch.zeros(1024, 576, dtype=torch.float8_e4m3fn)
+    i1 = torch.zeros(R, 300, dtype=torch.int32)
+    i2 = torch.zeros(R, 100, dtype=torch.int32)
+    p1, p2, _ = _lib.sparse_mla_plan2(q, paged, i1, extra, i2)
+    assert p1["variant"] == 3 and p2["grid"] == 0
+    padded = _lib.sparse_mla_plan(q, paged, torch.zeros(R, 320 + 100, dtype=torch.int32))
+    assert p1 == padded
+
+
 # ------------------------------------------------------------ output epilogue
 
 def _epi_args(R=4, H=16, mx=True, rope=True):
